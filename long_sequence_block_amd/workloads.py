@@ -1,0 +1,166 @@
+"""Seeded synthetic workloads for block attention.
+
+This module only draws random numbers and lays them out; it holds none of
+the attention arithmetic.  It is the one module that the oracle-side tests
+and the GPU path both use, so that both see identical inputs.
+
+The pages measure on production user-engagement histories ("GEM (Meta)",
+sections "Architecture" and "Training infrastructure": histories from
+hundreds to tens of thousands of events, jagged per user; section "Custom
+kernels": 64-token blocks).  No public dataset is named, so seeded synthetic
+sequences of those shapes stand in for them:
+
+* lengths, for the jagged workloads: lognormal with median 600 (mu = ln 600)
+  and sigma 0.8 in log space, rounded to the nearest integer and clipped to
+  [16, 4096]; offsets are the int32 exclusive prefix sum;
+* Q, K, V and the upstream gradient dO: i.i.d. standard normal float32 of
+  shape [T, H, D]; the bf16 workloads round them to bf16 (round to nearest
+  even) on the way to the device, and the oracle sees those rounded values;
+* scale = 1/sqrt(D).
+
+Random streams: numpy ``Generator(PCG64(SeedSequence([workload, stream])))``
+with stream 0 = lengths, 1 = Q, 2 = K, 3 = V, 4 = dO.  The training-step
+workload reuses the jagged workload's lengths and Q/K/V (workload id 3) and
+draws dO from [5, 4].
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+STREAM_LENGTHS, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = 0, 1, 2, 3, 4
+
+
+def rng(workload: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload, stream])))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """A synthetic block-attention workload (sizes only; draws are lazy)."""
+    wid: int                 # seed id of the lengths and Q/K/V streams
+    name: str
+    users: int
+    heads: int
+    head_dim: int
+    block_size: int
+    window_blocks: int
+    dtype: str               # "fp32" or "bf16"
+    backward: bool
+    fixed_length: int = 0    # >0: every user has this length
+    dout_wid: int = 0        # seed id of the dO stream (backward only)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def lengths(self) -> np.ndarray:
+        if self.fixed_length > 0:
+            return np.full(self.users, self.fixed_length, dtype=np.int32)
+        return lognormal_lengths(self.wid, self.users)
+
+    def offsets(self) -> np.ndarray:
+        return offsets_from_lengths(self.lengths())
+
+
+def lognormal_lengths(wid: int, users: int, median: float = 600.0,
+                      sigma: float = 0.8, lo: int = 16, hi: int = 4096) -> np.ndarray:
+    g = rng(wid, STREAM_LENGTHS)
+    x = g.lognormal(mean=math.log(median), sigma=sigma, size=users)
+    return np.clip(np.rint(x), lo, hi).astype(np.int32)
+
+
+def offsets_from_lengths(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=off[1:])
+    if off[-1] > np.iinfo(np.int32).max:
+        raise ValueError("total token count does not fit int32 offsets")
+    return off.astype(np.int32)
+
+
+def normal(wid: int, stream: int, shape) -> np.ndarray:
+    """i.i.d. N(0, 1) float32 draws for one tensor."""
+    return rng(wid, stream).standard_normal(size=shape, dtype=np.float32)
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny-fp32", users=2, heads=1, head_dim=32, block_size=32,
+                window_blocks=1, dtype="fp32", backward=False, fixed_length=256),
+    2: Workload(2, "fixed-bf16", users=64, heads=4, head_dim=64, block_size=64,
+                window_blocks=2, dtype="bf16", backward=False, fixed_length=1024),
+    3: Workload(3, "jagged-bf16", users=256, heads=8, head_dim=64, block_size=128,
+                window_blocks=2, dtype="bf16", backward=False),
+    4: Workload(4, "long-context-bf16", users=32, heads=8, head_dim=128,
+                block_size=256, window_blocks=4, dtype="bf16", backward=False,
+                fixed_length=16384),
+    5: Workload(3, "jagged-bf16-train", users=256, heads=8, head_dim=64,
+                block_size=128, window_blocks=2, dtype="bf16", backward=True,
+                dout_wid=5),
+}
+
+# Length sweep of the long-context workload (time should grow linearly).
+LONG_CONTEXT_SWEEP = (2048, 4096, 8192, 16384)
+
+
+def long_context(length: int) -> Workload:
+    w = WORKLOADS[4]
+    return dataclasses.replace(w, fixed_length=int(length),
+                               name=f"long-context-bf16-L{length}")
+
+
+def draw(w: Workload, users=None):
+    """Draw the tensors of a workload.
+
+    Returns a dict with ``offsets`` (int32 [batch+1]) and float32 numpy
+    arrays ``q``, ``k``, ``v`` (and ``dout`` for backward workloads) of shape
+    [T, H, D].  ``users`` (a slice) keeps only those users' rows; draws are
+    made for the whole workload first so a subset matches the full run.
+    """
+    off = w.offsets()
+    T = int(off[-1])
+    shape = (T, w.heads, w.head_dim)
+    out = {"offsets": off,
+           "q": normal(w.wid, STREAM_Q, shape),
+           "k": normal(w.wid, STREAM_K, shape),
+           "v": normal(w.wid, STREAM_V, shape)}
+    if w.backward:
+        out["dout"] = normal(w.dout_wid, STREAM_DO, shape)
+    if users is not None:
+        out = subset_users(out, users)
+    return out
+
+
+def subset_users(tensors: dict, users: slice) -> dict:
+    """Keep a contiguous range of users (rows and re-based offsets)."""
+    off = tensors["offsets"]
+    idx = np.arange(len(off) - 1)[users]
+    if len(idx) == 0:
+        lo = hi = 0
+    else:
+        if np.any(np.diff(idx) != 1):
+            raise ValueError("subset_users needs a contiguous range")
+        lo, hi = int(off[idx[0]]), int(off[idx[-1] + 1])
+    res = {"offsets": (off[idx[0]: idx[-1] + 2] - lo).astype(np.int32)
+           if len(idx) else np.zeros(1, np.int32)}
+    for key, val in tensors.items():
+        if key != "offsets":
+            res[key] = val[lo:hi]
+    return res
+
+
+def random_case(seed: int, lengths, heads: int, head_dim: int, with_dout=True):
+    """Small seeded case for tests: given per-user lengths, N(0,1) tensors."""
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    shape = (T, heads, head_dim)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000, seed])))
+    out = {"offsets": off,
+           "q": g.standard_normal(size=shape, dtype=np.float32),
+           "k": g.standard_normal(size=shape, dtype=np.float32),
+           "v": g.standard_normal(size=shape, dtype=np.float32)}
+    if with_dout:
+        out["dout"] = g.standard_normal(size=shape, dtype=np.float32)
+    return out

@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for block attention.
+
+TEST INFRASTRUCTURE ONLY.  This package may be imported by the test suite,
+by the smoke check and by the benchmark's CPU-baseline leg, and by nothing
+else: the product path (the HIP library and its binding) never imports,
+calls or links it, and the two share no code.
+
+The arithmetic lives in ``blockattn_oracle.c`` (plain C, fp64, OpenMP over
+(user, head) pairs); this module builds it with gcc and wraps it with ctypes.
+What it computes, and the readings of the pages it rests on, are stated in
+the header of that C file.  Pins that tie it to something other than itself
+are in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "blockattn_oracle.c")
+_LIB = os.path.join(_HERE, "libblockattn_oracle.so")
+_lib = None
+
+
+def build_oracle() -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build_oracle()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_fwd.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32,
+                               f64, dp, dp]
+    lib.oracle_fwd.restype = ctypes.c_int
+    lib.oracle_bwd.argtypes = [dp, dp, dp, dp, ip, i32, i64, i32, i32, i32,
+                               i32, f64, dp, dp, dp]
+    lib.oracle_bwd.restype = ctypes.c_int
+    lib.oracle_probs.argtypes = [dp, dp, ip, i32, i64, i32, i32, i32, i32,
+                                 f64, i32, i32, dp]
+    lib.oracle_probs.restype = ctypes.c_int
+    lib.oracle_pair_count.argtypes = [ip, i32, i32, i32]
+    lib.oracle_pair_count.restype = ctypes.c_int64
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _dp(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _ip(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs with (OMP_NUM_THREADS or all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def pair_count(offsets, block_size: int, window_blocks: int) -> int:
+    """Number of visible (query, key) pairs per head, summed over users."""
+    off = _i32(offsets)
+    r = _load().oracle_pair_count(_ip(off), len(off) - 1, int(block_size),
+                                  int(window_blocks))
+    if r < 0:
+        raise ValueError("oracle_pair_count: invalid arguments")
+    return int(r)
+
+
+def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float):
+    """Forward pass.  q, k, v: [T, H, D]; offsets: [batch+1].
+
+    Returns (out [T, H, D] fp64, lse [H, T] fp64).
+    """
+    q, k, v, off = _f64(q), _f64(k), _f64(v), _i32(offsets)
+    T, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [T, H, D] shape")
+    out = np.zeros((T, H, D), np.float64)
+    lse = np.zeros((H, T), np.float64)
+    rc = _load().oracle_fwd(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T,
+                            H, D, int(block_size), int(window_blocks),
+                            float(scale), _dp(out), _dp(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_fwd failed with status {rc}")
+    return out, lse
+
+
+def bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int,
+        scale: float):
+    """Backward pass.  Returns (dq, dk, dv), each [T, H, D] fp64."""
+    q, k, v, do, off = _f64(q), _f64(k), _f64(v), _f64(dout), _i32(offsets)
+    T, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or do.shape != q.shape:
+        raise ValueError("q, k, v, dout must share one [T, H, D] shape")
+    dq = np.zeros((T, H, D), np.float64)
+    dk = np.zeros((T, H, D), np.float64)
+    dv = np.zeros((T, H, D), np.float64)
+    rc = _load().oracle_bwd(_dp(q), _dp(k), _dp(v), _dp(do), _ip(off),
+                            len(off) - 1, T, H, D, int(block_size),
+                            int(window_blocks), float(scale), _dp(dq), _dp(dk),
+                            _dp(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_bwd failed with status {rc}")
+    return dq, dk, dv
+
+
+def probs(q, k, offsets, block_size: int, window_blocks: int, scale: float,
+          user: int, head: int) -> np.ndarray:
+    """Dense [L, L] attention-probability matrix of one (user, head)."""
+    q, k, off = _f64(q), _f64(k), _i32(offsets)
+    T, H, D = q.shape
+    L = int(off[user + 1] - off[user])
+    P = np.zeros((L, L), np.float64)
+    rc = _load().oracle_probs(_dp(q), _dp(k), _ip(off), len(off) - 1, T, H, D,
+                              int(block_size), int(window_blocks), float(scale),
+                              int(user), int(head), _dp(P))
+    if rc != 0:
+        raise ValueError(f"oracle_probs failed with status {rc}")
+    return P

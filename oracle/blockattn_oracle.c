@@ -1,0 +1,270 @@
+/*
+ * Block-attention oracle: plain, slow, fp64 CPU implementation of the
+ * definition.  TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library; the
+ * product path never calls it and shares no code with it.
+ *
+ * What it computes.  "GEM (Meta)" (aiwiki.ai), section "Custom kernels",
+ * says BlockAttention splits long user-history self-attention into
+ * independent 64-token block computations; the ai.info news item, section
+ * "Kunlun changes how GEM scales", and the sysdesai.com summary, section
+ * "Kunlun Architecture Details", say block attention is sparse attention
+ * arranged in blocks whose cost is linear in sequence length for a fixed
+ * window.  "GEM (Meta)", section "Training infrastructure", says the
+ * sequences are jagged (per-user lengths, no padding).  The pages give no
+ * formula; the readings taken here are:
+ *
+ *   - each user u owns tokens [offsets[u], offsets[u+1]) of a packed
+ *     [T, H, D] tensor; indices below are local to the user;
+ *   - blocks of B tokens start at the user's first token (the last one may
+ *     be partial) and never straddle users;
+ *   - query i sees key j iff  j <= i  and  floor(i/B) - floor(j/B) <= W-1,
+ *     i.e. its own block up to itself plus the W-1 previous blocks;
+ *   - scores s_ij = scale * <q_i, k_j>, softmax over the visible set,
+ *     O_i = sum_j P_ij v_j, lse_i = ln sum_j exp(s_ij)  (natural log,
+ *     scale included);
+ *   - backward: dP_ij = <dO_i, v_j>, delta_i = sum_j P_ij dP_ij,
+ *     dS_ij = P_ij (dP_ij - delta_i), dQ_i = scale sum_j dS_ij k_j,
+ *     dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i.
+ *
+ * The softmax is two-pass (max, then sum of exponentials) over the visible
+ * range of each query, in fp64; delta comes from P and dP, not from <dO,O>.
+ * Work is split over (user, head) pairs with OpenMP; every output element is
+ * written by exactly one thread in a fixed order, so results do not depend
+ * on the thread count.
+ *
+ * Layouts: q, k, v, out, dout, dq, dk, dv are fp64 [T, H, D] row-major;
+ * lse is fp64 [H, T]; offsets is int32 [batch+1].
+ * Return value: 0 on success, -1 on invalid arguments or malformed offsets,
+ * -2 if scratch memory could not be allocated.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* First local key index visible to local query i (window start). */
+static int64_t first_visible(int64_t i, int64_t B, int64_t W)
+{
+    int64_t blk = i / B - (W - 1);
+    return (blk < 0 ? 0 : blk) * B;
+}
+
+static int check_args(const int32_t *offsets, int batch, int64_t T, int H, int D,
+                      int B, int W)
+{
+    if (batch < 0 || T < 0 || H < 1 || D < 1 || B < 1 || W < 1 || !offsets)
+        return -1;
+    if (offsets[0] != 0 || (int64_t)offsets[batch] != T)
+        return -1;
+    for (int u = 0; u < batch; ++u)
+        if (offsets[u + 1] < offsets[u])
+            return -1;
+    return 0;
+}
+
+static double dot(const double *a, const double *b, int D)
+{
+    double s = 0.0;
+    for (int d = 0; d < D; ++d)
+        s += a[d] * b[d];
+    return s;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Sum over all users of the number of visible keys per query (one head). */
+int64_t oracle_pair_count(const int32_t *offsets, int batch, int B, int W)
+{
+    if (batch < 0 || B < 1 || W < 1 || !offsets)
+        return -1;
+    int64_t total = 0;
+    for (int u = 0; u < batch; ++u) {
+        int64_t L = (int64_t)offsets[u + 1] - offsets[u];
+        for (int64_t i = 0; i < L; ++i)
+            total += i - first_visible(i, B, W) + 1;
+    }
+    return total;
+}
+
+/* Forward pass: out [T,H,D] and lse [H,T]. */
+int oracle_fwd(const double *q, const double *k, const double *v,
+               const int32_t *offsets, int batch, int64_t T, int H, int D,
+               int B, int W, double scale, double *out, double *lse)
+{
+    if (check_args(offsets, batch, T, H, D, B, W))
+        return -1;
+    int status = 0;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D; /* token stride */
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)W * (size_t)B);
+        if (!s) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < npairs; ++p) {
+            if (!s)
+                continue;
+            const int u = (int)(p / H), h = (int)(p % H);
+            const int64_t t0 = offsets[u];
+            const int64_t L = (int64_t)offsets[u + 1] - t0;
+            for (int64_t i = 0; i < L; ++i) {
+                const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+                const int64_t j0 = first_visible(i, B, W);
+                const int64_t n = i - j0 + 1;
+                /* pass 1: scores and their maximum */
+                double m = -INFINITY;
+                for (int64_t t = 0; t < n; ++t) {
+                    const double *kj = k + (t0 + j0 + t) * rs + (int64_t)h * D;
+                    s[t] = scale * dot(qi, kj, D);
+                    if (s[t] > m)
+                        m = s[t];
+                }
+                /* pass 2: normaliser */
+                double l = 0.0;
+                for (int64_t t = 0; t < n; ++t)
+                    l += exp(s[t] - m);
+                double *oi = out + (t0 + i) * rs + (int64_t)h * D;
+                for (int d = 0; d < D; ++d)
+                    oi[d] = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    const double pij = exp(s[t] - m) / l;
+                    const double *vj = v + (t0 + j0 + t) * rs + (int64_t)h * D;
+                    for (int d = 0; d < D; ++d)
+                        oi[d] += pij * vj[d];
+                }
+                lse[(int64_t)h * T + t0 + i] = m + log(l);
+            }
+        }
+        free(s);
+    }
+    return status;
+}
+
+/* Backward pass: dq, dk, dv [T,H,D] from the upstream gradient dout. */
+int oracle_bwd(const double *q, const double *k, const double *v,
+               const double *dout, const int32_t *offsets, int batch, int64_t T,
+               int H, int D, int B, int W, double scale, double *dq, double *dk,
+               double *dv)
+{
+    if (check_args(offsets, batch, T, H, D, B, W))
+        return -1;
+    int status = 0;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)W * (size_t)B);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)W * (size_t)B);
+        if (!s || !dp) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < npairs; ++p) {
+            if (!s || !dp)
+                continue;
+            const int u = (int)(p / H), h = (int)(p % H);
+            const int64_t t0 = offsets[u];
+            const int64_t L = (int64_t)offsets[u + 1] - t0;
+            /* this thread owns rows [t0, t0+L) of head h in dk and dv */
+            for (int64_t i = 0; i < L; ++i) {
+                double *dki = dk + (t0 + i) * rs + (int64_t)h * D;
+                double *dvi = dv + (t0 + i) * rs + (int64_t)h * D;
+                for (int d = 0; d < D; ++d)
+                    dki[d] = dvi[d] = 0.0;
+            }
+            for (int64_t i = 0; i < L; ++i) {
+                const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+                const double *doi = dout + (t0 + i) * rs + (int64_t)h * D;
+                const int64_t j0 = first_visible(i, B, W);
+                const int64_t n = i - j0 + 1;
+                double m = -INFINITY;
+                for (int64_t t = 0; t < n; ++t) {
+                    const double *kj = k + (t0 + j0 + t) * rs + (int64_t)h * D;
+                    s[t] = scale * dot(qi, kj, D);
+                    if (s[t] > m)
+                        m = s[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < n; ++t)
+                    l += exp(s[t] - m);
+                /* s[] now holds P_ij, dp[] holds dP_ij */
+                double delta = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    const double *vj = v + (t0 + j0 + t) * rs + (int64_t)h * D;
+                    s[t] = exp(s[t] - m) / l;
+                    dp[t] = dot(doi, vj, D);
+                    delta += s[t] * dp[t];
+                }
+                double *dqi = dq + (t0 + i) * rs + (int64_t)h * D;
+                for (int d = 0; d < D; ++d)
+                    dqi[d] = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    const int64_t j = t0 + j0 + t;
+                    const double *kj = k + j * rs + (int64_t)h * D;
+                    double *dkj = dk + j * rs + (int64_t)h * D;
+                    double *dvj = dv + j * rs + (int64_t)h * D;
+                    const double ds = s[t] * (dp[t] - delta);
+                    for (int d = 0; d < D; ++d) {
+                        dqi[d] += scale * ds * kj[d];
+                        dkj[d] += scale * ds * qi[d];
+                        dvj[d] += s[t] * doi[d];
+                    }
+                }
+            }
+        }
+        free(s);
+        free(dp);
+    }
+    return status;
+}
+
+/*
+ * Dense probability matrix of one (user, head): P [L, L] row-major, zero
+ * where a key is not visible.  Meant for tiny inputs (row-sum and mask
+ * checks); L = offsets[u+1] - offsets[u].
+ */
+int oracle_probs(const double *q, const double *k, const int32_t *offsets,
+                 int batch, int64_t T, int H, int D, int B, int W, double scale,
+                 int u, int h, double *P)
+{
+    if (check_args(offsets, batch, T, H, D, B, W) || u < 0 || u >= batch ||
+        h < 0 || h >= H)
+        return -1;
+    const int64_t rs = (int64_t)H * D;
+    const int64_t t0 = offsets[u];
+    const int64_t L = (int64_t)offsets[u + 1] - t0;
+    memset(P, 0, sizeof(double) * (size_t)(L * L));
+    for (int64_t i = 0; i < L; ++i) {
+        const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+        const int64_t j0 = first_visible(i, B, W);
+        double m = -INFINITY;
+        for (int64_t j = j0; j <= i; ++j) {
+            const double sij =
+                scale * dot(qi, k + (t0 + j) * rs + (int64_t)h * D, D);
+            P[i * L + j] = sij;
+            if (sij > m)
+                m = sij;
+        }
+        double l = 0.0;
+        for (int64_t j = j0; j <= i; ++j)
+            l += exp(P[i * L + j] - m);
+        for (int64_t j = j0; j <= i; ++j)
+            P[i * L + j] = exp(P[i * L + j] - m) / l;
+    }
+    return 0;
+}
