@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of jagged block attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the forward kernel (scores, mask, online softmax, PV, epilogue) and, for
+training workloads, the fused backward kernel (dQ, dK, dV).  The default
+workload is the jagged bf16 training step: 256 users with lognormal lengths
+(median 600, sigma 0.8, clipped to [16, 4096]), 8 heads, head_dim 64,
+block 128, window 2 blocks, forward plus backward.
+
+Prints ONE JSON line.  ``value`` is algorithmic TFLOP/s over unmasked
+(query, key) pairs: 4*D flops per pair forward, 8*D backward.  Inputs are
+resident in HBM before the timed region.  ``roofline`` describes the
+dominant kernel (each entry point is a single kernel launch), timed with HIP
+events on the stream the kernels run on; ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "block-attention TFLOP/s and tokens/s (fwd+bwd, jagged bf16) and % of MFMA peak"
+KERNEL_SOURCES = ("common.h", "kernels.h", "api.hip", "scalar_kernels.hip",
+                  "mfma_fwd.hip", "mfma_bwd.hip")
+
+
+def pairs_per_head(offsets: np.ndarray, B: int, W: int) -> int:
+    """Number of visible (query, key) pairs per head: the FLOP count basis."""
+    total = 0
+    for L in np.diff(offsets.astype(np.int64)):
+        i = np.arange(L, dtype=np.int64)
+        total += int(np.sum(i - np.maximum(0, i // B - W + 1) * B + 1))
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "long_sequence_block_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(w, users: int, flops_per_pair_head: float):
+    """The fp64 oracle, as it stands, on users [0, users) of the workload."""
+    import oracle
+    from long_sequence_block_amd import workloads as wl
+    import torch
+    c = wl.draw(w, users=slice(0, users))
+    host = {}
+    for key, val in c.items():
+        if key == "offsets":
+            host[key] = val
+        else:
+            t = torch.from_numpy(val)
+            if w.dtype == "bf16":
+                t = t.to(torch.bfloat16)
+            host[key] = t.to(torch.float64).numpy()
+    off = host["offsets"]
+    t0 = time.perf_counter()
+    oracle.fwd(host["q"], host["k"], host["v"], off, w.block_size, w.window_blocks, w.scale)
+    if w.backward:
+        oracle.bwd(host["q"], host["k"], host["v"], host["dout"], off, w.block_size,
+                   w.window_blocks, w.scale)
+    dt = time.perf_counter() - t0
+    flops = flops_per_pair_head * pairs_per_head(off, w.block_size, w.window_blocks) * w.heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"users 0-{users - 1} of {w.name} ({int(off[-1])} tokens, "
+                       f"{'fwd+bwd' if w.backward else 'fwd'}, fp64), {dt:.1f} s"),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1 tiny fp32, 2 fixed bf16, 3 jagged bf16, 4 long context, "
+                         "5 jagged bf16 training step (default)")
+    ap.add_argument("--length", type=int, default=0,
+                    help="long-context workload: per-user length (sweep)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-users", type=int, default=64)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: this build has no multi-GPU path "
+                  "(users and heads shard across GPUs with no exchange; see DESIGN.md). "
+                  "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_sequence_block_amd as lsb
+    from long_sequence_block_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if args.length:
+        w = wl.long_context(args.length)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    c = wl.draw(w)
+    off_np = c["offsets"]
+    T = int(off_np[-1])
+    d = {k: torch.from_numpy(v).to(dev) if k == "offsets" else
+         torch.from_numpy(v).to(tdt).to(dev) for k, v in c.items()}
+    del c
+    B, W, sc = w.block_size, w.window_blocks, w.scale
+    H, D = w.heads, w.head_dim
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(d["q"]) for _ in range(3)) if w.backward else None
+    ws_n = lsb.blockattn_bwd_workspace_size(T, H, lsb.BF16 if w.dtype == "bf16" else lsb.FP32)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lsb.fwd(d["q"], d["k"], d["v"], d["offsets"], B, W, sc, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        if w.backward:
+            lsb.bwd(d["q"], d["k"], d["v"], out, d["dout"], lse, d["offsets"], B, W, sc,
+                    grads=grads, workspace=ws)
+            if ev is not None:
+                ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = (sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps) if w.backward else 0.0
+
+    npair = pairs_per_head(off_np, B, W)
+    e = 2 if w.dtype == "bf16" else 4
+    fwd_flops = 4.0 * D * npair * H
+    bwd_flops = 8.0 * D * npair * H if w.backward else 0.0
+    fwd_bytes = T * H * (4.0 * D * e + 4)
+    bwd_bytes = T * H * (8.0 * D * e + 4) if w.backward else 0.0
+    flops = fwd_flops + bwd_flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    # dominant kernel: the entry point (one launch each) with the larger time
+    if w.backward and bwd_ms >= fwd_ms:
+        kname, k_ms, k_flops, k_bytes = "bwd", bwd_ms, bwd_flops, bwd_bytes
+    else:
+        kname, k_ms, k_flops, k_bytes = "fwd", fwd_ms, fwd_flops, fwd_bytes
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if k_flops / k_bytes < ridge:
+        ach = k_bytes / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = k_flops / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(ach, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    roof["traffic"] = measured_traffic(kname, w.name)
+    roof["kernel"] = kname
+    roof["avg_launch_ms"] = round(k_ms, 4)
+    roof["algorithmic_bytes"] = k_bytes
+    roof["algorithmic_flops"] = k_flops
+
+    res = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; lognormal jagged lengths, N(0,1) values)",
+        "config": {"workload": w.name, "users": w.users, "tokens": T, "heads": H,
+                   "head_dim": D, "block_size": B, "window_blocks": W,
+                   "backward": w.backward, "pairs_per_head": npair,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "pct_mfma_peak": round(100.0 * tflops / peak, 3),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        users = min(args.cpu_users, w.users)
+        res["cpu_baseline"] = cpu_baseline(w, users, 4.0 * D + (8.0 * D if w.backward else 0))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,125 @@
+/*
+ * blockattn.h -- C ABI of the MI355X (gfx950) jagged block-attention library.
+ *
+ * Operation.  Block attention replaces full self-attention over a user's
+ * engagement history with sparse attention arranged in fixed-size token
+ * blocks, making the cost linear in sequence length for a fixed window (ai.info
+ * news item, section "Kunlun changes how GEM scales"; sysdesai.com summary,
+ * section "Kunlun Architecture Details"; "GEM (Meta)" on aiwiki.ai, section
+ * "Custom kernels", which names 64-token blocks).  Histories are jagged: each
+ * user has its own length and nothing is padded ("GEM (Meta)", sections
+ * "Training infrastructure" and "Custom kernels").
+ *
+ * Exact pattern computed (the pages give no formula; these are the readings):
+ *   user u owns packed tokens [offsets[u], offsets[u+1]);  with i, j local
+ *   indices inside that user, query i attends to key j iff
+ *       j <= i   and   floor(i/B) - floor(j/B) <= W - 1
+ *   (causal; its own block plus the W-1 previous blocks; blocks start at the
+ *   user's first token, never straddle users, and the last may be partial).
+ *   s_ij = scale * <q_i, k_j>,  P = softmax_j(s),  O_i = sum_j P_ij v_j,
+ *   lse_i = ln sum_j exp(s_ij).
+ * The backward pass returns dQ, dK, dV of sum(dO * O) (the production kernel
+ * fuses its backward, "GEM (Meta)", section "Custom kernels").
+ *
+ * Layouts.  q, k, v, out, dout, dq, dk, dv: contiguous [T, H, D] (token-major,
+ * then head, then head_dim), element type given by `dtype`.  lse: fp32 [H, T].
+ * offsets: int32 [batch + 1] in DEVICE memory, offsets[0] = 0, non-decreasing,
+ * offsets[batch] = T; zero-length users are allowed.  All tensor pointers are
+ * device pointers and must be 16-byte aligned.
+ *
+ * Ownership and execution.  The caller owns every buffer.  The library never
+ * allocates, frees or synchronises, keeps no per-call state, and never reads
+ * `offsets` on the host.  Calls are enqueued on `stream` and are asynchronous;
+ * calls on different streams may run concurrently if their outputs do not
+ * overlap.  Outputs are fully overwritten, never accumulated into.  Results are
+ * bitwise deterministic for identical inputs.  Malformed offsets (not
+ * satisfying the rules above) give unspecified values but no out-of-bounds
+ * memory access: every user range is clamped to [0, T].
+ *
+ * Errors.  Return codes only; nothing throws across the ABI.  Argument checks
+ * happen before any HIP call, so an invalid call enqueues nothing.
+ */
+#ifndef BLOCKATTN_H
+#define BLOCKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLOCKATTN_ABI_VERSION 1
+
+typedef enum {
+    BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
+    BLOCKATTN_FP32 = 1  /* fp32 storage and arithmetic                      */
+} blockattn_dtype;
+
+typedef enum {
+    BLOCKATTN_OK = 0,
+    BLOCKATTN_ERR_INVALID_ARGUMENT = 1, /* batch<0, T<0, H<1, B<1, W<1, non-finite
+                                           scale, null or misaligned pointer,
+                                           unknown dtype                        */
+    BLOCKATTN_ERR_UNSUPPORTED = 2,      /* D not in {32,64,128}; B not a multiple
+                                           of 16 or above 256; launch too large  */
+    BLOCKATTN_ERR_WORKSPACE = 3,        /* workspace needed but null, too small
+                                           or not 256-byte aligned              */
+    BLOCKATTN_ERR_HIP = 4               /* a HIP launch reported an error       */
+} blockattn_status;
+
+/*
+ * Forward pass.  Writes out [T,H,D] (dtype) and lse [H,T] (fp32).
+ *   batch          number of users (>= 0); offsets has batch+1 entries
+ *   total_tokens   T = offsets[batch]; T = 0 or batch = 0 returns OK at once
+ *   num_heads      H >= 1;  head_dim D in {32, 64, 128}
+ *   block_size     B, a multiple of 16 in [16, 256]
+ *   window_blocks  W >= 1 (W = 1: independent blocks)
+ *   scale          finite multiplier of <q, k> (typically 1/sqrt(D))
+ */
+blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
+                               const int32_t *offsets, int32_t batch,
+                               int64_t total_tokens, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t window_blocks, float scale,
+                               blockattn_dtype dtype, void *out, float *lse,
+                               hipStream_t stream);
+
+/*
+ * Bytes of device workspace blockattn_bwd needs for these sizes.  The
+ * current kernels recompute every row statistic they need and return 0;
+ * callers should still query it.  Returns SIZE_MAX for invalid sizes.
+ */
+size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t num_heads,
+                                    blockattn_dtype dtype);
+
+/*
+ * Backward pass.  Given the forward inputs, its out and lse, and the upstream
+ * gradient dout, writes dq, dk, dv [T,H,D] (dtype; fp32 accumulation).
+ * workspace: device memory of at least blockattn_bwd_workspace_size() bytes,
+ * 256-byte aligned, owned by the caller, contents on entry ignored; it may be
+ * reused once the stream has passed this call, and may be null when the size
+ * is 0.  Other arguments as for blockattn_fwd.
+ */
+blockattn_status blockattn_bwd(const void *q, const void *k, const void *v,
+                               const void *out, const void *dout,
+                               const float *lse, const int32_t *offsets,
+                               int32_t batch, int64_t total_tokens,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t block_size, int32_t window_blocks,
+                               float scale, blockattn_dtype dtype, void *dq,
+                               void *dk, void *dv, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *blockattn_status_string(blockattn_status status);
+
+/* BLOCKATTN_ABI_VERSION of the loaded library. */
+int blockattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKATTN_H */

@@ -1,1 +1,9 @@
-"""MI355X-native jagged block attention (binding package; see binding.py)."""
+"""MI355X-native (gfx950) jagged block attention.
+
+The computation runs in the HIP library built from ``csrc/`` and exposed
+through the C ABI of ``include/blockattn.h``; ``binding`` is its ctypes
+binding.  ``workloads`` draws the seeded synthetic inputs.
+"""
+from .binding import (BF16, FP32, BlockAttnError, blockattn_abi_version,  # noqa: F401
+                      blockattn_bwd, blockattn_bwd_workspace_size, blockattn_fwd,
+                      blockattn_status_string, bwd, fwd, library_path, load)

@@ -1,0 +1,166 @@
+"""Thin ctypes binding of the block-attention C ABI (include/blockattn.h).
+
+Functions named like the C entry points take raw device pointers and sizes
+and return the status code, exactly as the C ABI does.  ``fwd`` and ``bwd``
+are conveniences that take torch tensors (torch only provides device memory
+and the stream), allocate the outputs, call the C ABI and raise on error.
+Every step of the computation runs in the HIP library; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB, build_library
+
+BF16, FP32 = 0, 1
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+
+# Every symbol include/blockattn.h declares.
+EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
+           "blockattn_status_string", "blockattn_abi_version")
+
+_lib = None
+
+
+class BlockAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB
+
+
+def load() -> ctypes.CDLL:
+    """Loads the built library (building it first only if none is built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        build_library()
+    lib = ctypes.CDLL(LIB)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.blockattn_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32,
+                                  ctypes.c_int, vp, vp, vp]
+    lib.blockattn_fwd.restype = ctypes.c_int
+    lib.blockattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                  i32, f32, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t,
+                                  vp]
+    lib.blockattn_bwd.restype = ctypes.c_int
+    lib.blockattn_bwd_workspace_size.argtypes = [i64, i32, ctypes.c_int]
+    lib.blockattn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.blockattn_status_string.argtypes = [ctypes.c_int]
+    lib.blockattn_status_string.restype = ctypes.c_char_p
+    lib.blockattn_abi_version.argtypes = []
+    lib.blockattn_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- raw C ABI
+
+
+def blockattn_fwd(q, k, v, offsets, batch, total_tokens, num_heads, head_dim,
+                  block_size, window_blocks, scale, dtype, out, lse, stream) -> int:
+    return load().blockattn_fwd(q, k, v, offsets, batch, total_tokens, num_heads,
+                                head_dim, block_size, window_blocks, scale, dtype,
+                                out, lse, stream)
+
+
+def blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads,
+                  head_dim, block_size, window_blocks, scale, dtype, dq, dk, dv,
+                  workspace, workspace_bytes, stream) -> int:
+    return load().blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens,
+                                num_heads, head_dim, block_size, window_blocks, scale,
+                                dtype, dq, dk, dv, workspace, workspace_bytes, stream)
+
+
+def blockattn_bwd_workspace_size(total_tokens, num_heads, dtype) -> int:
+    return int(load().blockattn_bwd_workspace_size(total_tokens, num_heads, dtype))
+
+
+def blockattn_status_string(status: int) -> str:
+    return load().blockattn_status_string(status).decode()
+
+
+def blockattn_abi_version() -> int:
+    return int(load().blockattn_abi_version())
+
+
+status_string = blockattn_status_string
+
+# ------------------------------------------------------ torch conveniences
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _check(q, k, v, offsets):
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [T, H, D] tensors of one shape")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
+        raise ValueError("offsets must be a 1-D int32 device tensor")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
+        out=None, lse=None, stream=None):
+    """Forward block attention.  Returns (out [T,H,D], lse fp32 [H,T])."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    rc = blockattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                       offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                       float(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr(),
+                       _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_fwd", rc)
+    return out, lse
+
+
+def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
+        scale: float, grads=None, workspace=None, stream=None):
+    """Backward block attention.  Returns (dq, dk, dv), each [T,H,D]."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    for t in (out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("out and dout must match q")
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    code = _dtype_code(q)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    dq, dk, dv = grads
+    need = blockattn_bwd_workspace_size(T, H, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    rc = blockattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
+                       offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                       float(scale), code, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       ws_ptr, ws_len, _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_bwd", rc)
+    return dq, dk, dv

@@ -1,0 +1,127 @@
+// C ABI of the block-attention library: argument checks, then dispatch to
+// the HIP kernels.  The operation, layouts and error rules are documented in
+// include/blockattn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/blockattn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by the forward and backward entry points.  Returns OK when
+// the call is valid and has work to do, OK with *empty set when it is valid
+// and empty, or an error code.
+blockattn_status check_common(const int32_t *offsets, int32_t batch, int64_t T,
+                              int32_t H, int32_t D, int32_t B, int32_t W, float scale,
+                              blockattn_dtype dtype, bool *empty) {
+    *empty = false;
+    if (batch < 0 || T < 0 || H < 1 || B < 1 || W < 1 || !isfinite(scale))
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (dtype != BLOCKATTN_BF16 && dtype != BLOCKATTN_FP32)
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (D != 32 && D != 64 && D != 128) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (B % 16 != 0 || B > 256) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (T > INT32_MAX) return BLOCKATTN_ERR_UNSUPPORTED;
+    // every launch's grid is bounded by H * (T/B + batch) * ceil(B/32)
+    const int64_t tiles = ((T + B - 1) / B + batch) * (int64_t)((B + 31) / 32) * H;
+    if (tiles > (int64_t)INT32_MAX - 64) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (T == 0 || batch == 0) {
+        *empty = true;
+        return BLOCKATTN_OK;
+    }
+    if (!offsets) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    return BLOCKATTN_OK;
+}
+
+ba::Shape make_shape(const int32_t *offsets, int32_t batch, int64_t T, int32_t H, int32_t D,
+                     int32_t B, int32_t W, float scale) {
+    ba::Shape s;
+    s.offsets = offsets;
+    s.batch = batch;
+    s.T = T;
+    s.H = H;
+    s.D = D;
+    s.B = B;
+    s.W = W;
+    s.scale = scale;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int blockattn_abi_version(void) { return BLOCKATTN_ABI_VERSION; }
+
+const char *blockattn_status_string(blockattn_status status) {
+    switch (status) {
+    case BLOCKATTN_OK: return "ok";
+    case BLOCKATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BLOCKATTN_ERR_UNSUPPORTED: return "unsupported size";
+    case BLOCKATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case BLOCKATTN_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t num_heads,
+                                    blockattn_dtype dtype) {
+    if (total_tokens < 0 || num_heads < 1 ||
+        (dtype != BLOCKATTN_BF16 && dtype != BLOCKATTN_FP32))
+        return SIZE_MAX;
+    // The backward kernels recompute every row statistic they need (delta =
+    // <dO, O>) from their inputs, so no device workspace is needed.
+    return 0;
+}
+
+blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
+                               const int32_t *offsets, int32_t batch, int64_t total_tokens,
+                               int32_t num_heads, int32_t head_dim, int32_t block_size,
+                               int32_t window_blocks, float scale, blockattn_dtype dtype,
+                               void *out, float *lse, hipStream_t stream) {
+    bool empty;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
+                                       block_size, window_blocks, scale, dtype, &empty);
+    if (st != BLOCKATTN_OK || empty) return st;
+    if (!q || !k || !v || !out || !lse) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
+                                   block_size, window_blocks, scale);
+    hipError_t e = ba::launch_scalar_fwd(s, dtype == BLOCKATTN_BF16, q, k, v, out, lse,
+                                         stream);
+    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+}
+
+blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, const void *out,
+                               const void *dout, const float *lse, const int32_t *offsets,
+                               int32_t batch, int64_t total_tokens, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int32_t window_blocks,
+                               float scale, blockattn_dtype dtype, void *dq, void *dk,
+                               void *dv, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    bool empty;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
+                                       block_size, window_blocks, scale, dtype, &empty);
+    if (st != BLOCKATTN_OK || empty) return st;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const size_t need = blockattn_bwd_workspace_size(total_tokens, num_heads, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
+        return BLOCKATTN_ERR_WORKSPACE;
+    const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
+                                   block_size, window_blocks, scale);
+    hipError_t e = ba::launch_scalar_bwd(s, dtype == BLOCKATTN_BF16, q, k, v, out, dout, lse,
+                                         dq, dk, dv, stream);
+    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every symbol include/blockattn.h declares,
+and rejects invalid arguments before touching the GPU (no compute here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_sequence_block_amd as lsb
+from long_sequence_block_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blockattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(blockattn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lsb.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lsb.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(blockattn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings():
+    assert lsb.blockattn_abi_version() == 1
+    names = [lsb.blockattn_status_string(s) for s in range(5)]
+    assert len(set(names)) == 5 and names[0] == "ok"
+    assert lsb.blockattn_status_string(99) == "unknown status"
+
+
+FAKE = 0x1000  # aligned non-null pointer value; never dereferenced on these paths
+
+
+def fwd_status(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, offsets=FAKE, batch=2, total_tokens=100,
+             num_heads=2, head_dim=64, block_size=64, window_blocks=2, scale=0.125,
+             dtype=lsb.BF16, out=FAKE, lse=FAKE, stream=None)
+    a.update(kw)
+    return lsb.blockattn_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), binding.ERR_INVALID_ARGUMENT),
+    (dict(total_tokens=-5), binding.ERR_INVALID_ARGUMENT),
+    (dict(num_heads=0), binding.ERR_INVALID_ARGUMENT),
+    (dict(block_size=0), binding.ERR_INVALID_ARGUMENT),
+    (dict(window_blocks=0), binding.ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), binding.ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), binding.ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), binding.ERR_INVALID_ARGUMENT),
+    (dict(head_dim=48), binding.ERR_UNSUPPORTED),
+    (dict(head_dim=256), binding.ERR_UNSUPPORTED),
+    (dict(block_size=40), binding.ERR_UNSUPPORTED),
+    (dict(block_size=512), binding.ERR_UNSUPPORTED),
+    (dict(q=None), binding.ERR_INVALID_ARGUMENT),
+    (dict(lse=None), binding.ERR_INVALID_ARGUMENT),
+    (dict(offsets=None), binding.ERR_INVALID_ARGUMENT),
+    (dict(out=FAKE + 8), binding.ERR_INVALID_ARGUMENT),
+    (dict(total_tokens=0, q=None, offsets=None), binding.OK),
+    (dict(batch=0, q=None, offsets=None), binding.OK),
+])
+def test_fwd_argument_checks(kw, code):
+    assert fwd_status(**kw) == code
+
+
+def bwd_status(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, offsets=FAKE,
+             batch=2, total_tokens=100, num_heads=2, head_dim=64, block_size=64,
+             window_blocks=2, scale=0.125, dtype=lsb.BF16, dq=FAKE, dk=FAKE, dv=FAKE,
+             workspace=FAKE, workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lsb.blockattn_bwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), binding.ERR_INVALID_ARGUMENT),
+    (dict(dv=FAKE + 4), binding.ERR_INVALID_ARGUMENT),
+    (dict(head_dim=16), binding.ERR_UNSUPPORTED),
+    (dict(total_tokens=0, q=None, workspace=None), binding.OK),
+])
+def test_bwd_argument_checks(kw, code):
+    assert bwd_status(**kw) == code
+
+
+def test_workspace_size():
+    assert lsb.blockattn_bwd_workspace_size(0, 8, lsb.BF16) == 0
+    n = lsb.blockattn_bwd_workspace_size(213551, 8, lsb.BF16)
+    assert n % 256 == 0
+    assert lsb.blockattn_bwd_workspace_size(-1, 8, lsb.BF16) == ctypes.c_size_t(-1).value
+    assert lsb.blockattn_bwd_workspace_size(10, 0, lsb.BF16) == ctypes.c_size_t(-1).value
