@@ -92,8 +92,9 @@ blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
                                    block_size, window_blocks, scale);
-    hipError_t e = ba::launch_scalar_fwd(s, dtype == BLOCKATTN_BF16, q, k, v, out, lse,
-                                         stream);
+    hipError_t e = dtype == BLOCKATTN_BF16
+                       ? ba::launch_mfma_fwd(s, q, k, v, out, lse, stream)
+                       : ba::launch_scalar_fwd(s, false, q, k, v, out, lse, stream);
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 

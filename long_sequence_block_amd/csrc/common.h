@@ -34,7 +34,7 @@ struct Shape {
     float scale;
 };
 
-// One tile of work: sub-tile `sub` of block `blk` (local to the user), head
+// One tile of work: sub-tile `sub` of row unit `blk` (local to the user), head
 // h, of user `user` whose tokens start at packed index tok0 and who has len
 // tokens.  Callers turn `sub` into rows (and, for the backward, a role).
 struct Tile {
@@ -51,12 +51,13 @@ __device__ __forceinline__ int64_t clamp_off(int32_t o, int64_t T) {
     return x < 0 ? 0 : (x > T ? T : x);
 }
 
-// Tiles of user u: ceil(L/B) blocks, each with tpb sub-tiles, times H heads.
-__device__ __forceinline__ int64_t user_tiles(const Shape &s, int u, int tpb) {
+// Tiles of user u: ceil(L/R) row units of R rows, each with tpb sub-tiles,
+// times H heads.
+__device__ __forceinline__ int64_t user_tiles(const Shape &s, int u, int R, int tpb) {
     const int64_t a = clamp_off(s.offsets[u], s.T);
     const int64_t b = clamp_off(s.offsets[u + 1], s.T);
     const int64_t L = b > a ? b - a : 0;
-    return ((L + s.B - 1) / s.B) * (int64_t)tpb * s.H;
+    return ((L + R - 1) / R) * (int64_t)tpb * s.H;
 }
 
 // Inclusive prefix sum over the NT threads of a workgroup (NT a multiple of
@@ -80,9 +81,10 @@ __device__ __forceinline__ int64_t wg_inclusive_scan(int64_t v, int64_t *sh) {
     return v;
 }
 
-// Maps this workgroup to its tile.  The logical tile order is user-major,
-// then block, then sub-tile (tpb per block), then head, so the tiles that
-// share a K/V block (same user and head, neighbouring blocks) are close.
+// Maps this workgroup to its tile.  A user's rows are cut into units of R
+// rows (t.blk is the unit index); the logical tile order is user-major, then
+// unit, then sub-tile (tpb per unit), then head, so the tiles that share K/V
+// rows (same user and head, neighbouring units) are close.
 // Consecutive workgroup ids are dealt round-robin over the 8 XCDs of the
 // chip; the remap below gives each XCD one contiguous run of logical tiles
 // (so neighbouring blocks share that XCD's L2) and balances the real tile
@@ -90,13 +92,13 @@ __device__ __forceinline__ int64_t wg_inclusive_scan(int64_t v, int64_t *sh) {
 // the real tile count rounded up to one.  Returns false for an idle
 // workgroup.  `sh` must hold NT/64 + 4 int64 values in LDS.
 template <int NT>
-__device__ bool decode_tile(const Shape &s, int tpb, Tile &t, int64_t *sh) {
+__device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int64_t *sh) {
     const int tid = threadIdx.x;
     // pass 1: total number of tiles
     int64_t total = 0;
     for (int c0 = 0; c0 < s.batch; c0 += NT) {
         const int u = c0 + tid;
-        const int64_t n = u < s.batch ? user_tiles(s, u, tpb) : 0;
+        const int64_t n = u < s.batch ? user_tiles(s, u, R, tpb) : 0;
         const int64_t inc = wg_inclusive_scan<NT>(n, sh);
         if (tid == NT - 1) sh[NT / 64] = inc;
         __syncthreads();
@@ -113,7 +115,7 @@ __device__ bool decode_tile(const Shape &s, int tpb, Tile &t, int64_t *sh) {
     int64_t base = 0;
     for (int c0 = 0; c0 < s.batch; c0 += NT) {
         const int u = c0 + tid;
-        const int64_t n = u < s.batch ? user_tiles(s, u, tpb) : 0;
+        const int64_t n = u < s.batch ? user_tiles(s, u, R, tpb) : 0;
         const int64_t inc = wg_inclusive_scan<NT>(n, sh);
         if (u < s.batch && n > 0 && lt >= base + inc - n && lt < base + inc) {
             sh[NT / 64 + 1] = u;
@@ -142,9 +144,9 @@ __device__ bool decode_tile(const Shape &s, int tpb, Tile &t, int64_t *sh) {
 }
 
 // Grid size for a tile space: an upper bound on the real tile count
-// (sum_u ceil(L_u/B) <= T/B + batch), rounded up to a multiple of 8.
-inline int64_t grid_upper_bound(int64_t T, int batch, int B, int tpb, int H) {
-    const int64_t blocks = (T + B - 1) / B + batch;
+// (sum_u ceil(L_u/R) <= T/R + batch), rounded up to a multiple of 8.
+inline int64_t grid_upper_bound(int64_t T, int batch, int R, int tpb, int H) {
+    const int64_t blocks = (T + R - 1) / R + batch;
     const int64_t g = blocks * tpb * H;
     return (g + 7) / 8 * 8;
 }

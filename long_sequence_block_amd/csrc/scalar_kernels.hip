@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restric
     __shared__ float ks[kChunk][D + 1];
     __shared__ float vs[kChunk][D + 1];
     Tile t;
-    if (!decode_tile<kRows>(s, tpb, t, sh)) return;
+    if (!decode_tile<kRows>(s, s.B, tpb, t, sh)) return;
     const int lane = threadIdx.x;
     const int64_t rs = (int64_t)s.H * D;
     const int row0 = t.blk * s.B + t.sub * kRows;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kRows) void bwd_scalar(
     __shared__ float bs[kChunk][D + 1];
     __shared__ float ls[kChunk], dls[kChunk];
     Tile t;
-    if (!decode_tile<kRows>(s, 2 * tpb, t, sh)) return;
+    if (!decode_tile<kRows>(s, s.B, 2 * tpb, t, sh)) return;
     const int row0 = t.blk * s.B + (t.sub % tpb) * kRows;
     if (t.sub < tpb)
         bwd_dq_tile<TI, D>(s, t, row0, q, k, v, out, dout, lse, dq, as, bs);
