@@ -120,8 +120,10 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
         return BLOCKATTN_ERR_WORKSPACE;
     const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
                                    block_size, window_blocks, scale);
-    hipError_t e = ba::launch_scalar_bwd(s, dtype == BLOCKATTN_BF16, q, k, v, out, dout, lse,
-                                         dq, dk, dv, stream);
+    hipError_t e = dtype == BLOCKATTN_BF16
+                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, stream)
+                       : ba::launch_scalar_bwd(s, false, q, k, v, out, dout, lse, dq, dk, dv,
+                                               stream);
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 
