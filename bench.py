@@ -102,6 +102,28 @@ def cpu_baseline(w, users: int, flops_per_pair_head: float):
             "seconds": dt}
 
 
+def copy_calibration(mib: int, steps: int, warmup: int):
+    """Times torch's device-to-device copy of a known size: its HBM byte
+    counters (read mib MiB, write mib MiB per launch) calibrate the counters
+    taken on the attention kernels."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": ms,
+                      "GB_per_s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,19 +136,26 @@ def main():
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-users", type=int, default=64)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the workload, time a plain device copy of MIB MiB "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
             print("bench.py measures one GPU only: this build has no multi-GPU path "
-                  "(users and heads shard across GPUs with no exchange; see DESIGN.md). "
+                  "(users and heads would shard across GPUs with no exchange). "
                   "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import long_sequence_block_amd as lsb
     from long_sequence_block_amd import workloads as wl
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps, args.warmup)
+        return
 
     w = wl.WORKLOADS[args.workload]
     if args.length:

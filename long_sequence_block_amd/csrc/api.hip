@@ -28,7 +28,7 @@ blockattn_status check_common(const int32_t *offsets, int32_t batch, int64_t T,
     if (T > INT32_MAX) return BLOCKATTN_ERR_UNSUPPORTED;
     // every launch's grid is bounded by H * (T/B + batch) * ceil(B/32)
     const int64_t tiles = ((T + B - 1) / B + batch) * (int64_t)((B + 31) / 32) * H;
-    if (tiles > (int64_t)INT32_MAX - 64) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (tiles > (int64_t)INT32_MAX - 1024) return BLOCKATTN_ERR_UNSUPPORTED;
     if (T == 0 || batch == 0) {
         *empty = true;
         return BLOCKATTN_OK;

@@ -46,109 +46,101 @@ struct Tile {
     int len;
 };
 
-__device__ __forceinline__ int64_t clamp_off(int32_t o, int64_t T) {
-    int64_t x = o;
-    return x < 0 ? 0 : (x > T ? T : x);
-}
-
-// Tiles of user u: ceil(L/R) row units of R rows, each with tpb sub-tiles,
-// times H heads.
-__device__ __forceinline__ int64_t user_tiles(const Shape &s, int u, int R, int tpb) {
-    const int64_t a = clamp_off(s.offsets[u], s.T);
-    const int64_t b = clamp_off(s.offsets[u + 1], s.T);
-    const int64_t L = b > a ? b - a : 0;
-    return ((L + R - 1) / R) * (int64_t)tpb * s.H;
-}
+__device__ __forceinline__ int clamp_off(int32_t o, int T) { return o < 0 ? 0 : (o > T ? T : o); }
 
 // Inclusive prefix sum over the NT threads of a workgroup (NT a multiple of
-// 64): wave-level shuffles, then one LDS pass over the wave totals.
+// 64): wave-level shuffles, then one LDS pass over the wave totals.  Also
+// returns the workgroup total.  `sh` holds NT/64 ints.
 template <int NT>
-__device__ __forceinline__ int64_t wg_inclusive_scan(int64_t v, int64_t *sh) {
+__device__ __forceinline__ int wg_inclusive_scan(int v, int *sh, int &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = __shfl_up(v, o, 64);
+        const int y = __shfl_up(v, o, 64);
         if (lane >= o) v += y;
     }
-    if (NT > 64) {
-        if (lane == 63) sh[wave] = v;
-        __syncthreads();
-        int64_t add = 0;
-        for (int w = 0; w < wave; ++w) add += sh[w];
-        v += add;
-        __syncthreads();
+    if (NT == 64) {
+        total = __shfl(v, 63, 64);
+        return v;
     }
-    return v;
+    if (lane == 63) sh[wave] = v;
+    __syncthreads();
+    int add = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int x = sh[w];
+        add += w < wave ? x : 0;
+        tot += x;
+    }
+    __syncthreads();
+    total = tot;
+    return v + add;
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs in id order.  The logical
+// tile of a workgroup is chosen so that each XCD works through runs of kRun
+// consecutive logical tiles: neighbouring tiles, which read the same K/V
+// rows, then share one XCD's L2.  The map is a bijection on [0, grid) when
+// grid is a multiple of 8 * kRun.
+constexpr int kRun = 16;
+__device__ __forceinline__ int logical_tile() {
+    const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+    return ((j / kRun) * 8 + xcd) * kRun + (j % kRun);
 }
 
 // Maps this workgroup to its tile.  A user's rows are cut into units of R
-// rows (t.blk is the unit index); the logical tile order is user-major, then
-// unit, then sub-tile (tpb per unit), then head, so the tiles that share K/V
-// rows (same user and head, neighbouring units) are close.
-// Consecutive workgroup ids are dealt round-robin over the 8 XCDs of the
-// chip; the remap below gives each XCD one contiguous run of logical tiles
-// (so neighbouring blocks share that XCD's L2) and balances the real tile
-// count over the XCDs.  Needs gridDim.x to be a multiple of 8 and at least
-// the real tile count rounded up to one.  Returns false for an idle
-// workgroup.  `sh` must hold NT/64 + 4 int64 values in LDS.
+// rows; the logical order is user, then head, then unit, then sub-tile (tpb
+// per unit), so consecutive tiles are consecutive row units of one (user,
+// head).  Tiles exist only for rows that exist: a jagged batch costs no
+// padding.  Returns false for a workgroup beyond the last tile (the grid is
+// an upper bound, since the host never reads the offsets).  `sh` must hold
+// NT/64 + 3 ints in LDS.  All results are wave-uniform.
 template <int NT>
-__device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int64_t *sh) {
+__device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
     const int tid = threadIdx.x;
-    // pass 1: total number of tiles
-    int64_t total = 0;
+    const int lt = logical_tile();
+    const int T = (int)s.T;
+    int base = 0;
     for (int c0 = 0; c0 < s.batch; c0 += NT) {
         const int u = c0 + tid;
-        const int64_t n = u < s.batch ? user_tiles(s, u, R, tpb) : 0;
-        const int64_t inc = wg_inclusive_scan<NT>(n, sh);
-        if (tid == NT - 1) sh[NT / 64] = inc;
-        __syncthreads();
-        total += sh[NT / 64];
-        __syncthreads();
-    }
-    // XCD-aware remap of the workgroup id onto a logical tile
-    const int xcd = blockIdx.x & 7;
-    const int64_t j = blockIdx.x >> 3;
-    const int64_t per = total >> 3, rem = total & 7;
-    if (j >= per + (xcd < rem ? 1 : 0)) return false;
-    const int64_t lt = xcd * per + (xcd < rem ? xcd : rem) + j;
-    // pass 2: find the user whose tile range holds lt
-    int64_t base = 0;
-    for (int c0 = 0; c0 < s.batch; c0 += NT) {
-        const int u = c0 + tid;
-        const int64_t n = u < s.batch ? user_tiles(s, u, R, tpb) : 0;
-        const int64_t inc = wg_inclusive_scan<NT>(n, sh);
-        if (u < s.batch && n > 0 && lt >= base + inc - n && lt < base + inc) {
-            sh[NT / 64 + 1] = u;
-            sh[NT / 64 + 2] = lt - (base + inc - n);
+        int n = 0;
+        if (u < s.batch) {
+            const int a = clamp_off(s.offsets[u], T), b = clamp_off(s.offsets[u + 1], T);
+            const int L = b > a ? b - a : 0;
+            n = (L + R - 1) / R * tpb * s.H;
         }
-        if (tid == NT - 1) sh[NT / 64] = inc;
-        __syncthreads();
-        const int64_t chunk = sh[NT / 64];
-        const bool done = lt < base + chunk;
+        int chunk;
+        const int incl = wg_inclusive_scan<NT>(n, sh, chunk);
+        if (n > 0 && lt >= base + incl - n && lt < base + incl) {
+            sh[NT / 64] = u;
+            sh[NT / 64 + 1] = lt - (base + incl - n);
+        }
         base += chunk;
-        if (done) break;
-        __syncthreads();
+        if (lt < base) break;  // uniform: base and lt are the same in every thread
     }
-    const int u = (int)sh[NT / 64 + 1];
-    const int64_t local = sh[NT / 64 + 2];
-    const int64_t h = local % s.H;
-    const int64_t rest = local / s.H;
+    if (lt >= base) return false;
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(sh[NT / 64]);
+    const int local = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 1]);
+    const int a = clamp_off(s.offsets[u], T), b = clamp_off(s.offsets[u + 1], T);
+    const int L = b > a ? b - a : 0;
+    const int per_head = (L + R - 1) / R * tpb;
     t.user = u;
-    t.h = (int)h;
-    t.blk = (int)(rest / tpb);
-    t.sub = (int)(rest % tpb);
-    t.tok0 = clamp_off(s.offsets[u], s.T);
-    const int64_t e = clamp_off(s.offsets[u + 1], s.T);
-    t.len = (int)(e > t.tok0 ? e - t.tok0 : 0);
+    t.h = local / per_head;
+    const int rem = local - t.h * per_head;
+    t.blk = rem / tpb;
+    t.sub = rem - t.blk * tpb;
+    t.tok0 = a;
+    t.len = L;
     return true;
 }
 
 // Grid size for a tile space: an upper bound on the real tile count
-// (sum_u ceil(L_u/R) <= T/R + batch), rounded up to a multiple of 8.
+// (sum_u ceil(L_u/R) <= T/R + batch), rounded up to a multiple of 8 * kRun.
 inline int64_t grid_upper_bound(int64_t T, int batch, int R, int tpb, int H) {
     const int64_t blocks = (T + R - 1) / R + batch;
     const int64_t g = blocks * tpb * H;
-    return (g + 7) / 8 * 8;
+    return (g + 8 * kRun - 1) / (8 * kRun) * (8 * kRun);
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void bwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ out, const bf16 *__restrict__ dout, const float *__restrict__ lse,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
-    __shared__ int64_t sh[8];
+    __shared__ int sh[8];
     __shared__ __align__(16) BwdSmem<D> sm;
     Tile t;
     if (!decode_tile<kThreads>(s, kTileRows, 2, t, sh)) return;

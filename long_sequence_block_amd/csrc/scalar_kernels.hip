@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restric
                                                     const TI *__restrict__ v,
                                                     TI *__restrict__ out,
                                                     float *__restrict__ lse, int tpb) {
-    __shared__ int64_t sh[8];
+    __shared__ int sh[8];
     __shared__ float ks[kChunk][D + 1];
     __shared__ float vs[kChunk][D + 1];
     Tile t;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kRows) void bwd_scalar(
     Shape s, const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
     const TI *__restrict__ out, const TI *__restrict__ dout, const float *__restrict__ lse,
     TI *__restrict__ dq, TI *__restrict__ dk, TI *__restrict__ dv, int tpb) {
-    __shared__ int64_t sh[8];
+    __shared__ int sh[8];
     __shared__ float as[kChunk][D + 1];
     __shared__ float bs[kChunk][D + 1];
     __shared__ float ls[kChunk], dls[kChunk];
