@@ -35,8 +35,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "block-attention TFLOP/s and tokens/s (fwd+bwd, jagged bf16) and % of MFMA peak"
-KERNEL_SOURCES = ("common.h", "kernels.h", "api.hip", "scalar_kernels.hip",
-                  "mfma_fwd.hip", "mfma_bwd.hip")
+KERNEL_SOURCES = ("common.h", "kernels.h", "mfma_util.h", "lds_tile.h", "api.hip",
+                  "scalar_kernels.hip", "mfma_fwd.hip", "mfma_bwd.hip")
 
 
 def pairs_per_head(offsets: np.ndarray, B: int, W: int) -> int:
@@ -135,7 +135,8 @@ def main():
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-users", type=int, default=64)
+    ap.add_argument("--cpu-users", type=int, default=0,
+                    help="users timed for the oracle baseline (default: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, time a plain device copy of MIB MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -251,7 +252,7 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        users = min(args.cpu_users, w.users)
+        users = min(args.cpu_users, w.users) if args.cpu_users > 0 else w.users
         res["cpu_baseline"] = cpu_baseline(w, users, 4.0 * D + (8.0 * D if w.backward else 0))
     print(json.dumps(res), flush=True)
 
