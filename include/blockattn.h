@@ -87,9 +87,10 @@ blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
                                hipStream_t stream);
 
 /*
- * Bytes of device workspace blockattn_bwd needs for these sizes.  The
- * current kernels recompute every row statistic they need and return 0;
- * callers should still query it.  Returns SIZE_MAX for invalid sizes.
+ * Bytes of device workspace blockattn_bwd needs for these sizes: for bf16,
+ * two fp32 row statistics per (head, token) (delta = <dO, O> and lse in base
+ * 2), i.e. 8 * H * T bytes rounded up to 256; 0 for fp32.  Returns SIZE_MAX
+ * for invalid sizes.
  */
 size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t num_heads,
                                     blockattn_dtype dtype);

@@ -4,7 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/blockattn.h"
+#include "blockattn.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -73,9 +73,11 @@ size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t num_heads,
     if (total_tokens < 0 || num_heads < 1 ||
         (dtype != BLOCKATTN_BF16 && dtype != BLOCKATTN_FP32))
         return SIZE_MAX;
-    // The backward kernels recompute every row statistic they need (delta =
-    // <dO, O>) from their inputs, so no device workspace is needed.
-    return 0;
+    if (dtype == BLOCKATTN_FP32) return 0;  // the fp32 kernels need no workspace
+    // bf16: two fp32 [H, T] row statistics (lse * log2 e and delta), 256-byte
+    // granularity.
+    const size_t bytes = (size_t)2 * (size_t)num_heads * (size_t)total_tokens * sizeof(float);
+    return (bytes + 255) / 256 * 256;
 }
 
 blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
@@ -121,7 +123,8 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
     const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
                                    block_size, window_blocks, scale);
     hipError_t e = dtype == BLOCKATTN_BF16
-                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, stream)
+                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, (float *)workspace,
+                                             stream)
                        : ba::launch_scalar_bwd(s, false, q, k, v, out, dout, lse, dq, dk, dv,
                                                stream);
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;

@@ -18,9 +18,11 @@ hipError_t launch_scalar_bwd(const Shape &s, bool bf16_io, const void *q, const 
 hipError_t launch_mfma_fwd(const Shape &s, const void *q, const void *k, const void *v,
                            void *out, float *lse, hipStream_t st);
 
-// bf16 MFMA backward (one launch: query-role and key-role workgroups).
+// bf16 MFMA backward: a row-statistics launch (delta, lse * log2 e into the
+// workspace `ws`, 2 * H * T floats) and one launch of query-role and
+// key-role workgroups.
 hipError_t launch_mfma_bwd(const Shape &s, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *dq,
-                           void *dk, void *dv, hipStream_t st);
+                           void *dk, void *dv, float *ws, hipStream_t st);
 
 }  // namespace ba

@@ -9,12 +9,13 @@
 //                                    dV_j = sum_i P_ij dO_i
 //
 // with P_ij = exp(scale <q_i,k_j> - lse_i), dP_ij = <dO_i, v_j>,
-// dS_ij = P_ij (dP_ij - delta_i) and delta_i = <dO_i, O_i>, recomputed by
-// both roles from O and dO.  Each output element has exactly one owner, so
-// there are no atomics and no workspace, and the result is deterministic.
-// Visibility is the block window: local query i sees local key j iff j <= i
-// and floor(i/B) - floor(j/B) < W, so key j is seen by queries
-// j <= i < (floor(j/B) + W) * B.
+// dS_ij = P_ij (dP_ij - delta_i) and delta_i = <dO_i, O_i>.  A first,
+// memory-bound launch writes delta and lse * log2(e) of every row to the
+// workspace; the main launch then never reads O.  Each output element of the
+// main launch has exactly one owner, so there are no atomics and the result
+// is deterministic.  Visibility is the block window: local query i sees
+// local key j iff j <= i and floor(i/B) - floor(j/B) < W, so key j is seen by
+// queries j <= i < (floor(j/B) + W) * B.
 //
 // Layouts follow the forward kernel: 32x32x16 bf16 MFMAs, one query (query
 // role) or one key (key role) per lane column; streamed rows sit in LDS
@@ -22,10 +23,8 @@
 // of the next product, and the products that contract along the streamed
 // rows read them with transposed LDS reads.  The query role keeps its Q and
 // dO rows in registers and streams K and V; the key role keeps K and V rows
-// and streams Q, dO, O and lse.  Chunks of 64 rows go from HBM straight into
-// three rotating LDS tiles; the key role computes delta (and lse * log2 e)
-// of chunk c+1 from the LDS copies while chunk c is consumed, so it needs no
-// extra barrier.
+// and streams Q, dO and the two row statistics.  Chunks of 64 rows go from
+// HBM straight into two LDS buffers in turn, one barrier per chunk.
 #include "kernels.h"
 #include "lds_tile.h"
 
@@ -35,24 +34,19 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kTileRows = 128;
 constexpr int kKC = 64;        // rows per streamed chunk
-constexpr int NB = 3;          // LDS chunk buffers in rotation
+constexpr int NB = 2;          // LDS chunk buffers in rotation
 
 // Waves per SIMD the register budget is sized for.
 template <int D>
 constexpr int kWavesPerSimd = D == 128 ? 1 : 2;
 
 // One chunk buffer: the query role uses tiles 0 (K) and 1 (V), the key role
-// tiles 0 (Q), 1 (dO), 2 (O) and the raw lse of the chunk's queries.
+// tiles 0 (Q) and 1 (dO) and the row statistics of the chunk's queries.
 template <int D>
 struct BwdChunk {
-    bf16 t[3][kKC * D];
-    float lse[kKC];
-};
-template <int D>
-struct BwdSmem {
-    BwdChunk<D> c[NB];
-    float lse2[NB][kKC];  // lse * log2(e), per key-role chunk
-    float dlt[NB][kKC];   // delta, per key-role chunk
+    bf16 t[2][kKC * D];
+    float lse2[kKC];  // lse * log2(e)
+    float dlt[kKC];   // delta
 };
 
 template <int D>
@@ -92,16 +86,6 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b, float acc) {
                                            __builtin_shufflevector(b, b, 6, 7), acc, false);
 }
 
-// Waits for the chunk about to be consumed and joins the barrier; `ahead`
-// says whether the next chunk's loads (kDma instructions) may stay in flight.
-template <int kDma>
-__device__ __forceinline__ void chunk_barrier(bool ahead) {
-    if (ahead)
-        wait_vm_barrier<kDma>();
-    else
-        wait_vm_barrier<0>();
-}
-
 // Per-lane LDS offsets shared by both roles.
 template <int D>
 struct ReadOffsets {
@@ -121,10 +105,10 @@ struct ReadOffsets {
 // ------------------------------------------------------------ query role
 
 template <int D>
-__device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave,
+__device__ void query_role(const Shape &s, const Tile &t, BwdChunk<D> *sm, int wave,
                            const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                           const bf16 *__restrict__ v, const bf16 *__restrict__ out,
-                           const bf16 *__restrict__ dout, const float *__restrict__ lse,
+                           const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
+                           const float *__restrict__ ws_lse2, const float *__restrict__ ws_dlt,
                            bf16 *__restrict__ dq) {
     using G = TileGeom<D>;
     constexpr int kDma = 2 * G::kDmaPerWave;
@@ -150,7 +134,7 @@ __device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wa
     const int nch = (row_end - kbeg + kKC - 1) / kKC;
     const bf16 *kb = k + base + (int64_t)kbeg * rs;
     const bf16 *vb = v + base + (int64_t)kbeg * rs;
-    lds_t *lds = (lds_t *)&sm;
+    lds_t *lds = (lds_t *)sm;
     uint32_t voff[G::kDmaPerWave];
     dma_offsets<D>(voff, wave, lane, rsb);
     auto issue = [&](int ci, int buf) {
@@ -166,15 +150,11 @@ __device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wa
     load_operand<D>(doop, dout + base + (int64_t)my_row * rs, my_valid, g);
     float my_lse2 = 0.f, my_dlt = 0.f;
     if (my_valid) {
-        my_lse2 = lse[(int64_t)t.h * s.T + t.tok0 + my_row] * kLog2e;
-        const bf16 *orow = out + base + (int64_t)my_row * rs;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            my_dlt = dot8(doop[ks], *(const bf16x8 *)(orow + ks * 16 + g * 8), my_dlt);
+        const int64_t i = (int64_t)t.h * s.T + t.tok0 + my_row;
+        my_lse2 = ws_lse2[i];
+        my_dlt = ws_dlt[i];
     }
-    my_dlt = swap_sum(my_dlt);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only tile loads in flight from here
-    if (nch > 1) issue(1, 1);
     const ReadOffsets<D> ro(lane);
 
     f32x16 acc[D / 32];
@@ -183,8 +163,8 @@ __device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wa
 
     auto step = [&](int ci, auto buf_c) {
         constexpr int buf = decltype(buf_c)::value;
-        chunk_barrier<kDma>(ci + 1 < nch);
-        if (ci + 2 < nch) issue(ci + 2, (buf + 2) % NB);
+        wait_vm_barrier<0>();
+        if (ci + 1 < nch) issue(ci + 1, buf ^ 1);
         if (!wave_live) return;
         const lds_t *kt = lds + buf * (int)sizeof(BwdChunk<D>);
         const lds_t *vt = kt + G::kBytes;
@@ -204,13 +184,17 @@ __device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wa
             // my_klo <= key <= my_row
             const int x = a + 8 * g - my_klo;
             const uint32_t span = (uint32_t)(my_row - my_klo);
+            float pr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -my_lse2));
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > span) pr[r] = 0.f;
+            }
             bf16x8 dsb[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -my_lse2));
-                if (masked && (uint32_t)(x + 16 * (r >> 3) + (r & 7)) > span) p = 0.f;
-                dsb[r >> 3][r & 7] = (bf16)(p * (dp[r] - my_dlt));
-            }
+            for (int r = 0; r < 16; ++r) dsb[r >> 3][r & 7] = (bf16)(pr[r] * (dp[r] - my_dlt));
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const lds_t *kr = kt + (sub * 32 + kk * 16) * G::kRowBytes;
@@ -224,7 +208,6 @@ __device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wa
     for (int ci = 0; ci < nch; ci += NB) {
         step(ci, std::integral_constant<int, 0>{});
         if (ci + 1 < nch) step(ci + 1, std::integral_constant<int, 1>{});
-        if (ci + 2 < nch) step(ci + 2, std::integral_constant<int, 2>{});
     }
     if (my_valid) store_out<D>(dq + base + (int64_t)my_row * rs, acc, s.scale, g);
 }
@@ -232,10 +215,10 @@ __device__ void query_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wa
 // -------------------------------------------------------------- key role
 
 template <int D>
-__device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave,
+__device__ void key_role(const Shape &s, const Tile &t, BwdChunk<D> *sm, int wave,
                          const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                         const bf16 *__restrict__ v, const bf16 *__restrict__ out,
-                         const bf16 *__restrict__ dout, const float *__restrict__ lse,
+                         const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
+                         const float *__restrict__ ws_lse2, const float *__restrict__ ws_dlt,
                          bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
     using G = TileGeom<D>;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -260,22 +243,22 @@ __device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave
     const int nch = (qend - row0 + kKC - 1) / kKC;
     const bf16 *qb = q + base + (int64_t)row0 * rs;
     const bf16 *db = dout + base + (int64_t)row0 * rs;
-    const bf16 *ob = out + base + (int64_t)row0 * rs;
-    const float *lsb = lse + (int64_t)t.h * s.T + t.tok0 + row0;
-    lds_t *lds = (lds_t *)&sm;
+    const int64_t srow = (int64_t)t.h * s.T + t.tok0 + row0;
+    lds_t *lds = (lds_t *)sm;
     uint32_t voff[G::kDmaPerWave];
     dma_offsets<D>(voff, wave, lane, rsb);
+    // A chunk: Q and dO tiles by every wave, the 64 lse2 and delta values
+    // (4 bytes per lane) by waves 0 and 1.
     auto issue = [&](int ci, int buf) {
         const int off = ci * kKC, rows = min(kKC, qend - row0 - off);
         lds_t *b = lds + buf * (int)sizeof(BwdChunk<D>);
         dma_tile<D>(row_desc<D>(qb + off * rs, rows, rs), b, voff, wave);
         dma_tile<D>(row_desc<D>(db + off * rs, rows, rs), b + G::kBytes, voff, wave);
-        dma_tile<D>(row_desc<D>(ob + off * rs, rows, rs), b + 2 * G::kBytes, voff, wave);
-        if (wave == 0) {
-            // 64 lse values, 4 bytes per lane
-            const uint64_t a = (uint64_t)(lsb + off);
+        if (wave < 2) {
+            const float *src = (wave == 0 ? ws_lse2 : ws_dlt) + srow + off;
+            const uint64_t a = (uint64_t)src;
             const i32x4 desc{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), rows * 4, 0x00020000};
-            const uint32_t dst = (uint32_t)(uintptr_t)(b + 3 * G::kBytes);
+            const uint32_t dst = (uint32_t)(uintptr_t)(b + 2 * G::kBytes + wave * kKC * 4);
             asm volatile(
                 "s_mov_b32 m0, %0\n\t"
                 "s_nop 0\n\t"
@@ -285,34 +268,12 @@ __device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave
                 : "memory", "m0");
         }
     };
-    // delta and lse * log2(e) of chunk buffer `buf` (its loads complete and
-    // visible): 4 threads per row, each over D/4 columns.
-    auto prep = [&](int buf) {
-        const lds_t *b = lds + buf * (int)sizeof(BwdChunk<D>);
-        const int r = tid >> 2, part = tid & 3;
-        const int p = sigma(r);
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-            const int off = G::at(p, part * (D / 32) + i);
-            d = dot8(lds_read16(b + G::kBytes + off), lds_read16(b + 2 * G::kBytes + off), d);
-        }
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        if (part == 0) {
-            sm.dlt[buf][r] = d;
-            sm.lse2[buf][r] = sm.c[buf].lse[r] * kLog2e;
-        }
-    };
 
     if (nch > 0) issue(0, 0);
     bf16x8 kop[D / 16], vop[D / 16];
     load_operand<D>(kop, k + base + (int64_t)my_key * rs, my_valid, g);
     load_operand<D>(vop, v + base + (int64_t)my_key * rs, my_valid, g);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): chunk 0 and the K, V rows are in
-    if (nch > 1) issue(1, 1);
-    asm volatile("s_barrier" ::: "memory");
-    if (nch > 0) prep(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only tile loads in flight from here
     const ReadOffsets<D> ro(lane);
 
     f32x16 adk[D / 32], adv[D / 32];
@@ -322,9 +283,9 @@ __device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave
     auto step = [&](int ci, auto buf_c) {
         constexpr int buf = decltype(buf_c)::value;
         wait_vm_barrier<0>();
-        if (ci + 2 < nch) issue(ci + 2, (buf + 2) % NB);
-        if (ci + 1 < nch) prep((buf + 1) % NB);
+        if (ci + 1 < nch) issue(ci + 1, buf ^ 1);
         if (!wave_live) return;
+        const BwdChunk<D> &cb = sm[buf];
         const lds_t *qt = lds + buf * (int)sizeof(BwdChunk<D>);
         const lds_t *dt_ = qt + G::kBytes;
         const int c0 = row0 + ci * kKC;
@@ -349,28 +310,37 @@ __device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int qrow = sub * 32 + hh * 16 + g * 8;
-                const float4 l0 = *(const float4 *)&sm.lse2[buf][qrow];
-                const float4 l1 = *(const float4 *)&sm.lse2[buf][qrow + 4];
-                const float4 d0 = *(const float4 *)&sm.dlt[buf][qrow];
-                const float4 d1 = *(const float4 *)&sm.dlt[buf][qrow + 4];
+                const float4 l0 = *(const float4 *)&cb.lse2[qrow];
+                const float4 l1 = *(const float4 *)&cb.lse2[qrow + 4];
+                const float4 d0 = *(const float4 *)&cb.dlt[qrow];
+                const float4 d1 = *(const float4 *)&cb.dlt[qrow + 4];
                 const float ls[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 const float ds[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = hh * 8 + i;
-                    float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[i]));
-                    if (masked && (uint32_t)(x + 16 * hh + i) >= span) p = 0.f;
-                    pf[r] = p;
-                    pmax = fmaxf(pmax, p);
-                    pb[hh][i] = (bf16)p;
-                    dsb[hh][i] = (bf16)(p * (dp[r] - ds[i]));
+                    pf[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[i]));
+                    dp[r] -= ds[i];
                 }
             }
-            // Rows that see few keys have weights near 1, where bf16
-            // rounding of P (2^-9 relative) would dominate dV.  There P is
-            // split into bf16 hi + lo and dV takes a second product;
-            // elsewhere P < 1/16 bounds the rounding error per term by 2^-13.
-            const bool split = __builtin_amdgcn_ballot_w64(pmax > 0.0625f) != 0;
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= span) pf[r] = 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                pmax = fmaxf(pmax, pf[r]);
+                pb[r >> 3][r & 7] = (bf16)pf[r];
+                dsb[r >> 3][r & 7] = (bf16)(pf[r] * dp[r]);
+            }
+            // Where a weight exceeds 1/4 (queries that see few keys), bf16
+            // rounding of P (up to 2^-8 relative) is split off into a bf16 lo
+            // part and dV takes a second product; elsewhere each term's
+            // rounding error stays below 2^-10 |dO|, well under the bf16
+            // rounding of dV itself.  About 2% of sub-tiles split on N(0,1)
+            // inputs.
+            const bool split = __builtin_amdgcn_ballot_w64(pmax > 0.25f) != 0;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const lds_t *qr = qt + (sub * 32 + kk * 16) * G::kRowBytes;
@@ -394,7 +364,6 @@ __device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave
     for (int ci = 0; ci < nch; ci += NB) {
         step(ci, std::integral_constant<int, 0>{});
         if (ci + 1 < nch) step(ci + 1, std::integral_constant<int, 1>{});
-        if (ci + 2 < nch) step(ci + 2, std::integral_constant<int, 2>{});
     }
     if (my_valid) {
         store_out<D>(dk + base + (int64_t)my_key * rs, adk, s.scale, g);
@@ -402,30 +371,58 @@ __device__ void key_role(const Shape &s, const Tile &t, BwdSmem<D> &sm, int wave
     }
 }
 
+// Row statistics of the backward pass: delta = <dO, O> (fp32 from bf16
+// products) and lse * log2(e), for every (head, token), into [H, T] arrays.
+// One thread per row; consecutive lanes take consecutive tokens of one head.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowstats(Shape s, const bf16 *__restrict__ out,
+                                                    const bf16 *__restrict__ dout,
+                                                    const float *__restrict__ lse,
+                                                    float *__restrict__ ws_lse2,
+                                                    float *__restrict__ ws_dlt) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int h = blockIdx.y;
+    if (t >= s.T) return;
+    const int64_t row = (t * s.H + h) * D;
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i)
+        d = dot8(*(const bf16x8 *)(dout + row + i * 8), *(const bf16x8 *)(out + row + i * 8), d);
+    const int64_t o = (int64_t)h * s.T + t;
+    ws_dlt[o] = d;
+    ws_lse2[o] = lse[o] * kLog2e;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ out, const bf16 *__restrict__ dout, const float *__restrict__ lse,
-    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+    const bf16 *__restrict__ dout, const float *__restrict__ ws_lse2,
+    const float *__restrict__ ws_dlt, bf16 *__restrict__ dq, bf16 *__restrict__ dk,
+    bf16 *__restrict__ dv) {
     __shared__ int sh[8];
-    __shared__ __align__(1024) BwdSmem<D> sm;
+    __shared__ __align__(1024) BwdChunk<D> sm[NB];
     Tile t;
     if (!decode_tile<kThreads>(s, kTileRows, 2, t, sh)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t.sub == 0)
-        query_role<D>(s, t, sm, wave, q, k, v, out, dout, lse, dq);
+        query_role<D>(s, t, sm, wave, q, k, v, dout, ws_lse2, ws_dlt, dq);
     else
-        key_role<D>(s, t, sm, wave, q, k, v, out, dout, lse, dk, dv);
+        key_role<D>(s, t, sm, wave, q, k, v, dout, ws_lse2, ws_dlt, dk, dv);
 }
 
 template <int D>
 hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v, const void *out,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                    hipStream_t st) {
+                    float *ws, hipStream_t st) {
+    float *ws_lse2 = ws, *ws_dlt = ws + s.H * s.T;
+    hipLaunchKernelGGL((bwd_rowstats<D>), dim3((unsigned)((s.T + 255) / 256), (unsigned)s.H),
+                       dim3(256), 0, st, s, (const bf16 *)out, (const bf16 *)dout, lse, ws_lse2,
+                       ws_dlt);
     const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 2, s.H);
     hipLaunchKernelGGL((bwd_mfma<D>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                       (const bf16 *)dout, lse, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv);
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)dout,
+                       (const float *)ws_lse2, (const float *)ws_dlt, (bf16 *)dq, (bf16 *)dk,
+                       (bf16 *)dv);
     return hipGetLastError();
 }
 
@@ -433,11 +430,11 @@ hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v,
 
 hipError_t launch_mfma_bwd(const Shape &s, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *dq,
-                           void *dk, void *dv, hipStream_t st) {
+                           void *dk, void *dv, float *ws, hipStream_t st) {
     switch (s.D) {
-    case 32: return launch_t<32>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
-    case 64: return launch_t<64>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
-    case 128: return launch_t<128>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
+    case 32: return launch_t<32>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    case 64: return launch_t<64>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    case 128: return launch_t<128>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
     }
     return hipErrorInvalidValue;
 }

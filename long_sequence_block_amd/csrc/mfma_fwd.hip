@@ -44,11 +44,13 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kTileRows = 128;
 constexpr int kKC = 64;        // keys per staged chunk
 
-// LDS tiles in rotation, and waves per SIMD the register budget is sized for.
+// LDS tiles in rotation (two: a small footprint lets more workgroups share a
+// CU, which hides more latency than a deeper prefetch), and waves per SIMD the
+// register budget is sized for.
 template <int D>
-constexpr int kBufs = D == 128 ? 2 : 3;
+constexpr int kBufs = 2;
 template <int D>
-constexpr int kWavesPerSimd = D == 128 ? 2 : 3;
+constexpr int kWavesPerSimd = D == 128 ? 2 : 4;
 
 template <int D>
 struct FwdChunk {

@@ -39,6 +39,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const bf16 *base, int
 // from inline assembly): base address, 16-bit high part and stride 0, byte
 // count, and the dword-format word of gfx9 raw buffers.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ i32x4 row_desc(const bf16 *base, int rows, int64_t rs) {
     const uint32_t bytes = rows > 0 ? (uint32_t)((int64_t)(rows - 1) * rs * 2 + D * 2) : 0u;
@@ -49,6 +50,17 @@ __device__ __forceinline__ i32x4 row_desc(const bf16 *base, int rows, int64_t rs
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ void buf_store16(uint4 x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(float x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+// Raw buffer resource over `bytes` bytes at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
