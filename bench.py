@@ -175,7 +175,8 @@ def main():
     out = torch.empty_like(d["q"])
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
     grads = tuple(torch.empty_like(d["q"]) for _ in range(3)) if w.backward else None
-    ws_n = lsb.blockattn_bwd_workspace_size(T, H, lsb.BF16 if w.dtype == "bf16" else lsb.FP32)
+    ws_n = lsb.blockattn_bwd_workspace_size(T, d["offsets"].numel() - 1, H,
+                                           lsb.BF16 if w.dtype == "bf16" else lsb.FP32)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
 
     def step(ev=None):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 1
+#define BLOCKATTN_ABI_VERSION 2
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -87,21 +87,25 @@ blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
                                hipStream_t stream);
 
 /*
- * Bytes of device workspace blockattn_bwd needs for these sizes: for bf16,
- * two fp32 row statistics per (head, token) (delta = <dO, O> and lse in base
- * 2), i.e. 8 * H * T bytes rounded up to 256; 0 for fp32.  Returns SIZE_MAX
- * for invalid sizes.
+ * Bytes of device workspace blockattn_bwd needs for these sizes.  For bf16:
+ * two fp32 row statistics per (head, token) (lse in base 2 and -delta, with
+ * delta = <dO, O>), 64 bytes of counters, batch + 1 int32 tile prefix sums
+ * and a 16-byte tile-table entry per (user, head, 128-row unit, role), i.e.
+ * at most 2 * (ceil(T / 128) + batch) * H entries; each region is rounded up
+ * to 256 bytes.  0 for fp32 and for empty calls (T or batch 0).  Returns
+ * SIZE_MAX for invalid sizes.
  */
-size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t num_heads,
-                                    blockattn_dtype dtype);
+size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t batch,
+                                    int32_t num_heads, blockattn_dtype dtype);
 
 /*
  * Backward pass.  Given the forward inputs, its out and lse, and the upstream
  * gradient dout, writes dq, dk, dv [T,H,D] (dtype; fp32 accumulation).
  * workspace: device memory of at least blockattn_bwd_workspace_size() bytes,
- * 256-byte aligned, owned by the caller, contents on entry ignored; it may be
- * reused once the stream has passed this call, and may be null when the size
- * is 0.  Other arguments as for blockattn_fwd.
+ * 256-byte aligned, owned by the caller, contents on entry ignored; the call
+ * uses it as scratch on `stream` (two calls that share a workspace must not
+ * overlap), it may be reused once the stream has passed this call, and may
+ * be null when the size is 0.  Other arguments as for blockattn_fwd.
  */
 blockattn_status blockattn_bwd(const void *q, const void *k, const void *v,
                                const void *out, const void *dout,

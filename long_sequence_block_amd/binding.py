@@ -51,7 +51,7 @@ def load() -> ctypes.CDLL:
                                   i32, f32, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t,
                                   vp]
     lib.blockattn_bwd.restype = ctypes.c_int
-    lib.blockattn_bwd_workspace_size.argtypes = [i64, i32, ctypes.c_int]
+    lib.blockattn_bwd_workspace_size.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.blockattn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
@@ -79,8 +79,8 @@ def blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_hea
                                 dtype, dq, dk, dv, workspace, workspace_bytes, stream)
 
 
-def blockattn_bwd_workspace_size(total_tokens, num_heads, dtype) -> int:
-    return int(load().blockattn_bwd_workspace_size(total_tokens, num_heads, dtype))
+def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
+    return int(load().blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype))
 
 
 def blockattn_status_string(status: int) -> str:
@@ -151,7 +151,7 @@ def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
     dq, dk, dv = grads
-    need = blockattn_bwd_workspace_size(T, H, code)
+    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

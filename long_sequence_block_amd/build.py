@@ -19,8 +19,13 @@ BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -amdgpu-atomic-optimizer-strategy=None: the backward's tile-queue atomic is
+# issued by one lane and its result is needed only a tile later; the
+# optimizer's rewrite consumes the result at once, which would stall the wave
+# for the atomic's full round trip on every tile.
 HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
                "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC]
 
 

@@ -29,6 +29,9 @@ blockattn_status check_common(const int32_t *offsets, int32_t batch, int64_t T,
     // every launch's grid is bounded by H * (T/B + batch) * ceil(B/32)
     const int64_t tiles = ((T + B - 1) / B + batch) * (int64_t)((B + 31) / 32) * H;
     if (tiles > (int64_t)INT32_MAX - 1024) return BLOCKATTN_ERR_UNSUPPORTED;
+    // and the backward's tile table by (ceil(T/128) + batch) * 2 * H
+    if (ba::bwd_max_tiles(T, batch, H) > (int64_t)INT32_MAX - 1024)
+        return BLOCKATTN_ERR_UNSUPPORTED;
     if (T == 0 || batch == 0) {
         *empty = true;
         return BLOCKATTN_OK;
@@ -68,16 +71,14 @@ const char *blockattn_status_string(blockattn_status status) {
     return "unknown status";
 }
 
-size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t num_heads,
+size_t blockattn_bwd_workspace_size(int64_t total_tokens, int32_t batch, int32_t num_heads,
                                     blockattn_dtype dtype) {
-    if (total_tokens < 0 || num_heads < 1 ||
+    if (total_tokens < 0 || batch < 0 || num_heads < 1 ||
         (dtype != BLOCKATTN_BF16 && dtype != BLOCKATTN_FP32))
         return SIZE_MAX;
     if (dtype == BLOCKATTN_FP32) return 0;  // the fp32 kernels need no workspace
-    // bf16: two fp32 [H, T] row statistics (lse * log2 e and delta), 256-byte
-    // granularity.
-    const size_t bytes = (size_t)2 * (size_t)num_heads * (size_t)total_tokens * sizeof(float);
-    return (bytes + 255) / 256 * 256;
+    if (total_tokens == 0 || batch == 0) return 0;  // nothing to launch
+    return ba::bwd_workspace_bytes(total_tokens, batch, num_heads);
 }
 
 blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
@@ -117,13 +118,13 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
         !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
         !aligned16(dv))
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
-    const size_t need = blockattn_bwd_workspace_size(total_tokens, num_heads, dtype);
+    const size_t need = blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
         return BLOCKATTN_ERR_WORKSPACE;
     const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
                                    block_size, window_blocks, scale);
     hipError_t e = dtype == BLOCKATTN_BF16
-                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, (float *)workspace,
+                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, workspace,
                                              stream)
                        : ba::launch_scalar_bwd(s, false, q, k, v, out, dout, lse, dq, dk, dv,
                                                stream);

@@ -51,12 +51,12 @@ __device__ __forceinline__ int clamp_off(int32_t o, int T) { return o < 0 ? 0 : 
 // Inclusive prefix sum over the NT threads of a workgroup (NT a multiple of
 // 64): wave-level shuffles, then one LDS pass over the wave totals.  Also
 // returns the workgroup total.  `sh` holds NT/64 ints.
-template <int NT>
-__device__ __forceinline__ int wg_inclusive_scan(int v, int *sh, int &total) {
+template <int NT, typename I = int>
+__device__ __forceinline__ I wg_inclusive_scan(I v, I *sh, I &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o, 64);
+        const I y = __shfl_up(v, o, 64);
         if (lane >= o) v += y;
     }
     if (NT == 64) {
@@ -65,10 +65,10 @@ __device__ __forceinline__ int wg_inclusive_scan(int v, int *sh, int &total) {
     }
     if (lane == 63) sh[wave] = v;
     __syncthreads();
-    int add = 0, tot = 0;
+    I add = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
-        const int x = sh[w];
+        const I x = sh[w];
         add += w < wave ? x : 0;
         tot += x;
     }

@@ -18,11 +18,45 @@ hipError_t launch_scalar_bwd(const Shape &s, bool bf16_io, const void *q, const 
 hipError_t launch_mfma_fwd(const Shape &s, const void *q, const void *k, const void *v,
                            void *out, float *lse, hipStream_t st);
 
-// bf16 MFMA backward: a row-statistics launch (delta, lse * log2 e into the
-// workspace `ws`, 2 * H * T floats) and one launch of query-role and
-// key-role workgroups.
+// bf16 MFMA backward.  Workspace (caller-owned device memory, 256-byte
+// aligned): per-(head, token) row statistics lse * log2(e) and -delta, a
+// 64-byte block of counters (tile queue, tile count), per-user tile prefix
+// sums, and the tile table.  Each region starts on a 256-byte boundary.
+constexpr int kBwdTileRows = 128;
+
+inline int64_t bwd_max_tiles(int64_t T, int batch, int H) {
+    // sum over users of ceil(L_u / 128) <= ceil(T / 128) + batch, x 2 roles
+    return ((T + kBwdTileRows - 1) / kBwdTileRows + batch) * 2 * (int64_t)H;
+}
+
+struct BwdWorkspace {
+    float *lse2, *ndlt;
+    int *ctr, *ubase;
+    int4 *table;
+};
+
+inline size_t ws_align(size_t x) { return (x + 255) / 256 * 256; }
+
+inline size_t bwd_workspace_bytes(int64_t T, int batch, int H) {
+    return 2 * ws_align((size_t)H * (size_t)T * sizeof(float)) + 256 +
+           ws_align(((size_t)batch + 1) * sizeof(int)) +
+           ws_align((size_t)bwd_max_tiles(T, batch, H) * 16);
+}
+
+inline BwdWorkspace bwd_workspace_layout(void *ws, int64_t T, int batch, int H) {
+    char *p = (char *)ws;
+    BwdWorkspace w;
+    const size_t stat = ws_align((size_t)H * (size_t)T * sizeof(float));
+    w.lse2 = (float *)p;
+    w.ndlt = (float *)(p + stat);
+    w.ctr = (int *)(p + 2 * stat);
+    w.ubase = (int *)(p + 2 * stat + 256);
+    w.table = (int4 *)(p + 2 * stat + 256 + ws_align(((size_t)batch + 1) * sizeof(int)));
+    return w;
+}
+
 hipError_t launch_mfma_bwd(const Shape &s, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *dq,
-                           void *dk, void *dv, float *ws, hipStream_t st);
+                           void *dk, void *dv, void *ws, hipStream_t st);
 
 }  // namespace ba

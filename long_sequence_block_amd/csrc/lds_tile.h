@@ -72,10 +72,15 @@ template <int D>
 __device__ __forceinline__ void dma_tile(i32x4 desc, lds_t *tile,
                                          const uint32_t (&voff)[TileGeom<D>::kDmaPerWave],
                                          int wave) {
-    const uint32_t base = (uint32_t)(uintptr_t)tile;
+    // The LDS address and the descriptor are wave-uniform; readfirstlane
+    // states it, so they are given to the instruction in scalar registers.
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)tile);
+    desc = i32x4{__builtin_amdgcn_readfirstlane(desc[0]), __builtin_amdgcn_readfirstlane(desc[1]),
+                 __builtin_amdgcn_readfirstlane(desc[2]), __builtin_amdgcn_readfirstlane(desc[3])};
 #pragma unroll
     for (int j = 0; j < TileGeom<D>::kDmaPerWave; ++j) {
-        const uint32_t dst = base + (uint32_t)(wave * TileGeom<D>::kDmaPerWave + j) * 1024u;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            base + (uint32_t)(wave * TileGeom<D>::kDmaPerWave + j) * 1024u);
         asm volatile(
             "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"

@@ -1,21 +1,30 @@
-// Backward block attention on bf16 MFMA (gfx950), one launch.
+// Backward block attention on bf16 MFMA (gfx950).
 //
 // The production block-attention kernel fuses its backward pass ("GEM (Meta)"
-// on aiwiki.ai, section "Custom kernels").  Here every 128-row tile of a
-// (user, head) is worked on by two workgroups of the same launch:
+// on aiwiki.ai, section "Custom kernels").  Every 128-row tile of a
+// (user, head) is worked on twice, in two roles:
 //
 //   query role  (rows = queries i):  dQ_i = scale * sum_j dS_ij k_j
 //   key role    (rows = keys j):     dK_j = scale * sum_i dS_ij q_i,
 //                                    dV_j = sum_i P_ij dO_i
 //
 // with P_ij = exp(scale <q_i,k_j> - lse_i), dP_ij = <dO_i, v_j>,
-// dS_ij = P_ij (dP_ij - delta_i) and delta_i = <dO_i, O_i>.  A first,
-// memory-bound launch writes delta and lse * log2(e) of every row to the
-// workspace; the main launch then never reads O.  Each output element of the
-// main launch has exactly one owner, so there are no atomics and the result
-// is deterministic.  Visibility is the block window: local query i sees
-// local key j iff j <= i and floor(i/B) - floor(j/B) < W, so key j is seen by
-// queries j <= i < (floor(j/B) + W) * B.
+// dS_ij = P_ij (dP_ij - delta_i) and delta_i = <dO_i, O_i>.  Each output
+// element has exactly one owner, so there are no atomics on outputs and the
+// result is deterministic.  Visibility is the block window: local query i
+// sees local key j iff j <= i and floor(i/B) - floor(j/B) < W, so key j is
+// seen by queries j <= i < (floor(j/B) + W) * B.
+//
+// Three launches:
+//   1. bwd_tile_index (one workgroup): per-user tile counts from the jagged
+//      offsets, their prefix sums, the total, and a zeroed queue counter.
+//   2. bwd_prep: delta and lse * log2(e) of every row (memory bound), and the
+//      tile table (one 16-byte entry per (user, head, unit, role)).
+//   3. bwd_mfma: as many workgroups as fit on the GPU at once; each takes
+//      tiles from the queue counter until it runs dry.  While it works on one
+//      tile it already holds the next tile's table entry, has issued the next
+//      tile's first chunk and operand rows, and has requested the index of
+//      the tile after that, so per-tile set-up latency is hidden.
 //
 // Layouts follow the forward kernel: 32x32x16 bf16 MFMAs, one query (query
 // role) or one key (key role) per lane column; streamed rows sit in LDS
@@ -25,6 +34,8 @@
 // dO rows in registers and streams K and V; the key role keeps K and V rows
 // and streams Q, dO and the two row statistics.  Chunks of 64 rows go from
 // HBM straight into two LDS buffers in turn, one barrier per chunk.
+#include <algorithm>
+
 #include "kernels.h"
 #include "lds_tile.h"
 
@@ -32,9 +43,8 @@ namespace ba {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kTileRows = 128;
+constexpr int kTileRows = kBwdTileRows;
 constexpr int kKC = 64;        // rows per streamed chunk
-constexpr int NB = 2;          // LDS chunk buffers in rotation
 
 // Waves per SIMD the register budget is sized for.
 template <int D>
@@ -46,34 +56,8 @@ template <int D>
 struct BwdChunk {
     bf16 t[2][kKC * D];
     float lse2[kKC];  // lse * log2(e)
-    float dlt[kKC];   // delta
+    float ndlt[kKC];  // -delta
 };
-
-template <int D>
-__device__ __forceinline__ void store_out(bf16 *dst, const f32x16 (&acc)[D / 32], float mul,
-                                          int g) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            bf16x8 x;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = (bf16)(acc[dt][half * 8 + i] * mul);
-            *(bf16x8 *)(dst + dt * 32 + half * 16 + g * 8) = x;
-        }
-}
-
-// Loads one row of a [T,H,D] tensor as MFMA B operands (lane column = row).
-template <int D>
-__device__ __forceinline__ void load_operand(bf16x8 (&op)[D / 16], const bf16 *row, bool valid,
-                                             int g) {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (valid) x = *(const uint4 *)(row + ks * 16 + g * 8);
-        op[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-}
 
 __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
@@ -102,327 +86,683 @@ struct ReadOffsets {
     }
 };
 
+// A decoded tile; every field is wave-uniform.
+struct BwdTile {
+    int role;           // 0: query role, 1: key role
+    int h, blk, len, tok0;
+    int row0, row_end;  // the tile's own rows (local indices)
+    int sbeg, send;     // the streamed rows
+    int nch;            // chunks of streamed rows
+};
+
+// Table entry: {tok0, len, unit, 2 * head + role}.
+__device__ __forceinline__ BwdTile make_tile(const Shape &s, int4 e) {
+    BwdTile t;
+    t.tok0 = __builtin_amdgcn_readfirstlane(e.x);
+    t.len = __builtin_amdgcn_readfirstlane(e.y);
+    t.blk = __builtin_amdgcn_readfirstlane(e.z);
+    const int hr = __builtin_amdgcn_readfirstlane(e.w);
+    t.h = hr >> 1;
+    t.role = hr & 1;
+    t.row0 = t.blk * kTileRows;
+    t.row_end = min(t.row0 + kTileRows, t.len);
+    if (t.role == 0) {  // keys of the window of the tile's queries
+        t.sbeg = window_start(t.row0, s.B, s.W);
+        t.send = t.row_end;
+    } else {            // queries that see the tile's keys
+        t.sbeg = t.row0;
+        t.send = window_end(t.row_end - 1, s.B, s.W, t.len);
+    }
+    t.nch = (t.send - t.sbeg + kKC - 1) / kKC;
+    return t;
+}
+
+// The rows a wave owns in a tile: 32 rows, rotated with the unit index so
+// that the SIMDs share the lighter and heavier row groups evenly.
+__device__ __forceinline__ int wave_rows(const BwdTile &t, int wave) {
+    return t.row0 + ((wave + t.blk) & 3) * 32;
+}
+
+// The registers a wave keeps for one tile: the MFMA B operands of its own
+// row (Q and dO for the query role, K and V for the key role) and, for the
+// query role, the row's lse * log2(e) and -delta.
+template <int D>
+struct Ops {
+    bf16x8 a[D / 16], b[D / 16];
+    float lse2, ndlt;
+};
+
+// LDS staging of a tile's own rows (two 64-row TileGeom tiles per tensor)
+// and, for the query role, their row statistics.  The next tile's rows land
+// here while the current tile's last chunk is worked on.
+template <int D>
+struct OpsLds {
+    bf16 a[2][kKC * D];
+    bf16 b[2][kKC * D];
+    float lse2[kTileRows];
+    float ndlt[kTileRows];
+};
+
+// Output store instructions per wave and tile.  The counts are fixed
+// (buffer instructions clip rows past the tile instead of branching around
+// them), so the next tile's first wait can allow for exactly these.
+template <int D>
+constexpr int kStores(int role) { return role == 0 ? D / 16 : D / 8; }
+
+// Writes a wave's 32 rows of one output (scaled by mul) as bf16; rows past
+// the tile are clipped by the buffer range.
+template <int D>
+__device__ __forceinline__ void store_rows(bf16 *dst_tile, int rows, int64_t rs, uint32_t lrow,
+                                           const f32x16 (&acc)[D / 32], float mul, int g) {
+    const auto r = row_rsrc<D>(dst_tile, rows, rs);
+    const uint32_t off = lrow * (uint32_t)(rs * 2) + (uint32_t)g * 16u;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 p = pack_bf16(acc[dt][half * 8 + 2 * j] * mul,
+                                           acc[dt][half * 8 + 2 * j + 1] * mul);
+                x[2 * j] = p[0];
+                x[2 * j + 1] = p[1];
+            }
+            buf_store16(__builtin_bit_cast(uint4, x), r, off + (uint32_t)(dt * 64 + half * 32));
+        }
+}
+
 // ------------------------------------------------------------ query role
 
+// One 64-key chunk of the query role: S^T and dP^T for each 32-key
+// sub-tile, then dQ^T += K^T dS^T.  c0 = first key of the chunk.
 template <int D>
-__device__ void query_role(const Shape &s, const Tile &t, BwdChunk<D> *sm, int wave,
-                           const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                           const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
-                           const float *__restrict__ ws_lse2, const float *__restrict__ ws_dlt,
-                           bf16 *__restrict__ dq) {
+__device__ __forceinline__ void query_chunk(const Shape &s, const BwdTile &t, int wave, int lane,
+                                            const lds_t *kt, int c0, const Ops<D> &op,
+                                            const f32x16 &ndlt, const ReadOffsets<D> &ro,
+                                            f32x16 (&acc)[D / 32]) {
     using G = TileGeom<D>;
-    constexpr int kDma = 2 * G::kDmaPerWave;
-    const int lane = threadIdx.x & 63;
-    const int w = (wave + t.blk) & 3;
     const int qi = lane & 31, g = lane >> 5;
-    const int64_t rs = (int64_t)s.H * D;
-    const uint32_t rsb = (uint32_t)(rs * 2);
-    const int64_t base = t.tok0 * rs + (int64_t)t.h * D;
-    const int row0 = t.blk * kTileRows;
-    const int row_end = min(row0 + kTileRows, t.len);
-    const int wr0 = row0 + w * 32;
-    const int my_row = wr0 + qi;
-    const bool wave_live = wr0 < row_end;
-    const bool my_valid = my_row < row_end;
-    const int w_last = min(wr0 + 31, row_end - 1);
+    const int wr0 = wave_rows(t, wave);
+    const int w_last = min(wr0 + 31, t.row_end - 1);
     const int wave_klo = window_start(wr0, s.B, s.W);
     const int wave_klo_max = window_start(max(wr0, w_last), s.B, s.W);
+    const int my_row = wr0 + qi;
     const int my_klo = window_start(my_row, s.B, s.W);
     const float c = s.scale * kLog2e;
-
-    const int kbeg = window_start(row0, s.B, s.W);
-    const int nch = (row_end - kbeg + kKC - 1) / kKC;
-    const bf16 *kb = k + base + (int64_t)kbeg * rs;
-    const bf16 *vb = v + base + (int64_t)kbeg * rs;
-    lds_t *lds = (lds_t *)sm;
-    uint32_t voff[G::kDmaPerWave];
-    dma_offsets<D>(voff, wave, lane, rsb);
-    auto issue = [&](int ci, int buf) {
-        const int off = ci * kKC, rows = min(kKC, row_end - kbeg - off);
-        lds_t *b = lds + buf * (int)sizeof(BwdChunk<D>);
-        dma_tile<D>(row_desc<D>(kb + off * rs, rows, rs), b, voff, wave);
-        dma_tile<D>(row_desc<D>(vb + off * rs, rows, rs), b + G::kBytes, voff, wave);
-    };
-
-    if (nch > 0) issue(0, 0);
-    bf16x8 qop[D / 16], doop[D / 16];
-    load_operand<D>(qop, q + base + (int64_t)my_row * rs, my_valid, g);
-    load_operand<D>(doop, dout + base + (int64_t)my_row * rs, my_valid, g);
-    float my_lse2 = 0.f, my_dlt = 0.f;
-    if (my_valid) {
-        const int64_t i = (int64_t)t.h * s.T + t.tok0 + my_row;
-        my_lse2 = ws_lse2[i];
-        my_dlt = ws_dlt[i];
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only tile loads in flight from here
-    const ReadOffsets<D> ro(lane);
-
-    f32x16 acc[D / 32];
+    const lds_t *vt = kt + G::kBytes;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-
-    auto step = [&](int ci, auto buf_c) {
-        constexpr int buf = decltype(buf_c)::value;
-        wait_vm_barrier<0>();
-        if (ci + 1 < nch) issue(ci + 1, buf ^ 1);
-        if (!wave_live) return;
-        const lds_t *kt = lds + buf * (int)sizeof(BwdChunk<D>);
-        const lds_t *vt = kt + G::kBytes;
-        const int c0 = kbeg + ci * kKC;
+    for (int sub = 0; sub < 2; ++sub) {
+        const int a = c0 + sub * 32;
+        if (!(a <= w_last && a + 31 >= wave_klo)) continue;
+        // Every LDS read of the sub-tile is issued before its first use, so
+        // their latencies overlap each other and the products.
+        const lds_t *ks_ = kt + sub * 32 * G::kRowBytes;
+        const lds_t *vs_ = vt + sub * 32 * G::kRowBytes;
+        bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int a = c0 + sub * 32;
-            if (!(a <= w_last && a + 31 >= wave_klo)) continue;
-            f32x16 sc = {}, dp = {};
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                sc = mfma32(lds_read16(kt + sub * 32 * G::kRowBytes + ro.rd[ks]), qop[ks], sc);
-                dp = mfma32(lds_read16(vt + sub * 32 * G::kRowBytes + ro.rd[ks]), doop[ks], dp);
-            }
-            const bool masked = a + 31 > wr0 || a < wave_klo_max;
-            // key of register r: a + 8g + 16(r/8) + r%8; visible iff
-            // my_klo <= key <= my_row
-            const int x = a + 8 * g - my_klo;
-            const uint32_t span = (uint32_t)(my_row - my_klo);
-            float pr[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -my_lse2));
-            if (masked) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > span) pr[r] = 0.f;
-            }
-            bf16x8 dsb[2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dsb[r >> 3][r & 7] = (bf16)(pr[r] * (dp[r] - my_dlt));
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const lds_t *kr = kt + (sub * 32 + kk * 16) * G::kRowBytes;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] = mfma32(lds_read_tr(kr + ro.trd[0][dt], kr + ro.trd[1][dt]),
-                                     dsb[kk], acc[dt]);
-            }
+        for (int ks = 0; ks < D / 16; ++ks) {
+            ka[ks] = lds_read16(ks_ + ro.rd[ks]);
+            va[ks] = lds_read16(vs_ + ro.rd[ks]);
         }
-    };
-    for (int ci = 0; ci < nch; ci += NB) {
-        step(ci, std::integral_constant<int, 0>{});
-        if (ci + 1 < nch) step(ci + 1, std::integral_constant<int, 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        // dP^T starts from -delta of the lane's query: the products leave
+        // dP - delta.
+        f32x16 sc = mfma32(ka[0], op.a[0], f32x16{}), dp = mfma32(va[0], op.b[0], ndlt);
+#pragma unroll
+        for (int ks = 1; ks < D / 16; ++ks) {
+            sc = mfma32(ka[ks], op.a[ks], sc);
+            dp = mfma32(va[ks], op.b[ks], dp);
+        }
+        bf16x8 ktr[2][D / 32];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const lds_t *kr = ks_ + kk * 16 * G::kRowBytes;
+                ktr[kk][dt] = lds_read_tr(kr + ro.trd[0][dt], kr + ro.trd[1][dt]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        const bool masked = a + 31 > wr0 || a < wave_klo_max;
+        // key of register r: a + 8g + 16(r/8) + r%8; visible iff
+        // my_klo <= key <= my_row
+        const int x = a + 8 * g - my_klo;
+        const uint32_t span = (uint32_t)(my_row - my_klo);
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -op.lse2));
+        if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > span) pr[r] = 0.f;
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = kk * 8 + 2 * j;
+                const bf16x2 v2 = pack_bf16(pr[r] * dp[r], pr[r + 1] * dp[r + 1]);
+                dsb[kk][2 * j] = v2[0];
+                dsb[kk][2 * j + 1] = v2[1];
+            }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma32(ktr[kk][dt], dsb[kk], acc[dt]);
     }
-    if (my_valid) store_out<D>(dq + base + (int64_t)my_row * rs, acc, s.scale, g);
 }
 
 // -------------------------------------------------------------- key role
 
+// One 64-query chunk of the key role: S and dP for each 32-query sub-tile,
+// then dV^T += dO^T P and dK^T += Q^T dS.  c0 = first query of the chunk;
+// cb holds the chunk's row statistics.
 template <int D>
-__device__ void key_role(const Shape &s, const Tile &t, BwdChunk<D> *sm, int wave,
-                         const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                         const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
-                         const float *__restrict__ ws_lse2, const float *__restrict__ ws_dlt,
-                         bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+__device__ __forceinline__ void key_chunk(const Shape &s, const BwdTile &t, int wave, int lane,
+                                          const lds_t *qt, const BwdChunk<D> &cb, int c0,
+                                          const Ops<D> &op, const ReadOffsets<D> &ro,
+                                          f32x16 (&adk)[D / 32], f32x16 (&adv)[D / 32]) {
     using G = TileGeom<D>;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = (wave + t.blk) & 3;
     const int qi = lane & 31, g = lane >> 5;
-    const int64_t rs = (int64_t)s.H * D;
-    const uint32_t rsb = (uint32_t)(rs * 2);
-    const int64_t base = t.tok0 * rs + (int64_t)t.h * D;
-    const int row0 = t.blk * kTileRows;
-    const int row_end = min(row0 + kTileRows, t.len);  // keys of this tile end here
-    const int wk0 = row0 + w * 32;
-    const int my_key = wk0 + qi;
-    const bool wave_live = wk0 < row_end;
-    const bool my_valid = my_key < row_end;
-    const int wk_last = min(wk0 + 31, row_end - 1);
-    const int qend = window_end(row_end - 1, s.B, s.W, t.len);  // queries of the tile end here
+    const int wk0 = wave_rows(t, wave);
+    const int wk_last = min(wk0 + 31, t.row_end - 1);
     const int wave_qend_min = window_end(wk0, s.B, s.W, t.len);
     const int wave_qend_max = window_end(max(wk0, wk_last), s.B, s.W, t.len);
+    const int my_key = wk0 + qi;
     const int my_qend = window_end(my_key, s.B, s.W, t.len);
     const float c = s.scale * kLog2e;
-
-    const int nch = (qend - row0 + kKC - 1) / kKC;
-    const bf16 *qb = q + base + (int64_t)row0 * rs;
-    const bf16 *db = dout + base + (int64_t)row0 * rs;
-    const int64_t srow = (int64_t)t.h * s.T + t.tok0 + row0;
-    lds_t *lds = (lds_t *)sm;
-    uint32_t voff[G::kDmaPerWave];
-    dma_offsets<D>(voff, wave, lane, rsb);
-    // A chunk: Q and dO tiles by every wave, the 64 lse2 and delta values
-    // (4 bytes per lane) by waves 0 and 1.
-    auto issue = [&](int ci, int buf) {
-        const int off = ci * kKC, rows = min(kKC, qend - row0 - off);
-        lds_t *b = lds + buf * (int)sizeof(BwdChunk<D>);
-        dma_tile<D>(row_desc<D>(qb + off * rs, rows, rs), b, voff, wave);
-        dma_tile<D>(row_desc<D>(db + off * rs, rows, rs), b + G::kBytes, voff, wave);
-        if (wave < 2) {
-            const float *src = (wave == 0 ? ws_lse2 : ws_dlt) + srow + off;
-            const uint64_t a = (uint64_t)src;
-            const i32x4 desc{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), rows * 4, 0x00020000};
-            const uint32_t dst = (uint32_t)(uintptr_t)(b + 2 * G::kBytes + wave * kKC * 4);
-            asm volatile(
-                "s_mov_b32 m0, %0\n\t"
-                "s_nop 0\n\t"
-                "buffer_load_dword %1, %2, 0 offen lds"
-                :
-                : "s"(dst), "v"((uint32_t)lane * 4u), "s"(desc)
-                : "memory", "m0");
+    const lds_t *dt_ = qt + G::kBytes;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        const int a = c0 + sub * 32;  // first query of the sub-tile
+        if (!(a + 31 >= wk0 && a < wave_qend_max)) continue;
+        const lds_t *qs_ = qt + sub * 32 * G::kRowBytes;
+        const lds_t *ds_ = dt_ + sub * 32 * G::kRowBytes;
+        bf16x8 qa[D / 16], da[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            qa[ks] = lds_read16(qs_ + ro.rd[ks]);
+            da[ks] = lds_read16(ds_ + ro.rd[ks]);
         }
-    };
-
-    if (nch > 0) issue(0, 0);
-    bf16x8 kop[D / 16], vop[D / 16];
-    load_operand<D>(kop, k + base + (int64_t)my_key * rs, my_valid, g);
-    load_operand<D>(vop, v + base + (int64_t)my_key * rs, my_valid, g);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only tile loads in flight from here
-    const ReadOffsets<D> ro(lane);
-
-    f32x16 adk[D / 32], adv[D / 32];
+        // lse2 and -delta of the sub-tile's queries, in register order:
+        // register r holds query a + 8g + 16(r/8) + r%8.
+        f32x16 ls, nd;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) adk[dt] = adv[dt] = f32x16{};
-
-    auto step = [&](int ci, auto buf_c) {
-        constexpr int buf = decltype(buf_c)::value;
-        wait_vm_barrier<0>();
-        if (ci + 1 < nch) issue(ci + 1, buf ^ 1);
-        if (!wave_live) return;
-        const BwdChunk<D> &cb = sm[buf];
-        const lds_t *qt = lds + buf * (int)sizeof(BwdChunk<D>);
-        const lds_t *dt_ = qt + G::kBytes;
-        const int c0 = row0 + ci * kKC;
+        for (int hh = 0; hh < 2; ++hh) {
+            const int qrow = sub * 32 + hh * 16 + g * 8;
+            const float4 l0 = *(const float4 *)&cb.lse2[qrow];
+            const float4 l1 = *(const float4 *)&cb.lse2[qrow + 4];
+            const float4 d0 = *(const float4 *)&cb.ndlt[qrow];
+            const float4 d1 = *(const float4 *)&cb.ndlt[qrow + 4];
+            ls[hh * 8 + 0] = l0.x; ls[hh * 8 + 1] = l0.y; ls[hh * 8 + 2] = l0.z;
+            ls[hh * 8 + 3] = l0.w; ls[hh * 8 + 4] = l1.x; ls[hh * 8 + 5] = l1.y;
+            ls[hh * 8 + 6] = l1.z; ls[hh * 8 + 7] = l1.w;
+            nd[hh * 8 + 0] = d0.x; nd[hh * 8 + 1] = d0.y; nd[hh * 8 + 2] = d0.z;
+            nd[hh * 8 + 3] = d0.w; nd[hh * 8 + 4] = d1.x; nd[hh * 8 + 5] = d1.y;
+            nd[hh * 8 + 6] = d1.z; nd[hh * 8 + 7] = d1.w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dP starts from -delta of each query: the products leave dP - delta.
+        f32x16 sc = mfma32(qa[0], op.a[0], f32x16{}), dp = mfma32(da[0], op.b[0], nd);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int a = c0 + sub * 32;  // first query of the sub-tile
-            if (!(a + 31 >= wk0 && a < wave_qend_max)) continue;
-            f32x16 sc = {}, dp = {};
+        for (int ks = 1; ks < D / 16; ++ks) {
+            sc = mfma32(qa[ks], op.a[ks], sc);
+            dp = mfma32(da[ks], op.b[ks], dp);
+        }
+        bf16x8 qtr[2][D / 32], dtr[2][D / 32];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                sc = mfma32(lds_read16(qt + sub * 32 * G::kRowBytes + ro.rd[ks]), kop[ks], sc);
-                dp = mfma32(lds_read16(dt_ + sub * 32 * G::kRowBytes + ro.rd[ks]), vop[ks], dp);
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const lds_t *qr = qs_ + kk * 16 * G::kRowBytes;
+                const lds_t *dr = ds_ + kk * 16 * G::kRowBytes;
+                dtr[kk][dt] = lds_read_tr(dr + ro.trd[0][dt], dr + ro.trd[1][dt]);
+                qtr[kk][dt] = lds_read_tr(qr + ro.trd[0][dt], qr + ro.trd[1][dt]);
             }
-            const bool masked = a < wk_last || a + 31 >= wave_qend_min;
-            // query of register r: a + 8g + 16(r/8) + r%8; it sees this
-            // lane's key iff my_key <= query < my_qend
-            const int x = a + 8 * g - my_key;
-            const uint32_t span = (uint32_t)max(my_qend - my_key, 0);
-            float pf[16];
-            bf16x8 pb[2], dsb[2];
-            float pmax = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+        const bool masked = a < wk_last || a + 31 >= wave_qend_min;
+        // query of register r sees this lane's key iff
+        // my_key <= query < my_qend
+        const int x = a + 8 * g - my_key;
+        const uint32_t span = (uint32_t)max(my_qend - my_key, 0);
+        float pf[16];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int qrow = sub * 32 + hh * 16 + g * 8;
-                const float4 l0 = *(const float4 *)&cb.lse2[qrow];
-                const float4 l1 = *(const float4 *)&cb.lse2[qrow + 4];
-                const float4 d0 = *(const float4 *)&cb.dlt[qrow];
-                const float4 d1 = *(const float4 *)&cb.dlt[qrow + 4];
-                const float ls[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-                const float ds[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        for (int r = 0; r < 16; ++r) pf[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[r]));
+        if (masked) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = hh * 8 + i;
-                    pf[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[i]));
-                    dp[r] -= ds[i];
-                }
+            for (int r = 0; r < 16; ++r)
+                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= span) pf[r] = 0.f;
+        }
+        // Largest weight, compared as bits (weights are >= 0).
+        uint32_t pmax = 0u;
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = kk * 8 + 2 * j;
+                pmax = max(pmax, max(__float_as_uint(pf[r]), __float_as_uint(pf[r + 1])));
+                const bf16x2 p2 = pack_bf16(pf[r], pf[r + 1]);
+                const bf16x2 s2 = pack_bf16(pf[r] * dp[r], pf[r + 1] * dp[r + 1]);
+                pb[kk][2 * j] = p2[0];
+                pb[kk][2 * j + 1] = p2[1];
+                dsb[kk][2 * j] = s2[0];
+                dsb[kk][2 * j + 1] = s2[1];
             }
-            if (masked) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= span) pf[r] = 0.f;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                pmax = fmaxf(pmax, pf[r]);
-                pb[r >> 3][r & 7] = (bf16)pf[r];
-                dsb[r >> 3][r & 7] = (bf16)(pf[r] * dp[r]);
-            }
-            // Where a weight exceeds 1/4 (queries that see few keys), bf16
-            // rounding of P (up to 2^-8 relative) is split off into a bf16 lo
-            // part and dV takes a second product; elsewhere each term's
-            // rounding error stays below 2^-10 |dO|, well under the bf16
-            // rounding of dV itself.  About 2% of sub-tiles split on N(0,1)
-            // inputs.
-            const bool split = __builtin_amdgcn_ballot_w64(pmax > 0.25f) != 0;
+        // Where a weight exceeds 1/4 (queries that see few keys), bf16
+        // rounding of P (up to 2^-8 relative) is split off into a bf16 lo
+        // part and dV takes a second product; elsewhere each term's rounding
+        // error stays below 2^-10 |dO|, well under the bf16 rounding of dV
+        // itself.  About 2% of sub-tiles split on N(0,1) inputs.
+        if (__builtin_amdgcn_ballot_w64(pmax > __float_as_uint(0.25f)) != 0) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const lds_t *qr = qt + (sub * 32 + kk * 16) * G::kRowBytes;
-                const lds_t *dr = dt_ + (sub * 32 + kk * 16) * G::kRowBytes;
                 bf16x8 lo;
-                if (split) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) lo[i] = (bf16)(pf[kk * 8 + i] - (float)pb[kk][i]);
+                for (int j = 0; j < 4; ++j) {
+                    const int r = kk * 8 + 2 * j;
+                    const bf16x2 l2 = pack_bf16(pf[r] - (float)pb[kk][2 * j],
+                                                pf[r + 1] - (float)pb[kk][2 * j + 1]);
+                    lo[2 * j] = l2[0];
+                    lo[2 * j + 1] = l2[1];
                 }
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const bf16x8 da = lds_read_tr(dr + ro.trd[0][dt], dr + ro.trd[1][dt]);
-                    adv[dt] = mfma32(da, pb[kk], adv[dt]);
-                    if (split) adv[dt] = mfma32(da, lo, adv[dt]);
-                    adk[dt] = mfma32(lds_read_tr(qr + ro.trd[0][dt], qr + ro.trd[1][dt]),
-                                     dsb[kk], adk[dt]);
-                }
+                for (int dt = 0; dt < D / 32; ++dt) adv[dt] = mfma32(dtr[kk][dt], lo, adv[dt]);
             }
         }
-    };
-    for (int ci = 0; ci < nch; ci += NB) {
-        step(ci, std::integral_constant<int, 0>{});
-        if (ci + 1 < nch) step(ci + 1, std::integral_constant<int, 1>{});
-    }
-    if (my_valid) {
-        store_out<D>(dk + base + (int64_t)my_key * rs, adk, s.scale, g);
-        store_out<D>(dv + base + (int64_t)my_key * rs, adv, 1.f, g);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                adv[dt] = mfma32(dtr[kk][dt], pb[kk], adv[dt]);
+                adk[dt] = mfma32(qtr[kk][dt], dsb[kk], adk[dt]);
+            }
     }
 }
 
-// Row statistics of the backward pass: delta = <dO, O> (fp32 from bf16
-// products) and lse * log2(e), for every (head, token), into [H, T] arrays.
-// One thread per row; consecutive lanes take consecutive tokens of one head.
+// ------------------------------------------------------------ pre-passes
+
+// Tile counts per user (ceil(L / 128) units x 2 roles x H heads), their
+// exclusive prefix sums into ubase[0..batch], the total into ctr[1], and
+// the queue counter ctr[0] = 0.  One workgroup.  Sums are capped at `cap`
+// (the table's capacity, which well-formed offsets never reach), so
+// malformed offsets cannot make the table writes overrun.
+__global__ __launch_bounds__(1024) void bwd_tile_index(Shape s, int cap, int *__restrict__ ctr,
+                                                       int *__restrict__ ubase) {
+    __shared__ long long sh[16];
+    const int T = (int)s.T;
+    long long run = 0;
+    for (int c0 = 0; c0 < s.batch; c0 += 1024) {
+        const int u = c0 + (int)threadIdx.x;
+        long long n = 0;
+        if (u < s.batch) {
+            const int a = clamp_off(s.offsets[u], T), b = clamp_off(s.offsets[u + 1], T);
+            const int L = b > a ? b - a : 0;
+            n = (long long)((L + kTileRows - 1) / kTileRows) * 2 * s.H;
+        }
+        long long total;
+        const long long incl = wg_inclusive_scan<1024, long long>(n, sh, total);
+        if (u < s.batch) ubase[u] = (int)min(run + incl - n, (long long)cap);
+        run += total;
+    }
+    if (threadIdx.x == 0) {
+        const int n = (int)min(run, (long long)cap);
+        ubase[s.batch] = n;
+        ctr[0] = 0;
+        ctr[1] = n;
+    }
+}
+
+// Workgroups [0, nrs) write the row statistics, one thread per (head,
+// token): delta = <dO, O> (fp32 from bf16 products), stored negated, and
+// lse * log2(e).  Workgroup nrs + u writes the table entries of user u in
+// the order head, unit, role.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_rowstats(Shape s, const bf16 *__restrict__ out,
-                                                    const bf16 *__restrict__ dout,
-                                                    const float *__restrict__ lse,
-                                                    float *__restrict__ ws_lse2,
-                                                    float *__restrict__ ws_dlt) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int h = blockIdx.y;
-    if (t >= s.T) return;
-    const int64_t row = (t * s.H + h) * D;
-    float d = 0.f;
+__global__ __launch_bounds__(256) void bwd_prep(Shape s, int nrs, const bf16 *__restrict__ out,
+                                                const bf16 *__restrict__ dout,
+                                                const float *__restrict__ lse,
+                                                float *__restrict__ ws_lse2,
+                                                float *__restrict__ ws_ndlt,
+                                                const int *__restrict__ ubase,
+                                                int4 *__restrict__ table) {
+    const int b = (int)blockIdx.x;
+    if (b < nrs) {
+        const int nx = (int)((s.T + 255) / 256);
+        const int h = b / nx;
+        const int64_t t = (int64_t)(b - h * nx) * 256 + threadIdx.x;
+        if (t >= s.T) return;
+        const int64_t row = (t * s.H + h) * D;
+        float d = 0.f;
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i)
-        d = dot8(*(const bf16x8 *)(dout + row + i * 8), *(const bf16x8 *)(out + row + i * 8), d);
-    const int64_t o = (int64_t)h * s.T + t;
-    ws_dlt[o] = d;
-    ws_lse2[o] = lse[o] * kLog2e;
+        for (int i = 0; i < D / 8; ++i)
+            d = dot8(*(const bf16x8 *)(dout + row + i * 8), *(const bf16x8 *)(out + row + i * 8),
+                     d);
+        const int64_t o = (int64_t)h * s.T + t;
+        ws_ndlt[o] = -d;
+        ws_lse2[o] = lse[o] * kLog2e;
+        return;
+    }
+    const int u = b - nrs;
+    const int j0 = ubase[u], j1 = ubase[u + 1];
+    if (j1 <= j0) return;
+    const int T = (int)s.T;
+    const int a = clamp_off(s.offsets[u], T), e = clamp_off(s.offsets[u + 1], T);
+    const int L = e - a;
+    const int per_head = (L + kTileRows - 1) / kTileRows * 2;
+    for (int j = j0 + (int)threadIdx.x; j < j1; j += 256) {
+        const int loc = j - j0, h = loc / per_head, rem = loc - h * per_head;
+        table[j] = make_int4(a, L, rem >> 1, (h << 1) | (rem & 1));
+    }
+}
+
+// ------------------------------------------------------------ main kernel
+
+// Kernel arguments and per-wave constants of the main kernel.
+template <int D>
+struct BwdArgs {
+    Shape s;
+    const bf16 *q, *k, *v, *dout;
+    const float *ws_lse2, *ws_ndlt;
+    int *ctr;
+    const int4 *table;
+    bf16 *dq, *dk, *dv;
+    int ntiles;
+    int wave, lane;
+    lds_t *lds;       // chunk buffers
+    BwdChunk<D> *sm;
+    OpsLds<D> *ol;    // the tile's own rows
+    int *ring;        // tile indices, requested three tiles ahead
+    int *entry;       // the next tile's table entry (dwords 0..3)
+    uint32_t voff[TileGeom<D>::kDmaPerWave];
+};
+
+// Where a workgroup is in its stream of tiles.
+struct BwdSched {
+    int kt;         // tiles done
+    int buf;        // LDS buffer of the next chunk
+    int prev_role;  // role of the previous tile (-1: none)
+    int pend;       // wave 0, lane 0: the tile index requested three tiles ahead
+};
+
+// LDS byte address of a pointer into LDS (generic pointers to LDS carry the
+// offset in their low 32 bits).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ uint32_t lds_addr(const lds_t *p) { return (uint32_t)(uintptr_t)p; }
+
+// One dword per lane from `src` (`bytes` valid, the rest zero) into LDS at
+// byte address `dst`: 64 lanes x 4 bytes.
+__device__ __forceinline__ void dma_dwords(const void *src, uint32_t bytes, uint32_t dst,
+                                           int lane) {
+    const uint64_t a = (uint64_t)src;
+    const i32x4 desc{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                     __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
+                     __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+    const uint32_t d = __builtin_amdgcn_readfirstlane(dst);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(d), "v"((uint32_t)lane * 4u), "s"(desc)
+        : "memory", "m0");
+}
+
+// Issues this wave's share of chunk ci of tile t into buffer `buf`.
+template <int D>
+__device__ __forceinline__ void issue_chunk(const BwdArgs<D> &A, const BwdTile &t, int ci,
+                                            int buf) {
+    using G = TileGeom<D>;
+    const int64_t rs = (int64_t)A.s.H * D;
+    const int off = t.sbeg + ci * kKC, rows = min(kKC, t.send - off);
+    const int64_t base = ((int64_t)t.tok0 + off) * rs + (int64_t)t.h * D;
+    lds_t *b = A.lds + buf * (int)sizeof(BwdChunk<D>);
+    // (uniform branches rather than pointer selects, which the compiler
+    // would turn into an indexed copy of the arguments in scratch memory)
+    if (t.role == 0) {
+        dma_tile<D>(row_desc<D>(A.k + base, rows, rs), b, A.voff, A.wave);
+        dma_tile<D>(row_desc<D>(A.v + base, rows, rs), b + G::kBytes, A.voff, A.wave);
+    } else {
+        dma_tile<D>(row_desc<D>(A.q + base, rows, rs), b, A.voff, A.wave);
+        dma_tile<D>(row_desc<D>(A.dout + base, rows, rs), b + G::kBytes, A.voff, A.wave);
+        // the chunk's 64 lse2 and -delta values
+        const int64_t so = (int64_t)t.h * A.s.T + t.tok0 + off;
+        if (A.wave == 0)
+            dma_dwords(A.ws_lse2 + so, (uint32_t)rows * 4u, lds_addr(b + 2 * G::kBytes), A.lane);
+        else if (A.wave == 1)
+            dma_dwords(A.ws_ndlt + so, (uint32_t)rows * 4u, lds_addr(b + 2 * G::kBytes + kKC * 4),
+                       A.lane);
+    }
+}
+
+// Issues this wave's share of tile t's own rows (and, for the query role,
+// their row statistics) into the operand staging area.
+template <int D>
+__device__ __forceinline__ void issue_ops(const BwdArgs<D> &A, const BwdTile &t) {
+    const int64_t rs = (int64_t)A.s.H * D;
+    const int64_t base = ((int64_t)t.tok0 + t.row0) * rs + (int64_t)t.h * D;
+    const int rows = t.row_end - t.row0;
+    auto rows_of = [&](const bf16 *src, bf16 (&dst)[2][kKC * D]) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int r = max(0, min(kKC, rows - half * kKC));
+            dma_tile<D>(row_desc<D>(src + base + (int64_t)half * kKC * rs, r, rs),
+                        (lds_t *)dst[half], A.voff, A.wave);
+        }
+    };
+    if (t.role == 0) {
+        rows_of(A.q, A.ol->a);
+        rows_of(A.dout, A.ol->b);
+        // wave w: statistic w & 1 of rows 64 (w >> 1) ..
+        const int half = A.wave >> 1;
+        const int r = max(0, min(kKC, rows - half * kKC));
+        const int64_t so = (int64_t)t.h * A.s.T + t.tok0 + t.row0 + half * kKC;
+        if (A.wave & 1)
+            dma_dwords(A.ws_ndlt + so, (uint32_t)r * 4u, lds_addr(A.ol->ndlt + half * kKC), A.lane);
+        else
+            dma_dwords(A.ws_lse2 + so, (uint32_t)r * 4u, lds_addr(A.ol->lse2 + half * kKC), A.lane);
+    } else {
+        rows_of(A.k, A.ol->a);
+        rows_of(A.v, A.ol->b);
+    }
+}
+
+// Reads this wave's operand registers from the staging area: lane
+// (qi, g) takes row wave_rows + qi, 16-byte granules 2ks + g.
+template <int D>
+__device__ __forceinline__ void read_ops(const BwdArgs<D> &A, const BwdTile &t, Ops<D> &op) {
+    using G = TileGeom<D>;
+    const int qi = A.lane & 31, g = A.lane >> 5;
+    const int lr = wave_rows(t, A.wave) - t.row0 + qi;  // 0 .. 127
+    const int half = lr >> 6, p = sigma(lr & 63);      // physical row of logical row lr
+    const lds_t *ta = (const lds_t *)A.ol->a[half];
+    const lds_t *tb = (const lds_t *)A.ol->b[half];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const int o = G::at(p, 2 * ks + g);
+        op.a[ks] = lds_read16(ta + o);
+        op.b[ks] = lds_read16(tb + o);
+    }
+    if (t.role == 0) {
+        op.lse2 = A.ol->lse2[lr];
+        op.ndlt = A.ol->ndlt[lr];
+    } else {
+        op.lse2 = op.ndlt = 0.f;
+    }
+}
+
+// Works through tile t (of role ROLE, whose own rows and first chunk are in
+// flight or landed) and sets up the next one: returns false when the queue
+// has run dry, else the next tile in tn with its rows and first chunk issued.
+template <int D, int ROLE>
+__device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<D> &ro,
+                                         BwdSched &sc, const BwdTile &t, BwdTile &tn) {
+    constexpr int NA = ROLE == 0 ? 1 : 2;  // accumulator sets
+    const int tid = threadIdx.x, g = A.lane >> 5;
+    // The tile's rows and first chunk have landed; only the previous tile's
+    // output stores may still be in flight.
+    if (sc.prev_role < 0)
+        wait_vm_barrier<0>();
+    else if (sc.prev_role == 0)
+        wait_vm_barrier<kStores<D>(0)>();
+    else
+        wait_vm_barrier<kStores<D>(1)>();
+    Ops<D> op;
+    read_ops<D>(A, t, op);
+    if (sc.kt > 0 && tid == 0) A.ring[(sc.kt + 2) & 3] = sc.pend;
+    const int jn = __builtin_amdgcn_readfirstlane(A.ring[(sc.kt + 1) & 3]);
+    // The next tile's 16-byte entry goes straight into LDS (lanes 0..3 one
+    // dword each, the rest past the range); the chunk waits cover it.
+    if (jn < A.ntiles && A.wave == 0) dma_dwords(A.table + jn, 16u, lds_addr(A.entry), A.lane);
+    // A one-chunk tile needs the entry in this same step, and must not
+    // overwrite the staging area before every wave has read its rows.
+    if (t.nch == 1) wait_vm_barrier<0>();
+    if (tid == 0) sc.pend = atomicAdd(A.ctr, 1);
+
+    f32x16 acc[NA][D / 32];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[i][dt] = f32x16{};
+    f32x16 ndlt;
+    if (ROLE == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ndlt[r] = op.ndlt;
+    }
+    bool has_next = false;
+    for (int ci = 0; ci < t.nch; ++ci) {
+        if (ci > 0) wait_vm_barrier<0>();  // chunk ci has landed
+        if (ci + 1 < t.nch) {
+            issue_chunk<D>(A, t, ci + 1, sc.buf ^ 1);
+        } else if (jn < A.ntiles) {
+            const int *e = A.entry;
+            tn = make_tile(A.s, make_int4(e[0], e[1], e[2], e[3]));
+            issue_chunk<D>(A, tn, 0, sc.buf ^ 1);
+            issue_ops<D>(A, tn);
+            has_next = true;
+        }
+        const lds_t *b = A.lds + sc.buf * (int)sizeof(BwdChunk<D>);
+        const int c0 = t.sbeg + ci * kKC;
+        if (wave_rows(t, A.wave) < t.row_end) {
+            if (ROLE == 0)
+                query_chunk<D>(A.s, t, A.wave, A.lane, b, c0, op, ndlt, ro, acc[0]);
+            else
+                key_chunk<D>(A.s, t, A.wave, A.lane, b, A.sm[sc.buf], c0, op, ro, acc[0],
+                             acc[NA - 1]);
+        }
+        sc.buf ^= 1;
+    }
+    // Outputs: a fixed number of stores per wave (rows past the tile are
+    // clipped), which the next tile's first wait allows for.
+    const int64_t rs = (int64_t)A.s.H * D;
+    const int64_t obase = ((int64_t)t.tok0 + t.row0) * rs + (int64_t)t.h * D;
+    const int rows = t.row_end - t.row0;
+    const uint32_t lrow = (uint32_t)(wave_rows(t, A.wave) - t.row0 + (A.lane & 31));
+    if (ROLE == 0) {
+        store_rows<D>(A.dq + obase, rows, rs, lrow, acc[0], A.s.scale, g);
+    } else {
+        store_rows<D>(A.dk + obase, rows, rs, lrow, acc[0], A.s.scale, g);
+        store_rows<D>(A.dv + obase, rows, rs, lrow, acc[NA - 1], 1.f, g);
+    }
+    sc.prev_role = ROLE;
+    ++sc.kt;
+    return has_next;
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ws_lse2,
-    const float *__restrict__ ws_dlt, bf16 *__restrict__ dq, bf16 *__restrict__ dk,
-    bf16 *__restrict__ dv) {
-    __shared__ int sh[8];
-    __shared__ __align__(1024) BwdChunk<D> sm[NB];
-    Tile t;
-    if (!decode_tile<kThreads>(s, kTileRows, 2, t, sh)) return;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (t.sub == 0)
-        query_role<D>(s, t, sm, wave, q, k, v, dout, ws_lse2, ws_dlt, dq);
-    else
-        key_role<D>(s, t, sm, wave, q, k, v, dout, ws_lse2, ws_dlt, dk, dv);
+    const float *__restrict__ ws_ndlt, int *__restrict__ ctr, const int4 *__restrict__ table,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+    __shared__ __align__(1024) BwdChunk<D> sm[2];
+    __shared__ __align__(1024) OpsLds<D> ol;
+    __shared__ int ring[4];
+    __shared__ int entry[64];  // 64 lanes x 4 bytes; dwords 0..3 hold the entry
+    const int tid = threadIdx.x;
+    BwdArgs<D> A;
+    A.s = s;
+    A.q = q;
+    A.k = k;
+    A.v = v;
+    A.dout = dout;
+    A.ws_lse2 = ws_lse2;
+    A.ws_ndlt = ws_ndlt;
+    A.ctr = ctr;
+    A.table = table;
+    A.dq = dq;
+    A.dk = dk;
+    A.dv = dv;
+    A.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    A.lane = tid & 63;
+    A.lds = (lds_t *)sm;
+    A.sm = sm;
+    A.ol = &ol;
+    A.ring = ring;
+    A.entry = entry;
+    dma_offsets<D>(A.voff, A.wave, A.lane, (uint32_t)((int64_t)s.H * D * 2));
+    const ReadOffsets<D> ro(A.lane);
+
+    if (tid == 0) {
+        ring[0] = atomicAdd(ctr, 1);
+        ring[1] = atomicAdd(ctr, 1);
+        ring[2] = atomicAdd(ctr, 1);
+    }
+    __syncthreads();
+    A.ntiles = __builtin_amdgcn_readfirstlane(ctr[1]);
+    const int j0 = __builtin_amdgcn_readfirstlane(ring[0]);
+    if (j0 >= A.ntiles) return;
+    BwdTile t = make_tile(s, table[j0]);
+    issue_chunk<D>(A, t, 0, 0);
+    issue_ops<D>(A, t);
+
+    BwdSched sc{0, 0, -1, 0};
+    for (;;) {
+        BwdTile tn;
+        const bool more = t.role == 0 ? run_tile<D, 0>(A, ro, sc, t, tn)
+                                      : run_tile<D, 1>(A, ro, sc, t, tn);
+        if (!more) break;
+        t = tn;
+    }
+}
+
+// Workgroups of bwd_mfma<D> that fit on the current device at once.
+template <int D>
+int resident_workgroups() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_mfma<D>, kThreads, 0) !=
+            hipSuccess ||
+        per < 1)
+        per = 1;
+    const int n = cus * per;
+    if (dev >= 0 && dev < 64) cached[dev] = n;
+    return n;
 }
 
 template <int D>
 hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v, const void *out,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                    float *ws, hipStream_t st) {
-    float *ws_lse2 = ws, *ws_dlt = ws + s.H * s.T;
-    hipLaunchKernelGGL((bwd_rowstats<D>), dim3((unsigned)((s.T + 255) / 256), (unsigned)s.H),
-                       dim3(256), 0, st, s, (const bf16 *)out, (const bf16 *)dout, lse, ws_lse2,
-                       ws_dlt);
-    const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 2, s.H);
+                    void *ws, hipStream_t st) {
+    const BwdWorkspace w = bwd_workspace_layout(ws, s.T, s.batch, s.H);
+    const int64_t max_tiles = bwd_max_tiles(s.T, s.batch, s.H);
+    hipLaunchKernelGGL(bwd_tile_index, dim3(1), dim3(1024), 0, st, s, (int)max_tiles, w.ctr,
+                       w.ubase);
+    const int nrs = (int)((s.T + 255) / 256) * s.H;
+    hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)(nrs + s.batch)), dim3(256), 0, st, s, nrs,
+                       (const bf16 *)out, (const bf16 *)dout, lse, w.lse2, w.ndlt,
+                       (const int *)w.ubase, w.table);
+    const int64_t grid = std::min<int64_t>(max_tiles, (int64_t)resident_workgroups<D>());
     hipLaunchKernelGGL((bwd_mfma<D>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
                        (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)dout,
-                       (const float *)ws_lse2, (const float *)ws_dlt, (bf16 *)dq, (bf16 *)dk,
-                       (bf16 *)dv);
+                       (const float *)w.lse2, (const float *)w.ndlt, w.ctr,
+                       (const int4 *)w.table, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv);
     return hipGetLastError();
 }
 
@@ -430,7 +770,7 @@ hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v,
 
 hipError_t launch_mfma_bwd(const Shape &s, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *dq,
-                           void *dk, void *dv, float *ws, hipStream_t st) {
+                           void *dk, void *dv, void *ws, hipStream_t st) {
     switch (s.D) {
     case 32: return launch_t<32>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
     case 64: return launch_t<64>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);

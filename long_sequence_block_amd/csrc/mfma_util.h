@@ -90,6 +90,12 @@ __device__ __forceinline__ void transpose4x4(const uint2 (&x)[4], uint2 (&c)[4])
                       __builtin_amdgcn_perm(x[3].y, x[2].y, 0x07060302u));
 }
 
+// Two floats rounded to bf16 (nearest even) in one packed register.
+__device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_convertvector((f32x2){a, b}, bf16x2);
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 1
+    assert lsb.blockattn_abi_version() == 2
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -96,8 +96,15 @@ def test_bwd_argument_checks(kw, code):
 
 
 def test_workspace_size():
-    assert lsb.blockattn_bwd_workspace_size(0, 8, lsb.BF16) == 0
-    n = lsb.blockattn_bwd_workspace_size(213551, 8, lsb.BF16)
-    assert n % 256 == 0
-    assert lsb.blockattn_bwd_workspace_size(-1, 8, lsb.BF16) == ctypes.c_size_t(-1).value
-    assert lsb.blockattn_bwd_workspace_size(10, 0, lsb.BF16) == ctypes.c_size_t(-1).value
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lsb.blockattn_bwd_workspace_size(0, 4, 8, lsb.BF16) == 0
+    assert lsb.blockattn_bwd_workspace_size(100, 0, 8, lsb.BF16) == 0
+    assert lsb.blockattn_bwd_workspace_size(213551, 256, 8, lsb.FP32) == 0
+    T, batch, H = 213551, 256, 8
+    n = lsb.blockattn_bwd_workspace_size(T, batch, H, lsb.BF16)
+    tiles = 2 * (-(-T // 128) + batch) * H
+    assert n == 2 * r256(4 * H * T) + 256 + r256(4 * (batch + 1)) + r256(16 * tiles)
+    bad = ctypes.c_size_t(-1).value
+    assert lsb.blockattn_bwd_workspace_size(-1, 1, 8, lsb.BF16) == bad
+    assert lsb.blockattn_bwd_workspace_size(10, -1, 8, lsb.BF16) == bad
+    assert lsb.blockattn_bwd_workspace_size(10, 1, 0, lsb.BF16) == bad
