@@ -89,7 +89,7 @@ blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
 /*
  * Bytes of device workspace blockattn_bwd needs for these sizes.  For bf16:
  * two fp32 row statistics per (head, token) (lse in base 2 and -delta, with
- * delta = <dO, O>), 64 bytes of counters, batch + 1 int32 tile prefix sums
+ * delta = <dO, O>), 256 bytes of counters, batch + 1 int32 tile prefix sums
  * and a 16-byte tile-table entry per (user, head, 128-row unit, role), i.e.
  * at most 2 * (ceil(T / 128) + batch) * H entries; each region is rounded up
  * to 256 bytes.  0 for fp32 and for empty calls (T or batch 0).  Returns

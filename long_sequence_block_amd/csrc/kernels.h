@@ -20,7 +20,7 @@ hipError_t launch_mfma_fwd(const Shape &s, const void *q, const void *k, const v
 
 // bf16 MFMA backward.  Workspace (caller-owned device memory, 256-byte
 // aligned): per-(head, token) row statistics lse * log2(e) and -delta, a
-// 64-byte block of counters (tile queue, tile count), per-user tile prefix
+// 256-byte block of counters (tile queues, tile count), per-user tile prefix
 // sums, and the tile table.  Each region starts on a 256-byte boundary.
 constexpr int kBwdTileRows = 128;
 

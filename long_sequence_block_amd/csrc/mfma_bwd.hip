@@ -46,6 +46,14 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kTileRows = kBwdTileRows;
 constexpr int kKC = 64;        // rows per streamed chunk
 
+// Tile queues.  Workgroups are dealt to the 8 XCDs round-robin, so group
+// blockIdx % 8 runs on one XCD.  Each group takes the tiles of its own runs
+// of kRunTiles consecutive tiles (8 units of one (user, head): neighbours
+// that read the same rows) from its own counter, so those rows are shared
+// in that XCD's L2.  Any placement of workgroups gives the same result.
+constexpr int kQueues = 8;
+constexpr int kRunTiles = 16;
+
 // Waves per SIMD the register budget is sized for.
 template <int D>
 constexpr int kWavesPerSimd = D == 128 ? 1 : 2;
@@ -174,27 +182,42 @@ __device__ __forceinline__ void store_rows(bf16 *dst_tile, int rows, int64_t rs,
 
 // ------------------------------------------------------------ query role
 
+// Per-tile window bounds of a wave's 32 rows (wave-uniform) and of each
+// lane's row, computed once per tile.  Query role: keys [klo, last] are
+// visited, sub-tiles with a key below klo_max or above first row wr0 are
+// masked, and key j is visible to the lane iff (x0 + j) <= span (unsigned).
+struct QWin {
+    int klo, last, klo_max, wr0;
+    int x0;
+    uint32_t span;
+};
+__device__ __forceinline__ QWin query_win(const Shape &s, const BwdTile &t, int wave, int lane) {
+    QWin w;
+    w.wr0 = wave_rows(t, wave);
+    w.last = min(w.wr0 + 31, t.row_end - 1);
+    w.klo = window_start(w.wr0, s.B, s.W);
+    w.klo_max = window_start(max(w.wr0, w.last), s.B, s.W);
+    const int my_row = w.wr0 + (lane & 31);
+    const int my_klo = window_start(my_row, s.B, s.W);
+    w.x0 = 8 * (lane >> 5) - my_klo;
+    w.span = (uint32_t)(my_row - my_klo);
+    return w;
+}
+
 // One 64-key chunk of the query role: S^T and dP^T for each 32-key
 // sub-tile, then dQ^T += K^T dS^T.  c0 = first key of the chunk.
 template <int D>
-__device__ __forceinline__ void query_chunk(const Shape &s, const BwdTile &t, int wave, int lane,
+__device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int lane,
                                             const lds_t *kt, int c0, const Ops<D> &op,
                                             const f32x16 &ndlt, const ReadOffsets<D> &ro,
                                             f32x16 (&acc)[D / 32]) {
     using G = TileGeom<D>;
-    const int qi = lane & 31, g = lane >> 5;
-    const int wr0 = wave_rows(t, wave);
-    const int w_last = min(wr0 + 31, t.row_end - 1);
-    const int wave_klo = window_start(wr0, s.B, s.W);
-    const int wave_klo_max = window_start(max(wr0, w_last), s.B, s.W);
-    const int my_row = wr0 + qi;
-    const int my_klo = window_start(my_row, s.B, s.W);
     const float c = s.scale * kLog2e;
     const lds_t *vt = kt + G::kBytes;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
         const int a = c0 + sub * 32;
-        if (!(a <= w_last && a + 31 >= wave_klo)) continue;
+        if (!(a <= w.last && a + 31 >= w.klo)) continue;
         // Every LDS read of the sub-tile is issued before its first use, so
         // their latencies overlap each other and the products.
         const lds_t *ks_ = kt + sub * 32 * G::kRowBytes;
@@ -205,15 +228,14 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const BwdTile &t, in
             ka[ks] = lds_read16(ks_ + ro.rd[ks]);
             va[ks] = lds_read16(vs_ + ro.rd[ks]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sc = mfma32(ka[0], op.a[0], f32x16{});
+#pragma unroll
+        for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(ka[ks], op.a[ks], sc);
         // dP^T starts from -delta of the lane's query: the products leave
         // dP - delta.
-        f32x16 sc = mfma32(ka[0], op.a[0], f32x16{}), dp = mfma32(va[0], op.b[0], ndlt);
+        f32x16 dp = mfma32(va[0], op.b[0], ndlt);
 #pragma unroll
-        for (int ks = 1; ks < D / 16; ++ks) {
-            sc = mfma32(ka[ks], op.a[ks], sc);
-            dp = mfma32(va[ks], op.b[ks], dp);
-        }
+        for (int ks = 1; ks < D / 16; ++ks) dp = mfma32(va[ks], op.b[ks], dp);
         bf16x8 ktr[2][D / 32];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -222,19 +244,29 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const BwdTile &t, in
                 const lds_t *kr = ks_ + kk * 16 * G::kRowBytes;
                 ktr[kk][dt] = lds_read_tr(kr + ro.trd[0][dt], kr + ro.trd[1][dt]);
             }
-        __builtin_amdgcn_sched_barrier(0);
-        const bool masked = a + 31 > wr0 || a < wave_klo_max;
-        // key of register r: a + 8g + 16(r/8) + r%8; visible iff
-        // my_klo <= key <= my_row
-        const int x = a + 8 * g - my_klo;
-        const uint32_t span = (uint32_t)(my_row - my_klo);
         float pr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -op.lse2));
+        // Issue order: all operand reads, the S products, the transposed
+        // reads, then each dP product followed by a share of the
+        // exponentials (which need only S), so one wave keeps both its
+        // matrix and vector pipes busy.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 32 / (D / 16), 0);
+        }
+        const bool masked = a + 31 > w.wr0 || a < w.klo_max;
+        // key of register r: a + 8g + 16(r/8) + r%8; visible iff
+        // my_klo <= key <= my_row
+        const int x = a + w.x0;
         if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > span) pr[r] = 0.f;
+                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > w.span) pr[r] = 0.f;
         }
         bf16x8 dsb[2];
 #pragma unroll
@@ -255,28 +287,43 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const BwdTile &t, in
 
 // -------------------------------------------------------------- key role
 
+// Key role: queries [wk0, qend_max) are visited, sub-tiles with a query
+// below wk_last or at or past qend_min are masked, and query i sees the
+// lane's key iff (x0 + i) < span (unsigned).
+struct KWin {
+    int wk0, qend_max, wk_last, qend_min;
+    int x0;
+    uint32_t span;
+};
+__device__ __forceinline__ KWin key_win(const Shape &s, const BwdTile &t, int wave, int lane) {
+    KWin w;
+    w.wk0 = wave_rows(t, wave);
+    w.wk_last = min(w.wk0 + 31, t.row_end - 1);
+    w.qend_min = window_end(w.wk0, s.B, s.W, t.len);
+    w.qend_max = window_end(max(w.wk0, w.wk_last), s.B, s.W, t.len);
+    const int my_key = w.wk0 + (lane & 31);
+    const int my_qend = window_end(my_key, s.B, s.W, t.len);
+    w.x0 = 8 * (lane >> 5) - my_key;
+    w.span = (uint32_t)max(my_qend - my_key, 0);
+    return w;
+}
+
 // One 64-query chunk of the key role: S and dP for each 32-query sub-tile,
 // then dV^T += dO^T P and dK^T += Q^T dS.  c0 = first query of the chunk;
 // cb holds the chunk's row statistics.
 template <int D>
-__device__ __forceinline__ void key_chunk(const Shape &s, const BwdTile &t, int wave, int lane,
+__device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lane,
                                           const lds_t *qt, const BwdChunk<D> &cb, int c0,
                                           const Ops<D> &op, const ReadOffsets<D> &ro,
                                           f32x16 (&adk)[D / 32], f32x16 (&adv)[D / 32]) {
     using G = TileGeom<D>;
-    const int qi = lane & 31, g = lane >> 5;
-    const int wk0 = wave_rows(t, wave);
-    const int wk_last = min(wk0 + 31, t.row_end - 1);
-    const int wave_qend_min = window_end(wk0, s.B, s.W, t.len);
-    const int wave_qend_max = window_end(max(wk0, wk_last), s.B, s.W, t.len);
-    const int my_key = wk0 + qi;
-    const int my_qend = window_end(my_key, s.B, s.W, t.len);
+    const int g = lane >> 5;
     const float c = s.scale * kLog2e;
     const lds_t *dt_ = qt + G::kBytes;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
         const int a = c0 + sub * 32;  // first query of the sub-tile
-        if (!(a + 31 >= wk0 && a < wave_qend_max)) continue;
+        if (!(a + 31 >= w.wk0 && a < w.qend_max)) continue;
         const lds_t *qs_ = qt + sub * 32 * G::kRowBytes;
         const lds_t *ds_ = dt_ + sub * 32 * G::kRowBytes;
         bf16x8 qa[D / 16], da[D / 16];
@@ -302,14 +349,13 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const BwdTile &t, int 
             nd[hh * 8 + 3] = d0.w; nd[hh * 8 + 4] = d1.x; nd[hh * 8 + 5] = d1.y;
             nd[hh * 8 + 6] = d1.z; nd[hh * 8 + 7] = d1.w;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // dP starts from -delta of each query: the products leave dP - delta.
-        f32x16 sc = mfma32(qa[0], op.a[0], f32x16{}), dp = mfma32(da[0], op.b[0], nd);
+        f32x16 sc = mfma32(qa[0], op.a[0], f32x16{});
 #pragma unroll
-        for (int ks = 1; ks < D / 16; ++ks) {
-            sc = mfma32(qa[ks], op.a[ks], sc);
-            dp = mfma32(da[ks], op.b[ks], dp);
-        }
+        for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(qa[ks], op.a[ks], sc);
+        // dP starts from -delta of each query: the products leave dP - delta.
+        f32x16 dp = mfma32(da[0], op.b[0], nd);
+#pragma unroll
+        for (int ks = 1; ks < D / 16; ++ks) dp = mfma32(da[ks], op.b[ks], dp);
         bf16x8 qtr[2][D / 32], dtr[2][D / 32];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -320,21 +366,29 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const BwdTile &t, int 
                 dtr[kk][dt] = lds_read_tr(dr + ro.trd[0][dt], dr + ro.trd[1][dt]);
                 qtr[kk][dt] = lds_read_tr(qr + ro.trd[0][dt], qr + ro.trd[1][dt]);
             }
-        __builtin_amdgcn_sched_barrier(0);
-        const bool masked = a < wk_last || a + 31 >= wave_qend_min;
-        // query of register r sees this lane's key iff
-        // my_key <= query < my_qend
-        const int x = a + 8 * g - my_key;
-        const uint32_t span = (uint32_t)max(my_qend - my_key, 0);
         float pf[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pf[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[r]));
+        // Issue order as in the query role.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16) + 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 * (D / 32), 0);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 32 / (D / 16), 0);
+        }
+        const bool masked = a < w.wk_last || a + 31 >= w.qend_min;
+        // query of register r (a + 8g + 16(r/8) + r%8) sees this lane's key
+        // iff my_key <= query < my_qend
+        const int x = a + w.x0;
         if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= span) pf[r] = 0.f;
+                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= w.span) pf[r] = 0.f;
         }
-        // Largest weight, compared as bits (weights are >= 0).
+        // P in bf16 (and its largest value, compared as bits since weights
+        // are >= 0), then the dV products, which need only P; dS needs dP.
         uint32_t pmax = 0u;
         bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -344,12 +398,13 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const BwdTile &t, int 
                 const int r = kk * 8 + 2 * j;
                 pmax = max(pmax, max(__float_as_uint(pf[r]), __float_as_uint(pf[r + 1])));
                 const bf16x2 p2 = pack_bf16(pf[r], pf[r + 1]);
-                const bf16x2 s2 = pack_bf16(pf[r] * dp[r], pf[r + 1] * dp[r + 1]);
                 pb[kk][2 * j] = p2[0];
                 pb[kk][2 * j + 1] = p2[1];
-                dsb[kk][2 * j] = s2[0];
-                dsb[kk][2 * j + 1] = s2[1];
             }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) adv[dt] = mfma32(dtr[kk][dt], pb[kk], adv[dt]);
         // Where a weight exceeds 1/4 (queries that see few keys), bf16
         // rounding of P (up to 2^-8 relative) is split off into a bf16 lo
         // part and dV takes a second product; elsewhere each term's rounding
@@ -374,20 +429,26 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const BwdTile &t, int 
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                adv[dt] = mfma32(dtr[kk][dt], pb[kk], adv[dt]);
-                adk[dt] = mfma32(qtr[kk][dt], dsb[kk], adk[dt]);
+            for (int j = 0; j < 4; ++j) {
+                const int r = kk * 8 + 2 * j;
+                const bf16x2 s2 = pack_bf16(pf[r] * dp[r], pf[r + 1] * dp[r + 1]);
+                dsb[kk][2 * j] = s2[0];
+                dsb[kk][2 * j + 1] = s2[1];
             }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) adk[dt] = mfma32(qtr[kk][dt], dsb[kk], adk[dt]);
     }
 }
 
 // ------------------------------------------------------------ pre-passes
 
 // Tile counts per user (ceil(L / 128) units x 2 roles x H heads), their
-// exclusive prefix sums into ubase[0..batch], the total into ctr[1], and
-// the queue counter ctr[0] = 0.  One workgroup.  Sums are capped at `cap`
-// (the table's capacity, which well-formed offsets never reach), so
-// malformed offsets cannot make the table writes overrun.
+// exclusive prefix sums into ubase[0..batch], the total into ctr[kQueues],
+// and the queue counters ctr[0 .. kQueues) = 0.  One workgroup.  Sums are
+// capped at `cap` (the table's capacity, which well-formed offsets never
+// reach), so malformed offsets cannot make the table writes overrun.
 __global__ __launch_bounds__(1024) void bwd_tile_index(Shape s, int cap, int *__restrict__ ctr,
                                                        int *__restrict__ ubase) {
     __shared__ long long sh[16];
@@ -409,15 +470,17 @@ __global__ __launch_bounds__(1024) void bwd_tile_index(Shape s, int cap, int *__
     if (threadIdx.x == 0) {
         const int n = (int)min(run, (long long)cap);
         ubase[s.batch] = n;
-        ctr[0] = 0;
-        ctr[1] = n;
+        for (int i = 0; i < kQueues; ++i) ctr[i] = 0;
+        ctr[kQueues] = n;
     }
 }
 
-// Workgroups [0, nrs) write the row statistics, one thread per (head,
-// token): delta = <dO, O> (fp32 from bf16 products), stored negated, and
-// lse * log2(e).  Workgroup nrs + u writes the table entries of user u in
-// the order head, unit, role.
+// Workgroups [0, nrs) write the row statistics of 256 consecutive rows of
+// the [T*H, D] tensors (contiguous memory): delta = <dO, O> (fp32 from bf16
+// products), stored negated, and lse * log2(e), into [H, T] arrays.  Each
+// row is read by D/8 consecutive lanes, one 16-byte granule each.
+// Workgroup nrs + u writes the table entries of user u in the order head,
+// unit, role.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(Shape s, int nrs, const bf16 *__restrict__ out,
                                                 const bf16 *__restrict__ dout,
@@ -428,19 +491,37 @@ __global__ __launch_bounds__(256) void bwd_prep(Shape s, int nrs, const bf16 *__
                                                 int4 *__restrict__ table) {
     const int b = (int)blockIdx.x;
     if (b < nrs) {
-        const int nx = (int)((s.T + 255) / 256);
-        const int h = b / nx;
-        const int64_t t = (int64_t)(b - h * nx) * 256 + threadIdx.x;
-        if (t >= s.T) return;
-        const int64_t row = (t * s.H + h) * D;
-        float d = 0.f;
+        constexpr int kLanes = D / 8;        // lanes per row
+        constexpr int kRows = 256 / kLanes;  // rows per pass of the workgroup
+        constexpr int kPass = 256 / kRows;
+        const int64_t nrow = s.T * s.H;
+        const int part = threadIdx.x % kLanes, rr = threadIdx.x / kLanes;
+        // all loads first, so each lane has 2 * kPass 16-byte loads in flight
+        bf16x8 xo[kPass], xd[kPass];
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i)
-            d = dot8(*(const bf16x8 *)(dout + row + i * 8), *(const bf16x8 *)(out + row + i * 8),
-                     d);
-        const int64_t o = (int64_t)h * s.T + t;
-        ws_ndlt[o] = -d;
-        ws_lse2[o] = lse[o] * kLog2e;
+        for (int p = 0; p < kPass; ++p) {
+            const int64_t row = (int64_t)b * 256 + p * kRows + rr;  // = t * H + h
+            const int64_t o = min(row, nrow - 1) * D + part * 8;
+            xd[p] = *(const bf16x8 *)(dout + o);
+            xo[p] = *(const bf16x8 *)(out + o);
+        }
+        // row b * 256 + k is (token t0 + (h0 + k) / H, head (h0 + k) % H)
+        const int64_t r0 = (int64_t)b * 256;
+        const int64_t t0 = r0 / s.H;
+        const int h0 = (int)(r0 - t0 * s.H);
+#pragma unroll
+        for (int p = 0; p < kPass; ++p) {
+            const int k = p * kRows + rr;
+            float d = dot8(xd[p], xo[p], 0.f);
+#pragma unroll
+            for (int m = 1; m < kLanes; m <<= 1) d += __shfl_xor(d, m, kLanes);
+            if (part == 0 && r0 + k < nrow) {
+                const int q = (h0 + k) / s.H;
+                const int64_t o = (int64_t)(h0 + k - q * s.H) * s.T + t0 + q;
+                ws_ndlt[o] = -d;
+                ws_lse2[o] = lse[o] * kLog2e;
+            }
+        }
         return;
     }
     const int u = b - nrs;
@@ -464,10 +545,11 @@ struct BwdArgs {
     Shape s;
     const bf16 *q, *k, *v, *dout;
     const float *ws_lse2, *ws_ndlt;
-    int *ctr;
+    int *ctr;         // this group's queue counter
     const int4 *table;
     bf16 *dq, *dk, *dv;
     int ntiles;
+    int group, ngroups;
     int wave, lane;
     lds_t *lds;       // chunk buffers
     BwdChunk<D> *sm;
@@ -489,6 +571,14 @@ struct BwdSched {
 // offset in their low 32 bits).
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t lds_addr(const lds_t *p) { return (uint32_t)(uintptr_t)p; }
+
+// Tile index of the n-th request of a group: runs group, group + ngroups,
+// ... of kRunTiles tiles, in order.
+// (Saturated at INT32_MAX, which no tile index reaches.)
+__device__ __forceinline__ int queue_tile(int n, int group, int ngroups) {
+    const int64_t j = ((int64_t)(n / kRunTiles) * ngroups + group) * kRunTiles + n % kRunTiles;
+    return (int)min(j, (int64_t)INT32_MAX);
+}
 
 // One dword per lane from `src` (`bytes` valid, the rest zero) into LDS at
 // byte address `dst`: 64 lanes x 4 bytes.
@@ -617,7 +707,7 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
     // A one-chunk tile needs the entry in this same step, and must not
     // overwrite the staging area before every wave has read its rows.
     if (t.nch == 1) wait_vm_barrier<0>();
-    if (tid == 0) sc.pend = atomicAdd(A.ctr, 1);
+    if (tid == 0) sc.pend = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
 
     f32x16 acc[NA][D / 32];
 #pragma unroll
@@ -629,6 +719,13 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
 #pragma unroll
         for (int r = 0; r < 16; ++r) ndlt[r] = op.ndlt;
     }
+    const bool live = wave_rows(t, A.wave) < t.row_end;
+    QWin qw;
+    KWin kw;
+    if (ROLE == 0)
+        qw = query_win(A.s, t, A.wave, A.lane);
+    else
+        kw = key_win(A.s, t, A.wave, A.lane);
     bool has_next = false;
     for (int ci = 0; ci < t.nch; ++ci) {
         if (ci > 0) wait_vm_barrier<0>();  // chunk ci has landed
@@ -643,12 +740,11 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
         }
         const lds_t *b = A.lds + sc.buf * (int)sizeof(BwdChunk<D>);
         const int c0 = t.sbeg + ci * kKC;
-        if (wave_rows(t, A.wave) < t.row_end) {
+        if (live) {
             if (ROLE == 0)
-                query_chunk<D>(A.s, t, A.wave, A.lane, b, c0, op, ndlt, ro, acc[0]);
+                query_chunk<D>(A.s, qw, A.lane, b, c0, op, ndlt, ro, acc[0]);
             else
-                key_chunk<D>(A.s, t, A.wave, A.lane, b, A.sm[sc.buf], c0, op, ro, acc[0],
-                             acc[NA - 1]);
+                key_chunk<D>(A.s, kw, A.lane, b, A.sm[sc.buf], c0, op, ro, acc[0], acc[NA - 1]);
         }
         sc.buf ^= 1;
     }
@@ -688,7 +784,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     A.dout = dout;
     A.ws_lse2 = ws_lse2;
     A.ws_ndlt = ws_ndlt;
-    A.ctr = ctr;
+    A.ngroups = min((int)gridDim.x, kQueues);
+    A.group = (int)blockIdx.x % A.ngroups;
+    A.ctr = ctr + A.group;
     A.table = table;
     A.dq = dq;
     A.dk = dk;
@@ -704,12 +802,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     const ReadOffsets<D> ro(A.lane);
 
     if (tid == 0) {
-        ring[0] = atomicAdd(ctr, 1);
-        ring[1] = atomicAdd(ctr, 1);
-        ring[2] = atomicAdd(ctr, 1);
+        ring[0] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
+        ring[1] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
+        ring[2] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
     }
     __syncthreads();
-    A.ntiles = __builtin_amdgcn_readfirstlane(ctr[1]);
+    A.ntiles = __builtin_amdgcn_readfirstlane(ctr[kQueues]);
     const int j0 = __builtin_amdgcn_readfirstlane(ring[0]);
     if (j0 >= A.ntiles) return;
     BwdTile t = make_tile(s, table[j0]);
@@ -754,7 +852,7 @@ hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v,
     const int64_t max_tiles = bwd_max_tiles(s.T, s.batch, s.H);
     hipLaunchKernelGGL(bwd_tile_index, dim3(1), dim3(1024), 0, st, s, (int)max_tiles, w.ctr,
                        w.ubase);
-    const int nrs = (int)((s.T + 255) / 256) * s.H;
+    const int nrs = (int)((s.T * s.H + 255) / 256);
     hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)(nrs + s.batch)), dim3(256), 0, st, s, nrs,
                        (const bf16 *)out, (const bf16 *)dout, lse, w.lse2, w.ndlt,
                        (const int *)w.ubase, w.table);
