@@ -554,7 +554,7 @@ struct BwdArgs {
     lds_t *lds;       // chunk buffers
     BwdChunk<D> *sm;
     OpsLds<D> *ol;    // the tile's own rows
-    int *ring;        // tile indices, requested three tiles ahead
+    int *ring;        // the next tile's index, by tile parity
     int *entry;       // the next tile's table entry (dwords 0..3)
     uint32_t voff[TileGeom<D>::kDmaPerWave];
 };
@@ -564,7 +564,6 @@ struct BwdSched {
     int kt;         // tiles done
     int buf;        // LDS buffer of the next chunk
     int prev_role;  // role of the previous tile (-1: none)
-    int pend;       // wave 0, lane 0: the tile index requested three tiles ahead
 };
 
 // LDS byte address of a pointer into LDS (generic pointers to LDS carry the
@@ -699,15 +698,20 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
         wait_vm_barrier<kStores<D>(1)>();
     Ops<D> op;
     read_ops<D>(A, t, op);
-    if (sc.kt > 0 && tid == 0) A.ring[(sc.kt + 2) & 3] = sc.pend;
-    const int jn = __builtin_amdgcn_readfirstlane(A.ring[(sc.kt + 1) & 3]);
+    // Index of the next tile (published at the end of the previous one).
+    const int jn = __builtin_amdgcn_readfirstlane(A.ring[(sc.kt + 1) & 1]);
     // The next tile's 16-byte entry goes straight into LDS (lanes 0..3 one
     // dword each, the rest past the range); the chunk waits cover it.
     if (jn < A.ntiles && A.wave == 0) dma_dwords(A.table + jn, 16u, lds_addr(A.entry), A.lane);
     // A one-chunk tile needs the entry in this same step, and must not
     // overwrite the staging area before every wave has read its rows.
     if (t.nch == 1) wait_vm_barrier<0>();
-    if (tid == 0) sc.pend = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
+    // Request the index of the tile after next.  Only its raw count is kept
+    // across the chunk loop; waiting for it happens at the end of the tile,
+    // where what else is in flight (the next tile's first DMAs) is needed by
+    // the next wait anyway.
+    int pend = 0;
+    if (tid == 0) pend = atomicAdd(A.ctr, 1);
 
     f32x16 acc[NA][D / 32];
 #pragma unroll
@@ -748,6 +752,11 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
         }
         sc.buf ^= 1;
     }
+    // (read in every lane by a convergent readfirstlane, which the compiler
+    // cannot move into the lane-0 branch, so the wait for the atomic is on
+    // every path and no register stays pending into the next tile)
+    const int jnn = queue_tile(__builtin_amdgcn_readfirstlane(pend), A.group, A.ngroups);
+    if (tid == 0) A.ring[sc.kt & 1] = jnn;
     // Outputs: a fixed number of stores per wave (rows past the tile are
     // clipped), which the next tile's first wait allows for.
     const int64_t rs = (int64_t)A.s.H * D;
@@ -773,7 +782,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
     __shared__ __align__(1024) BwdChunk<D> sm[2];
     __shared__ __align__(1024) OpsLds<D> ol;
-    __shared__ int ring[4];
+    __shared__ int ring[2];  // the next tile's index, by tile parity
     __shared__ int entry[64];  // 64 lanes x 4 bytes; dwords 0..3 hold the entry
     const int tid = threadIdx.x;
     BwdArgs<D> A;
@@ -804,7 +813,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     if (tid == 0) {
         ring[0] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
         ring[1] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
-        ring[2] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
     }
     __syncthreads();
     A.ntiles = __builtin_amdgcn_readfirstlane(ctr[kQueues]);
@@ -814,7 +822,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     issue_chunk<D>(A, t, 0, 0);
     issue_ops<D>(A, t);
 
-    BwdSched sc{0, 0, -1, 0};
+    BwdSched sc{0, 0, -1};
     for (;;) {
         BwdTile tn;
         const bool more = t.role == 0 ? run_tile<D, 0>(A, ro, sc, t, tn)
