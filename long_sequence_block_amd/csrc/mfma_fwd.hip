@@ -156,14 +156,18 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
         const lds_t *kt = lds + buf * (int)sizeof(FwdChunk<D>);
         const lds_t *vt = kt + G::kBytes;
         const int c0 = kbeg + ci * kKC;
+        // Softmax and P.V of the sub-tile `sub` (first key a) whose scores
+        // are in sc.  The V reads go first so that their latency hides under
+        // the vector work.
+        auto finish = [&](f32x16 sc, int sub, int a) {
+            bf16x8 vtr[2][D / 32];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int a = c0 + sub * 32;
-            if (!(a <= w_last && a + 31 >= wave_klo)) continue;
-            f32x16 sc = {};
+            for (int kk = 0; kk < 2; ++kk) {
+                const lds_t *vr = vt + (sub * 32 + kk * 16) * G::kRowBytes;
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                sc = mfma32(lds_read16(kt + sub * 32 * G::kRowBytes + rd[ks]), qreg[ks], sc);
+                for (int dt = 0; dt < D / 32; ++dt)
+                    vtr[kk][dt] = lds_read_tr(vr + trd[0][dt], vr + trd[1][dt]);
+            }
             if (a + 31 > wr0 || a < wave_klo_max) {
                 // key of register r: a + 8g + 16(r/8) + r%8; visible iff
                 // my_klo <= key <= my_row
@@ -191,21 +195,40 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
                     for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
             }
             const float mc = m == -INFINITY ? 0.f : m * c;
+            // The row sum stays in fp32 (four partial sums): a sum of the
+            // bf16-rounded weights would move lse by up to 2^-9 on rows that
+            // see few keys.
             bf16x8 pb[2];
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc));
-                l += p;
-                pb[r >> 3][r & 7] = (bf16)p;
+            for (int j = 0; j < 8; ++j) {
+                const int r = 2 * j;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c, -mc));
+                ls[j & 3] += p0 + p1;
+                const bf16x2 p2 = pack_bf16(p0, p1);
+                pb[r >> 3][r & 7] = p2[0];
+                pb[r >> 3][(r & 7) + 1] = p2[1];
             }
+            l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const lds_t *vr = vt + (sub * 32 + kk * 16) * G::kRowBytes;
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] = mfma32(lds_read_tr(vr + trd[0][dt], vr + trd[1][dt]), pb[kk],
-                                     acc[dt]);
-            }
+                for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma32(vtr[kk][dt], pb[kk], acc[dt]);
+        };
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int a = c0 + sub * 32;
+            if (!(a <= w_last && a + 31 >= wave_klo)) continue;
+            // All K reads of the sub-tile first, then the S products.
+            bf16x8 ka[D / 16];
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                ka[ks] = lds_read16(kt + sub * 32 * G::kRowBytes + rd[ks]);
+            f32x16 sc = mfma32(ka[0], qreg[0], f32x16{});
+#pragma unroll
+            for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(ka[ks], qreg[ks], sc);
+            finish(sc, sub, a);
         }
     };
     for (int ci = 0; ci < nch; ci += NB) {
