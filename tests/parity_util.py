@@ -48,7 +48,12 @@ def np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def assert_close(name, got, ref, dtype, is_lse=False):
+def assert_close(name, got, ref, dtype, is_lse=False, ulp_slack=False):
+    """The stated bounds.  ulp_slack (bf16 only) adds one bf16 ulp of the
+    reference value (2^-7 relative) to the per-element bound, for stress
+    cases whose gradients carry near-one-hot weights: there the backward's
+    delta comes from the forward's bf16 O, and dS = P (dP - delta) passes that
+    rounding on at full size."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -62,11 +67,13 @@ def assert_close(name, got, ref, dtype, is_lse=False):
     elif is_lse:
         assert err.max() <= LSE_MAX, f"{name}: max abs err {err.max():.3e} > {LSE_MAX}"
     else:
-        assert err.max() <= BF16_MAX, f"{name}: max abs err {err.max():.3e} > {BF16_MAX}"
+        bound = BF16_MAX + (np.abs(ref) * 2.0 ** -7 if ulp_slack else 0.0)
+        worst = (err - bound).max()
+        assert worst <= 0, f"{name}: max abs err {err.max():.3e} exceeds its bound by {worst:.3e}"
         assert err.mean() <= BF16_MEAN, f"{name}: mean abs err {err.mean():.3e} > {BF16_MEAN}"
 
 
-def check_full(case, dtype, B, W, scale, backward=True):
+def check_full(case, dtype, B, W, scale, backward=True, ulp_slack=False):
     """Whole-case parity: every output element against the oracle."""
     dev, host = to_device(case, dtype)
     out, lse = run_fwd(dev, B, W, scale)
@@ -78,7 +85,7 @@ def check_full(case, dtype, B, W, scale, backward=True):
         r = oracle.bwd(host["q"], host["k"], host["v"], host["dout"], host["offsets"], B, W,
                        scale)
         for name, g, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), r):
-            assert_close(name, np64(g), ref, dtype)
+            assert_close(name, np64(g), ref, dtype, ulp_slack=ulp_slack)
     torch.cuda.synchronize()
 
 

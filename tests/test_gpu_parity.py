@@ -48,6 +48,18 @@ def test_small_cases_every_element(idx):
     check_full(case, dtype, B, W, 1.0 / math.sqrt(D), backward=True)
 
 
+def test_many_users_every_element():
+    """1500 users of 0-40 tokens: the backward's tile-index scan runs over
+    several 1024-user passes, and most tiles are one-chunk tiles.  Windows
+    this short give near-one-hot weights, so the gradients are checked with
+    one bf16 ulp of slack (parity_util.assert_close)."""
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 41, 1500)]
+    _print(f"many users: {len(lengths)} users, T={sum(lengths)}")
+    case = wl.random_case(601, lengths, 2, 64)
+    check_full(case, "bf16", 32, 2, 0.125, backward=True, ulp_slack=True)
+
+
 def test_empty_inputs():
     for lengths in ([], [0], [0, 0, 0]):
         case = wl.random_case(7, lengths, 2, 64)
