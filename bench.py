@@ -131,7 +131,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5,
                     help="1 tiny fp32, 2 fixed bf16, 3 jagged bf16, 4 long context, "
-                         "5 jagged bf16 training step (default)")
+                         "5 jagged bf16 training step (default), 6 the same step with a "
+                         "194-token sliding window (same visible-pair count)")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 2
+#define BLOCKATTN_ABI_VERSION 3
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -62,8 +62,8 @@ typedef enum {
     BLOCKATTN_ERR_INVALID_ARGUMENT = 1, /* batch<0, T<0, H<1, B<1, W<1, non-finite
                                            scale, null or misaligned pointer,
                                            unknown dtype                        */
-    BLOCKATTN_ERR_UNSUPPORTED = 2,      /* D not in {32,64,128}; B not a multiple
-                                           of 16 or above 256; launch too large  */
+    BLOCKATTN_ERR_UNSUPPORTED = 2,      /* D not in {32,64,128}; T above 2^31-1;
+                                           launch too large                     */
     BLOCKATTN_ERR_WORKSPACE = 3,        /* workspace needed but null, too small
                                            or not 256-byte aligned              */
     BLOCKATTN_ERR_HIP = 4               /* a HIP launch reported an error       */
@@ -74,7 +74,8 @@ typedef enum {
  *   batch          number of users (>= 0); offsets has batch+1 entries
  *   total_tokens   T = offsets[batch]; T = 0 or batch = 0 returns OK at once
  *   num_heads      H >= 1;  head_dim D in {32, 64, 128}
- *   block_size     B, a multiple of 16 in [16, 256]
+ *   block_size     B >= 1 (B = 1 with W = w is the token sliding window of
+ *                  w tokens, see blockattn_swa_fwd)
  *   window_blocks  W >= 1 (W = 1: independent blocks)
  *   scale          finite multiplier of <q, k> (typically 1/sqrt(D))
  */
@@ -116,6 +117,32 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v,
                                float scale, blockattn_dtype dtype, void *dq,
                                void *dk, void *dv, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Token-level sliding-window attention: query i of a user sees keys
+ * i - window_tokens < j <= i of the same user.  This is the pattern the pages
+ * name as the predecessor of block attention and the baseline of its speedup
+ * ("GEM (Meta)", section "Custom kernels"); it is block attention with blocks
+ * of one token and a window of window_tokens blocks, and these two calls are
+ * exactly blockattn_fwd / blockattn_bwd with block_size 1 and window_blocks
+ * window_tokens (same layouts, workspace and errors; window_tokens < 1 is
+ * BLOCKATTN_ERR_INVALID_ARGUMENT).
+ */
+blockattn_status blockattn_swa_fwd(const void *q, const void *k, const void *v,
+                                   const int32_t *offsets, int32_t batch,
+                                   int64_t total_tokens, int32_t num_heads,
+                                   int32_t head_dim, int32_t window_tokens,
+                                   float scale, blockattn_dtype dtype, void *out,
+                                   float *lse, hipStream_t stream);
+blockattn_status blockattn_swa_bwd(const void *q, const void *k, const void *v,
+                                   const void *out, const void *dout,
+                                   const float *lse, const int32_t *offsets,
+                                   int32_t batch, int64_t total_tokens,
+                                   int32_t num_heads, int32_t head_dim,
+                                   int32_t window_tokens, float scale,
+                                   blockattn_dtype dtype, void *dq, void *dk,
+                                   void *dv, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *blockattn_status_string(blockattn_status status);

@@ -6,4 +6,5 @@ binding.  ``workloads`` draws the seeded synthetic inputs.
 """
 from .binding import (BF16, FP32, BlockAttnError, blockattn_abi_version,  # noqa: F401
                       blockattn_bwd, blockattn_bwd_workspace_size, blockattn_fwd,
-                      blockattn_status_string, bwd, fwd, library_path, load)
+                      blockattn_status_string, blockattn_swa_bwd, blockattn_swa_fwd, bwd,
+                      fwd, library_path, load, swa_bwd, swa_fwd)

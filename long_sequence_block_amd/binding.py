@@ -20,7 +20,8 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 
 # Every symbol include/blockattn.h declares.
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
-           "blockattn_status_string", "blockattn_abi_version")
+           "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_status_string",
+           "blockattn_abi_version")
 
 _lib = None
 
@@ -53,6 +54,12 @@ def load() -> ctypes.CDLL:
     lib.blockattn_bwd.restype = ctypes.c_int
     lib.blockattn_bwd_workspace_size.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.blockattn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.blockattn_swa_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, f32,
+                                      ctypes.c_int, vp, vp, vp]
+    lib.blockattn_swa_fwd.restype = ctypes.c_int
+    lib.blockattn_swa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                      f32, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.blockattn_swa_bwd.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_abi_version.argtypes = []
@@ -77,6 +84,20 @@ def blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_hea
     return load().blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens,
                                 num_heads, head_dim, block_size, window_blocks, scale,
                                 dtype, dq, dk, dv, workspace, workspace_bytes, stream)
+
+
+def blockattn_swa_fwd(q, k, v, offsets, batch, total_tokens, num_heads, head_dim,
+                      window_tokens, scale, dtype, out, lse, stream) -> int:
+    return load().blockattn_swa_fwd(q, k, v, offsets, batch, total_tokens, num_heads,
+                                    head_dim, window_tokens, scale, dtype, out, lse, stream)
+
+
+def blockattn_swa_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads,
+                      head_dim, window_tokens, scale, dtype, dq, dk, dv, workspace,
+                      workspace_bytes, stream) -> int:
+    return load().blockattn_swa_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens,
+                                    num_heads, head_dim, window_tokens, scale, dtype, dq, dk,
+                                    dv, workspace, workspace_bytes, stream)
 
 
 def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
@@ -163,4 +184,50 @@ def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
                        ws_ptr, ws_len, _stream(stream))
     if rc != OK:
         raise BlockAttnError("blockattn_bwd", rc)
+    return dq, dk, dv
+
+
+def swa_fwd(q, k, v, offsets, window_tokens: int, scale: float, out=None, lse=None,
+            stream=None):
+    """Token sliding-window forward (blockattn_swa_fwd).  Returns (out, lse)."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    rc = blockattn_swa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                           offsets.numel() - 1, T, H, D, window_tokens, float(scale),
+                           _dtype_code(q), out.data_ptr(), lse.data_ptr(), _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_swa_fwd", rc)
+    return out, lse
+
+
+def swa_bwd(q, k, v, out, dout, lse, offsets, window_tokens: int, scale: float,
+            grads=None, workspace=None, stream=None):
+    """Token sliding-window backward (blockattn_swa_bwd).  Returns (dq, dk, dv)."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    for t in (out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("out and dout must match q")
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    code = _dtype_code(q)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    dq, dk, dv = grads
+    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    rc = blockattn_swa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
+                           offsets.numel() - 1, T, H, D, window_tokens, float(scale), code,
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len,
+                           _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_swa_bwd", rc)
     return dq, dk, dv

@@ -24,7 +24,6 @@ blockattn_status check_common(const int32_t *offsets, int32_t batch, int64_t T,
     if (dtype != BLOCKATTN_BF16 && dtype != BLOCKATTN_FP32)
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     if (D != 32 && D != 64 && D != 128) return BLOCKATTN_ERR_UNSUPPORTED;
-    if (B % 16 != 0 || B > 256) return BLOCKATTN_ERR_UNSUPPORTED;
     if (T > INT32_MAX) return BLOCKATTN_ERR_UNSUPPORTED;
     // every launch's grid is bounded by H * (T/B + batch) * ceil(B/32)
     const int64_t tiles = ((T + B - 1) / B + batch) * (int64_t)((B + 31) / 32) * H;
@@ -129,6 +128,27 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
                        : ba::launch_scalar_bwd(s, false, q, k, v, out, dout, lse, dq, dk, dv,
                                                stream);
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+}
+
+blockattn_status blockattn_swa_fwd(const void *q, const void *k, const void *v,
+                                   const int32_t *offsets, int32_t batch, int64_t total_tokens,
+                                   int32_t num_heads, int32_t head_dim, int32_t window_tokens,
+                                   float scale, blockattn_dtype dtype, void *out, float *lse,
+                                   hipStream_t stream) {
+    return blockattn_fwd(q, k, v, offsets, batch, total_tokens, num_heads, head_dim, 1,
+                         window_tokens, scale, dtype, out, lse, stream);
+}
+
+blockattn_status blockattn_swa_bwd(const void *q, const void *k, const void *v,
+                                   const void *out, const void *dout, const float *lse,
+                                   const int32_t *offsets, int32_t batch, int64_t total_tokens,
+                                   int32_t num_heads, int32_t head_dim, int32_t window_tokens,
+                                   float scale, blockattn_dtype dtype, void *dq, void *dk,
+                                   void *dv, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    return blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads,
+                         head_dim, 1, window_tokens, scale, dtype, dq, dk, dv, workspace,
+                         workspace_bytes, stream);
 }
 
 }  // extern "C"

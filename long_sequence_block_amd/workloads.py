@@ -21,7 +21,8 @@ sequences of those shapes stand in for them:
 Random streams: numpy ``Generator(PCG64(SeedSequence([workload, stream])))``
 with stream 0 = lengths, 1 = Q, 2 = K, 3 = V, 4 = dO.  The training-step
 workload reuses the jagged workload's lengths and Q/K/V (workload id 3) and
-draws dO from [5, 4].
+draws dO from [5, 4]; the sliding-window training workload uses the same
+inputs.
 """
 from __future__ import annotations
 
@@ -98,6 +99,13 @@ WORKLOADS = {
                 fixed_length=16384),
     5: Workload(3, "jagged-bf16-train", users=256, heads=8, head_dim=64,
                 block_size=128, window_blocks=2, dtype="bf16", backward=True,
+                dout_wid=5),
+    # The token sliding window (blocks of one token) on the training step's
+    # inputs, with the window whose visible-pair count is closest to the
+    # block pattern's (194 tokens: 36,689,648 pairs per head against
+    # 36,616,647), so that both do the same algorithmic work.
+    6: Workload(3, "sliding-window-bf16-train", users=256, heads=8, head_dim=64,
+                block_size=1, window_blocks=194, dtype="bf16", backward=True,
                 dout_wid=5),
 }
 

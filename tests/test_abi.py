@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 2
+    assert lsb.blockattn_abi_version() == 3
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -63,8 +63,7 @@ def fwd_status(**kw):
     (dict(dtype=7), binding.ERR_INVALID_ARGUMENT),
     (dict(head_dim=48), binding.ERR_UNSUPPORTED),
     (dict(head_dim=256), binding.ERR_UNSUPPORTED),
-    (dict(block_size=40), binding.ERR_UNSUPPORTED),
-    (dict(block_size=512), binding.ERR_UNSUPPORTED),
+    (dict(total_tokens=2**31, batch=1), binding.ERR_UNSUPPORTED),
     (dict(q=None), binding.ERR_INVALID_ARGUMENT),
     (dict(lse=None), binding.ERR_INVALID_ARGUMENT),
     (dict(offsets=None), binding.ERR_INVALID_ARGUMENT),
@@ -93,6 +92,26 @@ def bwd_status(**kw):
 ])
 def test_bwd_argument_checks(kw, code):
     assert bwd_status(**kw) == code
+
+
+def test_sliding_window_argument_checks():
+    """The sliding-window entry points check arguments like blockattn_fwd/bwd
+    (window_tokens is the window in blocks of one token)."""
+    a = dict(q=FAKE, k=FAKE, v=FAKE, offsets=FAKE, batch=2, total_tokens=100,
+             num_heads=2, head_dim=64, window_tokens=0, scale=0.125, dtype=lsb.BF16,
+             out=FAKE, lse=FAKE, stream=None)
+    assert lsb.blockattn_swa_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(window_tokens=16, head_dim=96)
+    assert lsb.blockattn_swa_fwd(*a.values()) == binding.ERR_UNSUPPORTED
+    a.update(total_tokens=0, head_dim=64)
+    assert lsb.blockattn_swa_fwd(*a.values()) == binding.OK
+    b = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, offsets=FAKE,
+             batch=2, total_tokens=100, num_heads=2, head_dim=64, window_tokens=-3,
+             scale=0.125, dtype=lsb.BF16, dq=FAKE, dk=FAKE, dv=FAKE, workspace=FAKE,
+             workspace_bytes=1 << 20, stream=None)
+    assert lsb.blockattn_swa_bwd(*b.values()) == binding.ERR_INVALID_ARGUMENT
+    b.update(window_tokens=8, workspace=None)
+    assert lsb.blockattn_swa_bwd(*b.values()) == binding.ERR_WORKSPACE
 
 
 def test_workspace_size():

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from long_sequence_block_amd import workloads as wl
+import long_sequence_block_amd as lsb
 from parity_util import (assert_close, check_full, check_sampled, np64, run_bwd, run_fwd,
                          to_device)
 
@@ -30,6 +31,8 @@ SMALL = [
     ([100, 37, 0, 300, 1], 2, 64, 64, 2, "bf16"),
     ([129, 255, 513, 7], 2, 64, 128, 2, "bf16"),
     ([1000, 16, 17], 1, 128, 256, 4, "bf16"),
+    ([256, 257, 511, 1100, 3, 0], 2, 128, 256, 2, "bf16"),
+    ([700, 256, 40], 1, 128, 256, 1, "bf16"),
     ([77, 300, 5], 3, 32, 16, 3, "bf16"),
     ([90, 200], 2, 64, 48, 2, "bf16"),
     ([333, 64, 65], 2, 128, 64, 1, "bf16"),
@@ -37,6 +40,11 @@ SMALL = [
     ([100, 37, 0, 300, 1], 2, 64, 64, 2, "fp32"),
     ([129, 600], 2, 128, 128, 3, "fp32"),
     ([45, 80], 2, 32, 16, 2, "fp32"),
+    # block sizes that are not multiples of 16, or above 256
+    ([100, 37, 300], 2, 64, 7, 3, "bf16"),
+    ([600, 5], 1, 128, 100, 2, "bf16"),
+    ([513, 20], 2, 64, 300, 1, "bf16"),
+    ([77, 130], 2, 32, 5, 4, "fp32"),
 ]
 
 
@@ -46,6 +54,56 @@ def test_small_cases_every_element(idx):
     _print(f"small case {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype}")
     case = wl.random_case(500 + idx, lengths, H, D)
     check_full(case, dtype, B, W, 1.0 / math.sqrt(D), backward=True)
+
+
+SLIDING = [
+    # (lengths, H, D, window_tokens, dtype): the token sliding window, i.e.
+    # blocks of one token, through blockattn_swa_fwd / blockattn_swa_bwd
+    ([300, 1, 0, 129], 2, 64, 1, "bf16"),
+    ([500, 77], 2, 64, 37, "bf16"),
+    ([700, 64, 3], 1, 128, 200, "bf16"),
+    ([260, 31], 3, 32, 64, "bf16"),
+    ([90, 300], 2, 64, 1000, "bf16"),   # longer than every user: causal attention
+    ([200, 45], 2, 64, 19, "fp32"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SLIDING)))
+def test_sliding_window_every_element(idx):
+    lengths, H, D, w, dtype = SLIDING[idx]
+    _print(f"sliding window {idx}: lengths={lengths} H={H} D={D} w={w} {dtype}")
+    case = wl.random_case(800 + idx, lengths, H, D)
+    dev, host = to_device(case, dtype)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = lsb.swa_fwd(dev["q"], dev["k"], dev["v"], dev["offsets"], w, scale)
+    o_ref, l_ref = oracle.fwd(host["q"], host["k"], host["v"], host["offsets"], 1, w, scale)
+    assert_close("out", np64(out), o_ref, dtype)
+    assert_close("lse", np64(lse), l_ref, dtype, is_lse=True)
+    grads = lsb.swa_bwd(dev["q"], dev["k"], dev["v"], out, dev["dout"], lse, dev["offsets"],
+                        w, scale)
+    refs = oracle.bwd(host["q"], host["k"], host["v"], host["dout"], host["offsets"], 1, w,
+                      scale)
+    for name, g, ref in zip(("dq", "dk", "dv"), grads, refs):
+        assert_close(name, np64(g), ref, dtype)
+    # the same call as block attention with blocks of one token
+    out_b, lse_b = run_fwd(dev, 1, w, scale)
+    assert torch.equal(out_b, out) and torch.equal(lse_b, lse)
+    torch.cuda.synchronize()
+
+
+NEG_SCALE = [
+    # (lengths, H, D, B, W): a negative scale flips which key dominates
+    ([300, 64, 129], 2, 64, 64, 2),
+    ([600, 100], 1, 128, 256, 3),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(NEG_SCALE)))
+def test_negative_scale_every_element(idx):
+    lengths, H, D, B, W = NEG_SCALE[idx]
+    _print(f"negative scale {idx}: lengths={lengths} H={H} D={D} B={B} W={W}")
+    case = wl.random_case(700 + idx, lengths, H, D)
+    check_full(case, "bf16", B, W, -1.0 / math.sqrt(D), backward=True)
 
 
 def test_many_users_every_element():
@@ -95,7 +153,7 @@ def _samples(off, B, rng, n_users=6):
     return out
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6])
 def test_workload_full_size_sampled(wid):
     w = wl.WORKLOADS[wid]
     _print(f"workload {wid} ({w.name}) full size, sampled rows")

@@ -186,6 +186,56 @@ def test_brute_force_general_window(B, W):
         np.testing.assert_allclose(lse[:, a:b], lse_ref, atol=1e-12, rtol=0)
 
 
+# -------------------------------------------- token sliding window (B = 1)
+#
+# The sliding window that block attention replaced ("GEM (Meta)", section
+# "Custom kernels") is computed as blocks of one token with a window of w
+# blocks.  These pins tie that path to the token band written directly.
+
+
+def band_mask(L, w):
+    """The token band i - w < j <= i, with no block index in it."""
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    return (j <= i) & (i - j < w)
+
+
+@pytest.mark.parametrize("w", [1, 2, 5, 16, 100])
+def test_sliding_window_is_a_token_band(w):
+    lengths = [0, 1, 7, 30, 64]
+    c = case(300 + w, lengths, H=2, D=6)
+    sc = 0.45
+    out, lse = oracle.fwd(c["q"], c["k"], c["v"], c["offsets"], 1, w, sc)
+    off = c["offsets"]
+    for u, L in enumerate(lengths):
+        a, b = off[u], off[u + 1]
+        if L == 0:
+            continue
+        mask = band_mask(L, w)
+        t = [torch.from_numpy(np.ascontiguousarray(c[n][a:b].transpose(1, 0, 2))) for n in "qk"]
+        vt = torch.from_numpy(np.ascontiguousarray(c["v"][a:b].transpose(1, 0, 2)))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            t[0], t[1], vt, attn_mask=torch.from_numpy(mask), scale=sc)
+        np.testing.assert_allclose(out[a:b], ref.numpy().transpose(1, 0, 2), atol=1e-12, rtol=0)
+        s = np.einsum("hid,hjd->hij", t[0].numpy(), t[1].numpy()) * sc
+        lse_ref = logsumexp(np.where(mask[None], s, -np.inf), axis=-1)
+        np.testing.assert_allclose(lse[:, a:b], lse_ref, atol=1e-12, rtol=0)
+
+
+def test_sliding_window_of_one_token():
+    """w = 1: every query sees only itself, so out = v, lse = scale <q_i, k_i>,
+    dV = dO, and dQ = dK = 0 (a softmax over a single key is constant)."""
+    c = case(320, [9, 0, 4], H=2, D=5)
+    sc = 0.8
+    out, lse = oracle.fwd(c["q"], c["k"], c["v"], c["offsets"], 1, 1, sc)
+    np.testing.assert_allclose(out, c["v"], atol=1e-15, rtol=0)
+    np.testing.assert_allclose(lse, sc * np.sum(c["q"] * c["k"], axis=2).T, atol=1e-14, rtol=0)
+    dq, dk, dv = oracle.bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], 1, 1, sc)
+    np.testing.assert_allclose(dv, c["dout"], atol=1e-15, rtol=0)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+
+
 def test_pair_count_against_mask_and_closed_form():
     rs = np.random.default_rng(0)
     for _ in range(30):
@@ -297,7 +347,7 @@ def _loss(c, q, k, v, B, W, sc):
     return float(np.sum(out * c["dout"]))
 
 
-@pytest.mark.parametrize("B,W", [(4, 1), (4, 2), (3, 3)])
+@pytest.mark.parametrize("B,W", [(4, 1), (4, 2), (3, 3), (1, 4)])
 def test_backward_matches_central_finite_differences(B, W):
     c = case(21 + B + W, [11, 0, 6], H=2, D=3)
     sc, eps = 0.7, 1e-6
@@ -360,5 +410,9 @@ def test_workload_generator_shapes():
     off = w.offsets()
     assert off[0] == 0 and off[-1] == L.sum() and off.dtype == np.int32
     assert wl.WORKLOADS[5].offsets().tolist() == off.tolist()
+    assert wl.WORKLOADS[6].offsets().tolist() == off.tolist()
+    # the sliding window of workload 6 matches the block pattern's work to 0.2%
+    blk, swa = oracle.pair_count(off, 128, 2), oracle.pair_count(off, 1, 194)
+    assert abs(swa / blk - 1) < 2.1e-3
     # median of a lognormal(ln 600, 0.8) sample of 256 sits near 600
     assert 450 < np.median(L) < 750
