@@ -144,3 +144,63 @@ def probs(q, k, offsets, block_size: int, window_blocks: int, scale: float,
     if rc != 0:
         raise ValueError(f"oracle_probs failed with status {rc}")
     return P
+
+
+# ------------------------------------------------- rotary position embedding
+#
+# The production block-attention kernel fuses the backward of a rotary
+# position embedding ("GEM (Meta)" on aiwiki.ai, section "Custom kernels").
+# The pages name the embedding but not its variant, base or positions.  The
+# readings taken: the rotate-half form (feature d pairs with d + D/2), the
+# angle of pair d at position p is p * base**(-2d/D) with base 10000 unless
+# given, and p is the token's index inside its own user (positions restart
+# at every user, like the blocks).  Applied to Q and K only.  Plain numpy,
+# fp64.
+
+
+def rope_positions(offsets) -> np.ndarray:
+    """Local index of every packed token inside its user, [T] int64."""
+    off = _i32(offsets)
+    pos = np.zeros(int(off[-1]), np.int64)
+    for u in range(len(off) - 1):
+        pos[off[u]:off[u + 1]] = np.arange(off[u + 1] - off[u])
+    return pos
+
+
+def rope_angles(offsets, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """[T, D/2] rotation angles: position times base**(-2d/D)."""
+    if head_dim % 2:
+        raise ValueError("rotary embedding needs an even head dim")
+    d = np.arange(head_dim // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * d / head_dim)
+    return rope_positions(offsets).astype(np.float64)[:, None] * theta[None, :]
+
+
+def _rotate(x, offsets, base, sign):
+    x = _f64(x)
+    T, H, D = x.shape
+    a = rope_angles(offsets, D, base)[:, None, :]        # [T, 1, D/2]
+    c, s = np.cos(a), sign * np.sin(a)
+    lo, hi = x[..., :D // 2], x[..., D // 2:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def rope(x, offsets, base: float = 10000.0) -> np.ndarray:
+    """Rotate every (token, head) row of x [T, H, D]: each pair
+    (x_d, x_{d+D/2}) turns by its angle."""
+    return _rotate(x, offsets, base, 1.0)
+
+
+def rope_transpose(x, offsets, base: float = 10000.0) -> np.ndarray:
+    """The transpose (inverse) rotation, which is the backward of rope."""
+    return _rotate(x, offsets, base, -1.0)
+
+
+def rope_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int,
+             scale: float, base: float = 10000.0):
+    """Gradients with respect to the unrotated q and k (and v) of
+    sum(dout * attention(rope(q), rope(k), v)): the chain rule through the
+    rotation, which is its transpose."""
+    dqr, dkr, dv = bwd(rope(q, offsets, base), rope(k, offsets, base), v, dout, offsets,
+                       block_size, window_blocks, scale)
+    return rope_transpose(dqr, offsets, base), rope_transpose(dkr, offsets, base), dv

@@ -416,3 +416,113 @@ def test_workload_generator_shapes():
     assert abs(swa / blk - 1) < 2.1e-3
     # median of a lognormal(ln 600, 0.8) sample of 256 sits near 600
     assert 450 < np.median(L) < 750
+
+
+# ---------------------------------------------------- rotary embedding
+#
+# The rotate-half rotary embedding the production kernel's backward fuses
+# ("GEM (Meta)", section "Custom kernels"), with the readings stated in the
+# oracle (angle p * base**(-2d/D), p the index inside the user).
+
+
+def test_rope_single_pair_turns_by_the_position():
+    """D = 2: the only frequency is base**0 = 1, so the token at position p
+    turns (x0, x1) by p radians (math.cos / math.sin)."""
+    off = np.array([0, 6], np.int32)
+    x = np.zeros((6, 1, 2))
+    x[:, 0, 0], x[:, 0, 1] = 1.0, 0.5
+    r = oracle.rope(x, off)
+    for p in range(6):
+        c, s = math.cos(p), math.sin(p)
+        assert abs(r[p, 0, 0] - (c - 0.5 * s)) < 1e-15
+        assert abs(r[p, 0, 1] - (0.5 * c + s)) < 1e-15
+
+
+def test_rope_second_frequency_follows_the_base():
+    """D = 4: the second pair (features 1 and 3) turns by base**(-1/2) per
+    position: 0.01 rad for base 10000 (position 100 turns it by 1 rad) and
+    0.1 rad for base 100 (position 30 turns it by 3 rad)."""
+    for base, p, ang in ((10000.0, 100, 1.0), (100.0, 30, 3.0)):
+        off = np.array([0, p + 1], np.int32)
+        x = np.zeros((p + 1, 1, 4))
+        x[:, 0, 1] = 1.0
+        r = oracle.rope(x, off, base)
+        np.testing.assert_allclose(r[p, 0], [0.0, math.cos(ang), 0.0, math.sin(ang)],
+                                   atol=1e-13)
+        # the first pair has zero input and stays zero; the turn is p, not p+1
+        np.testing.assert_allclose(r[1, 0, [1, 3]],
+                                   [math.cos(ang / p), math.sin(ang / p)], atol=1e-15)
+
+
+def test_rope_is_complex_multiplication():
+    """As complex numbers z_d = x_d + i x_{d+D/2}, the embedding multiplies
+    z_d by exp(i p theta_d) (numpy complex exponential)."""
+    c = case(400, [9, 0, 13], H=2, D=8)
+    r = oracle.rope(c["q"], c["offsets"], 500.0)
+    z = c["q"][..., :4] + 1j * c["q"][..., 4:]
+    pos = np.concatenate([np.arange(9), np.arange(13)]).astype(np.float64)
+    theta = 500.0 ** (-np.arange(4) / 4.0)
+    zr = z * np.exp(1j * pos[:, None, None] * theta[None, None, :])
+    np.testing.assert_allclose(r[..., :4], zr.real, atol=1e-13)
+    np.testing.assert_allclose(r[..., 4:], zr.imag, atol=1e-13)
+
+
+def test_rope_scores_depend_only_on_the_offset():
+    """One q and one k vector repeated at every position: the rotated scores
+    <rope(q)_i, rope(k)_j> form a Toeplitz matrix (they depend on i - j only),
+    in every user, since positions restart per user."""
+    rs = np.random.default_rng(5)
+    qv, kv = rs.standard_normal(16), rs.standard_normal(16)
+    lengths = [20, 7]
+    off = wl.offsets_from_lengths(lengths)
+    T = sum(lengths)
+    q = np.tile(qv, (T, 1, 1))
+    k = np.tile(kv, (T, 1, 1))
+    qr, kr = oracle.rope(q, off), oracle.rope(k, off)
+    for u, L in enumerate(lengths):
+        a = off[u]
+        S = qr[a:a + L, 0] @ kr[a:a + L, 0].T
+        for dlt in range(-L + 1, L):
+            diag = np.diagonal(S, dlt)
+            np.testing.assert_allclose(diag, diag[0], atol=1e-12)
+    # and the first user's scores equal the second's for the same offsets
+    S0 = qr[:7, 0] @ kr[:7, 0].T
+    S1 = qr[20:27, 0] @ kr[20:27, 0].T
+    np.testing.assert_allclose(S0, S1, atol=1e-12)
+
+
+def test_rope_is_a_rotation():
+    c = case(401, [30, 4], H=3, D=16)
+    r = oracle.rope(c["k"], c["offsets"])
+    np.testing.assert_allclose(np.linalg.norm(r, axis=2), np.linalg.norm(c["k"], axis=2),
+                               atol=1e-12)
+    np.testing.assert_array_equal(r[0], c["k"][0])      # position 0 of user 0
+    np.testing.assert_array_equal(r[30], c["k"][30])    # position 0 of user 1
+    np.testing.assert_allclose(oracle.rope_transpose(r, c["offsets"]), c["k"], atol=1e-12)
+
+
+def test_rope_backward_matches_central_finite_differences():
+    """Gradients of sum(dO * attention(rope(q), rope(k), v)) with respect to
+    the unrotated q, k and v."""
+    c = case(402, [9, 5], H=1, D=4)
+    B, W, sc, base, eps = 2, 2, 0.6, 50.0, 1e-6
+
+    def loss(q, k, v):
+        o, _ = oracle.fwd(oracle.rope(q, c["offsets"], base), oracle.rope(k, c["offsets"], base),
+                          v, c["offsets"], B, W, sc)
+        return float(np.sum(o * c["dout"]))
+
+    grads = oracle.rope_bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], B, W, sc, base)
+    for name, grad in zip("qkv", grads):
+        num = np.zeros_like(grad)
+        it = np.nditer(grad, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args = {n: c[n].copy() for n in "qkv"}
+            args[name][idx] += eps
+            fp = loss(args["q"], args["k"], args["v"])
+            args[name][idx] -= 2 * eps
+            fm = loss(args["q"], args["k"], args["v"])
+            num[idx] = (fp - fm) / (2 * eps)
+        err = np.abs(num - grad).max() / max(np.abs(grad).max(), 1e-30)
+        assert err <= 1e-6, (name, err)
