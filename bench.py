@@ -36,7 +36,7 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "block-attention TFLOP/s and tokens/s (fwd+bwd, jagged bf16) and % of MFMA peak"
 KERNEL_SOURCES = ("common.h", "kernels.h", "mfma_util.h", "lds_tile.h", "api.hip",
-                  "scalar_kernels.hip", "mfma_fwd.hip", "mfma_bwd.hip")
+                  "scalar_kernels.hip", "mfma_fwd.hip", "mfma_bwd.hip", "rope.hip")
 
 
 def pairs_per_head(offsets: np.ndarray, B: int, W: int) -> int:
@@ -89,10 +89,15 @@ def cpu_baseline(w, users: int, flops_per_pair_head: float):
             host[key] = t.to(torch.float64).numpy()
     off = host["offsets"]
     t0 = time.perf_counter()
-    oracle.fwd(host["q"], host["k"], host["v"], off, w.block_size, w.window_blocks, w.scale)
-    if w.backward:
-        oracle.bwd(host["q"], host["k"], host["v"], host["dout"], off, w.block_size,
-                   w.window_blocks, w.scale)
+    q, k = host["q"], host["k"]
+    if w.rope_base:
+        q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
+    oracle.fwd(q, k, host["v"], off, w.block_size, w.window_blocks, w.scale)
+    if w.backward and w.rope_base:
+        oracle.rope_bwd(q, k, host["v"], host["dout"], off, w.block_size, w.window_blocks,
+                        w.scale, w.rope_base)
+    elif w.backward:
+        oracle.bwd(q, k, host["v"], host["dout"], off, w.block_size, w.window_blocks, w.scale)
     dt = time.perf_counter() - t0
     flops = flops_per_pair_head * pairs_per_head(off, w.block_size, w.window_blocks) * w.heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -132,7 +137,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5,
                     help="1 tiny fp32, 2 fixed bf16, 3 jagged bf16, 4 long context, "
                          "5 jagged bf16 training step (default), 6 the same step with a "
-                         "194-token sliding window (same visible-pair count)")
+                         "194-token sliding window (same visible-pair count), 7 the training "
+                         "step with the rotary embedding (rope, fwd, fused rope backward)")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,18 +185,25 @@ def main():
     ws_n = lsb.blockattn_bwd_workspace_size(T, d["offsets"].numel() - 1, H,
                                            lsb.BF16 if w.dtype == "bf16" else lsb.FP32)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    rb = w.rope_base
+    qa, ka = (torch.empty_like(d["q"]), torch.empty_like(d["k"])) if rb else (d["q"], d["k"])
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        lsb.fwd(d["q"], d["k"], d["v"], d["offsets"], B, W, sc, out=out, lse=lse)
+        if rb:  # rotary embedding of q and k into qa, ka
+            lsb.rope(d["q"], d["k"], d["offsets"], rb, q_rot=qa, k_rot=ka)
+        lsb.fwd(qa, ka, d["v"], d["offsets"], B, W, sc, out=out, lse=lse)
         if ev is not None:
             ev[1].record()
-        if w.backward:
-            lsb.bwd(d["q"], d["k"], d["v"], out, d["dout"], lse, d["offsets"], B, W, sc,
+        if w.backward and rb:  # gradients through attention and the rotation
+            lsb.rope_bwd(qa, ka, d["v"], out, d["dout"], lse, d["offsets"], B, W, sc, rb,
+                         grads=grads, workspace=ws)
+        elif w.backward:
+            lsb.bwd(qa, ka, d["v"], out, d["dout"], lse, d["offsets"], B, W, sc,
                     grads=grads, workspace=ws)
-            if ev is not None:
-                ev[2].record()
+        if w.backward and ev is not None:
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
@@ -211,7 +224,7 @@ def main():
     e = 2 if w.dtype == "bf16" else 4
     fwd_flops = 4.0 * D * npair * H
     bwd_flops = 8.0 * D * npair * H if w.backward else 0.0
-    fwd_bytes = T * H * (4.0 * D * e + 4)
+    fwd_bytes = T * H * (4.0 * D * e + 4) + (4.0 * T * H * D * e if rb else 0.0)
     bwd_bytes = T * H * (8.0 * D * e + 4) if w.backward else 0.0
     flops = fwd_flops + bwd_flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -245,6 +258,7 @@ def main():
         "config": {"workload": w.name, "users": w.users, "tokens": T, "heads": H,
                    "head_dim": D, "block_size": B, "window_blocks": W,
                    "backward": w.backward, "pairs_per_head": npair,
+                   **({"rope_base": rb} if rb else {}),
                    "parallelism": "single GPU"},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * tflops / peak, 3),

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 3
+#define BLOCKATTN_ABI_VERSION 4
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -143,6 +143,49 @@ blockattn_status blockattn_swa_bwd(const void *q, const void *k, const void *v,
                                    blockattn_dtype dtype, void *dq, void *dk,
                                    void *dv, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Rotary position embedding.  The production block-attention kernel carries
+ * a rotary embedding and fuses its backward ("GEM (Meta)", section "Custom
+ * kernels"); the pages give neither its form nor its base nor the positions.
+ * Readings: the rotate-half form, angle p * theta_base^(-2d/D) for the pair
+ * of features (d, d + D/2), d < D/2, and p the token's index inside its own
+ * user (positions restart at every user, like the blocks).  For each token
+ * and head of q and k:
+ *     x_rot[d]       = x[d] cos - x[d + D/2] sin
+ *     x_rot[d + D/2] = x[d + D/2] cos + x[d] sin
+ * Writes q_rot and k_rot [T, H, D] (dtype; fp32 arithmetic, the angle reduced
+ * in fp64).  q_rot may be q and k_rot may be k (in place); otherwise outputs
+ * must not overlap inputs.  theta_base must be finite and > 0 (typically
+ * 10000), else BLOCKATTN_ERR_INVALID_ARGUMENT.  Other arguments, layouts and
+ * errors as for blockattn_fwd.  The attention forward then runs on q_rot and
+ * k_rot (blockattn_fwd), and blockattn_rope_bwd gives the gradients.
+ */
+blockattn_status blockattn_rope(const void *q, const void *k, const int32_t *offsets,
+                                int32_t batch, int64_t total_tokens,
+                                int32_t num_heads, int32_t head_dim,
+                                float theta_base, blockattn_dtype dtype,
+                                void *q_rot, void *k_rot, hipStream_t stream);
+
+/*
+ * Backward of blockattn_fwd(q_rot, k_rot, v) with the rotary embedding's
+ * backward fused in: takes the rotated q_rot and k_rot (as blockattn_rope
+ * wrote them) with v, out, lse and dout, and writes dq and dk with respect
+ * to the UNROTATED q and k (each row turned back by its position's angles,
+ * R(p)^T, inside the kernel that computes it) and dv.  theta_base as for
+ * blockattn_rope; everything else as for blockattn_bwd.
+ */
+blockattn_status blockattn_rope_bwd(const void *q_rot, const void *k_rot,
+                                    const void *v, const void *out,
+                                    const void *dout, const float *lse,
+                                    const int32_t *offsets, int32_t batch,
+                                    int64_t total_tokens, int32_t num_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t window_blocks, float scale,
+                                    float theta_base, blockattn_dtype dtype,
+                                    void *dq, void *dk, void *dv,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *blockattn_status_string(blockattn_status status);

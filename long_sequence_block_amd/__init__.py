@@ -6,5 +6,6 @@ binding.  ``workloads`` draws the seeded synthetic inputs.
 """
 from .binding import (BF16, FP32, BlockAttnError, blockattn_abi_version,  # noqa: F401
                       blockattn_bwd, blockattn_bwd_workspace_size, blockattn_fwd,
-                      blockattn_status_string, blockattn_swa_bwd, blockattn_swa_fwd, bwd,
-                      fwd, library_path, load, swa_bwd, swa_fwd)
+                      blockattn_rope, blockattn_rope_bwd, blockattn_status_string,
+                      blockattn_swa_bwd, blockattn_swa_fwd, bwd, fwd, library_path, load,
+                      rope, rope_bwd, swa_bwd, swa_fwd)

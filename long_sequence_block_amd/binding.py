@@ -20,8 +20,8 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 
 # Every symbol include/blockattn.h declares.
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
-           "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_status_string",
-           "blockattn_abi_version")
+           "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_rope", "blockattn_rope_bwd",
+           "blockattn_status_string", "blockattn_abi_version")
 
 _lib = None
 
@@ -60,6 +60,13 @@ def load() -> ctypes.CDLL:
     lib.blockattn_swa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                       f32, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.blockattn_swa_bwd.restype = ctypes.c_int
+    lib.blockattn_rope.argtypes = [vp, vp, vp, i32, i64, i32, i32, f32, ctypes.c_int, vp, vp,
+                                   vp]
+    lib.blockattn_rope.restype = ctypes.c_int
+    lib.blockattn_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                       i32, f32, f32, ctypes.c_int, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
+    lib.blockattn_rope_bwd.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_abi_version.argtypes = []
@@ -98,6 +105,21 @@ def blockattn_swa_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num
     return load().blockattn_swa_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens,
                                     num_heads, head_dim, window_tokens, scale, dtype, dq, dk,
                                     dv, workspace, workspace_bytes, stream)
+
+
+def blockattn_rope(q, k, offsets, batch, total_tokens, num_heads, head_dim, theta_base, dtype,
+                   q_rot, k_rot, stream) -> int:
+    return load().blockattn_rope(q, k, offsets, batch, total_tokens, num_heads, head_dim,
+                                 theta_base, dtype, q_rot, k_rot, stream)
+
+
+def blockattn_rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, batch, total_tokens,
+                       num_heads, head_dim, block_size, window_blocks, scale, theta_base, dtype,
+                       dq, dk, dv, workspace, workspace_bytes, stream) -> int:
+    return load().blockattn_rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, batch,
+                                     total_tokens, num_heads, head_dim, block_size,
+                                     window_blocks, scale, theta_base, dtype, dq, dk, dv,
+                                     workspace, workspace_bytes, stream)
 
 
 def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
@@ -230,4 +252,53 @@ def swa_bwd(q, k, v, out, dout, lse, offsets, window_tokens: int, scale: float,
                            _stream(stream))
     if rc != OK:
         raise BlockAttnError("blockattn_swa_bwd", rc)
+    return dq, dk, dv
+
+
+def rope(q, k, offsets, theta_base: float = 10000.0, q_rot=None, k_rot=None, stream=None):
+    """Rotary embedding of q and k (blockattn_rope).  Returns (q_rot, k_rot);
+    pass q_rot=q, k_rot=k to rotate in place."""
+    _check(q, k, q, offsets)
+    T, H, D = q.shape
+    q_rot = torch.empty_like(q) if q_rot is None else q_rot
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    for t in (q_rot, k_rot):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q_rot and k_rot must match q")
+    rc = blockattn_rope(q.data_ptr(), k.data_ptr(), offsets.data_ptr(), offsets.numel() - 1, T,
+                        H, D, float(theta_base), _dtype_code(q), q_rot.data_ptr(),
+                        k_rot.data_ptr(), _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_rope", rc)
+    return q_rot, k_rot
+
+
+def rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
+             scale: float, theta_base: float = 10000.0, grads=None, workspace=None,
+             stream=None):
+    """Backward through attention and the rotary embedding (blockattn_rope_bwd):
+    (dq, dk, dv) with dq, dk taken with respect to the unrotated q, k."""
+    _check(q_rot, k_rot, v, offsets)
+    T, H, D = q_rot.shape
+    for t in (out, dout):
+        if t.shape != q_rot.shape or t.dtype != q_rot.dtype or not t.is_contiguous():
+            raise ValueError("out and dout must match q")
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    code = _dtype_code(q_rot)
+    if grads is None:
+        grads = tuple(torch.empty_like(q_rot) for _ in range(3))
+    dq, dk, dv = grads
+    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_rot.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    rc = blockattn_rope_bwd(q_rot.data_ptr(), k_rot.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
+                            offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                            float(scale), float(theta_base), code, dq.data_ptr(),
+                            dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_rope_bwd", rc)
     return dq, dk, dv

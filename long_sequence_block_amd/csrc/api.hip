@@ -50,7 +50,41 @@ ba::Shape make_shape(const int32_t *offsets, int32_t batch, int64_t T, int32_t H
     s.B = B;
     s.W = W;
     s.scale = scale;
+    s.rope_base = 0.f;
     return s;
+}
+
+// The backward entry points: plain (rope_base 0) or through a rotary
+// embedding of q and k (rope_base > 0, q and k already rotated).
+blockattn_status backward(const void *q, const void *k, const void *v, const void *out,
+                          const void *dout, const float *lse, const int32_t *offsets,
+                          int32_t batch, int64_t total_tokens, int32_t num_heads,
+                          int32_t head_dim, int32_t block_size, int32_t window_blocks,
+                          float scale, float rope_base, blockattn_dtype dtype, void *dq,
+                          void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    bool empty;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
+                                       block_size, window_blocks, scale, dtype, &empty);
+    if (st != BLOCKATTN_OK || empty) return st;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const size_t need = blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
+        return BLOCKATTN_ERR_WORKSPACE;
+    ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, block_size,
+                             window_blocks, scale);
+    s.rope_base = rope_base;
+    hipError_t e = dtype == BLOCKATTN_BF16
+                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, workspace,
+                                             stream)
+                       : ba::launch_scalar_bwd(s, false, q, k, v, out, dout, lse, dq, dk, dv,
+                                               stream);
+    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -107,27 +141,43 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
                                float scale, blockattn_dtype dtype, void *dq, void *dk,
                                void *dv, void *workspace, size_t workspace_bytes,
                                hipStream_t stream) {
+    return backward(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads, head_dim,
+                    block_size, window_blocks, scale, 0.f, dtype, dq, dk, dv, workspace,
+                    workspace_bytes, stream);
+}
+
+blockattn_status blockattn_rope(const void *q, const void *k, const int32_t *offsets,
+                                int32_t batch, int64_t total_tokens, int32_t num_heads,
+                                int32_t head_dim, float theta_base, blockattn_dtype dtype,
+                                void *q_rot, void *k_rot, hipStream_t stream) {
     bool empty;
-    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
-                                       block_size, window_blocks, scale, dtype, &empty);
-    if (st != BLOCKATTN_OK || empty) return st;
-    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    // B and W do not enter the embedding; 1 and 1 pass the shared checks
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim, 1, 1,
+                                       1.f, dtype, &empty);
+    if (st != BLOCKATTN_OK) return st;
+    if (!isfinite(theta_base) || !(theta_base > 0.f)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (empty) return BLOCKATTN_OK;
+    if (!q || !k || !q_rot || !k_rot) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_rot) || !aligned16(k_rot))
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
-        !aligned16(dv))
-        return BLOCKATTN_ERR_INVALID_ARGUMENT;
-    const size_t need = blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype);
-    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
-        return BLOCKATTN_ERR_WORKSPACE;
-    const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
-                                   block_size, window_blocks, scale);
-    hipError_t e = dtype == BLOCKATTN_BF16
-                       ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, workspace,
-                                             stream)
-                       : ba::launch_scalar_bwd(s, false, q, k, v, out, dout, lse, dq, dk, dv,
-                                               stream);
+    ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, 1, 1, 1.f);
+    s.rope_base = theta_base;
+    const hipError_t e = ba::launch_rope(s, dtype == BLOCKATTN_BF16, q, k, q_rot, k_rot, stream);
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+}
+
+blockattn_status blockattn_rope_bwd(const void *q_rot, const void *k_rot, const void *v,
+                                    const void *out, const void *dout, const float *lse,
+                                    const int32_t *offsets, int32_t batch, int64_t total_tokens,
+                                    int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t window_blocks, float scale, float theta_base,
+                                    blockattn_dtype dtype, void *dq, void *dk, void *dv,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (!isfinite(theta_base) || !(theta_base > 0.f)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    return backward(q_rot, k_rot, v, out, dout, lse, offsets, batch, total_tokens, num_heads,
+                    head_dim, block_size, window_blocks, scale, theta_base, dtype, dq, dk, dv,
+                    workspace, workspace_bytes, stream);
 }
 
 blockattn_status blockattn_swa_fwd(const void *q, const void *k, const void *v,

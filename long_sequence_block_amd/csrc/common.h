@@ -32,6 +32,8 @@ struct Shape {
     int B;  // block size (tokens)
     int W;  // window in blocks, own block included
     float scale;
+    float rope_base;  // > 0: the backward returns gradients through a rotary
+                      // embedding with this base (see rope_sincos); 0: none
 };
 
 // One tile of work: sub-tile `sub` of row unit `blk` (local to the user), head
@@ -141,6 +143,29 @@ inline int64_t grid_upper_bound(int64_t T, int batch, int R, int tpb, int H) {
     const int64_t blocks = (T + R - 1) / R + batch;
     const int64_t g = blocks * tpb * H;
     return (g + 8 * kRun - 1) / (8 * kRun) * (8 * kRun);
+}
+
+// Rotary embedding angles.  Pair d (features d and d + D/2) of a token at
+// position p turns by p * base^(-2d/D) radians; the kernels carry it as
+// `turns` = that angle / (2 pi), computed in fp64, and reduce it to
+// [-1/2, 1/2] turn before taking the sine and cosine, so large positions
+// keep full accuracy.  bf16 paths use the hardware's turn-based sine and
+// cosine (fp32); the fp32 path takes them in fp64.
+constexpr double kInv2Pi = 0.15915494309189533577;
+template <typename TI>
+__device__ __forceinline__ void rope_sincos(double turns, float &s, float &c);
+template <>
+__device__ __forceinline__ void rope_sincos<bf16>(double turns, float &s, float &c) {
+    const float f = (float)(turns - rint(turns));
+    s = __builtin_amdgcn_sinf(f);
+    c = __builtin_amdgcn_cosf(f);
+}
+template <>
+__device__ __forceinline__ void rope_sincos<float>(double turns, float &s, float &c) {
+    double sd, cd;
+    sincos((turns - rint(turns)) * 6.283185307179586477, &sd, &cd);
+    s = (float)sd;
+    c = (float)cd;
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

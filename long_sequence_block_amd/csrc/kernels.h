@@ -14,6 +14,11 @@ hipError_t launch_scalar_bwd(const Shape &s, bool bf16_io, const void *q, const 
                              const void *v, const void *out, const void *dout,
                              const float *lse, void *dq, void *dk, void *dv, hipStream_t st);
 
+// Rotary embedding of q and k (rotate-half, per-user positions, base
+// s.rope_base) into q_rot and k_rot; bf16 or fp32 storage.
+hipError_t launch_rope(const Shape &s, bool bf16_io, const void *q, const void *k, void *q_rot,
+                       void *k_rot, hipStream_t st);
+
 // bf16 MFMA forward.
 hipError_t launch_mfma_fwd(const Shape &s, const void *q, const void *k, const void *v,
                            void *out, float *lse, hipStream_t st);

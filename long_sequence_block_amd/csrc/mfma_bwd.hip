@@ -158,25 +158,57 @@ template <int D>
 constexpr int kStores(int role) { return role == 0 ? D / 16 : D / 8; }
 
 // Writes a wave's 32 rows of one output (scaled by mul) as bf16; rows past
-// the tile are clipped by the buffer range.
+// the tile are clipped by the buffer range.  With a rotary table (rrev, in
+// LDS: turns per position of each pair), the rows are first turned back by
+// their position's angles, which is the backward of the rotary embedding
+// applied to q and k before attention: the gradient with respect to the
+// unrotated input is R(p)^T times the gradient with respect to the rotated
+// one.  The lane holds column 32 dt + 16 half + 8 g + e in register
+// 8 half + e of acc[dt], so both columns of a pair (c, c + D/2) are in the
+// same lane: acc[dt + D/64] for D >= 64, the other half for D = 32.
 template <int D>
 __device__ __forceinline__ void store_rows(bf16 *dst_tile, int rows, int64_t rs, uint32_t lrow,
-                                           const f32x16 (&acc)[D / 32], float mul, int g) {
+                                           const f32x16 (&acc)[D / 32], float mul, int g,
+                                           const __attribute__((address_space(3))) double *rrev,
+                                           int pos) {
     const auto r = row_rsrc<D>(dst_tile, rows, rs);
     const uint32_t off = lrow * (uint32_t)(rs * 2) + (uint32_t)g * 16u;
+    f32x16 x[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[dt][e] = acc[dt][e] * mul;
+    if (rrev) {
+        constexpr int kLoTiles = D == 32 ? 1 : D / 64;
+        constexpr int kHalves = D == 32 ? 1 : 2;
+#pragma unroll
+        for (int dt = 0; dt < kLoTiles; ++dt)
+#pragma unroll
+            for (int half = 0; half < kHalves; ++half)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 32 * dt + 16 * half + 8 * g + e;
+                    const int dh = D == 32 ? 0 : dt + D / 64;
+                    const int rl = 8 * half + e, rh = D == 32 ? 8 + e : rl;
+                    float sn, cs;
+                    rope_sincos<bf16>((double)pos * rrev[c], sn, cs);
+                    const float a = x[dt][rl], b = x[dh][rh];
+                    x[dt][rl] = a * cs + b * sn;
+                    x[dh][rh] = b * cs - a * sn;
+                }
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            bf16x8 x;
+            bf16x8 y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x2 p = pack_bf16(acc[dt][half * 8 + 2 * j] * mul,
-                                           acc[dt][half * 8 + 2 * j + 1] * mul);
-                x[2 * j] = p[0];
-                x[2 * j + 1] = p[1];
+                const bf16x2 p = pack_bf16(x[dt][half * 8 + 2 * j], x[dt][half * 8 + 2 * j + 1]);
+                y[2 * j] = p[0];
+                y[2 * j + 1] = p[1];
             }
-            buf_store16(__builtin_bit_cast(uint4, x), r, off + (uint32_t)(dt * 64 + half * 32));
+            buf_store16(__builtin_bit_cast(uint4, y), r, off + (uint32_t)(dt * 64 + half * 32));
         }
 }
 
@@ -556,6 +588,8 @@ struct BwdArgs {
     OpsLds<D> *ol;    // the tile's own rows
     int *ring;        // the next tile's index, by tile parity
     int *entry;       // the next tile's table entry (dwords 0..3)
+    // rotary table (turns per position of each pair) or null
+    const __attribute__((address_space(3))) double *rrev;
     uint32_t voff[TileGeom<D>::kDmaPerWave];
 };
 
@@ -763,11 +797,12 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
     const int64_t obase = ((int64_t)t.tok0 + t.row0) * rs + (int64_t)t.h * D;
     const int rows = t.row_end - t.row0;
     const uint32_t lrow = (uint32_t)(wave_rows(t, A.wave) - t.row0 + (A.lane & 31));
+    const int pos = t.row0 + (int)lrow;  // local index of the lane's row
     if (ROLE == 0) {
-        store_rows<D>(A.dq + obase, rows, rs, lrow, acc[0], A.s.scale, g);
+        store_rows<D>(A.dq + obase, rows, rs, lrow, acc[0], A.s.scale, g, A.rrev, pos);
     } else {
-        store_rows<D>(A.dk + obase, rows, rs, lrow, acc[0], A.s.scale, g);
-        store_rows<D>(A.dv + obase, rows, rs, lrow, acc[NA - 1], 1.f, g);
+        store_rows<D>(A.dk + obase, rows, rs, lrow, acc[0], A.s.scale, g, A.rrev, pos);
+        store_rows<D>(A.dv + obase, rows, rs, lrow, acc[NA - 1], 1.f, g, nullptr, pos);
     }
     sc.prev_role = ROLE;
     ++sc.kt;
@@ -784,6 +819,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     __shared__ __align__(1024) OpsLds<D> ol;
     __shared__ int ring[2];  // the next tile's index, by tile parity
     __shared__ int entry[64];  // 64 lanes x 4 bytes; dwords 0..3 hold the entry
+    __shared__ double rrev[D / 2];  // rotary turns per position of each pair
     const int tid = threadIdx.x;
     BwdArgs<D> A;
     A.s = s;
@@ -807,6 +843,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     A.ol = &ol;
     A.ring = ring;
     A.entry = entry;
+    A.rrev = nullptr;
+    if (s.rope_base > 0.f) {
+        if (tid < D / 2) rrev[tid] = exp2(-2.0 * tid / D * log2((double)s.rope_base)) * kInv2Pi;
+        A.rrev = (const __attribute__((address_space(3))) double *)rrev;
+    }
     dma_offsets<D>(A.voff, A.wave, A.lane, (uint32_t)((int64_t)s.H * D * 2));
     const ReadOffsets<D> ro(A.lane);
 

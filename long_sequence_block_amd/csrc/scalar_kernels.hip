@@ -27,6 +27,23 @@ __device__ __forceinline__ void zero_row(float *r) {
     for (int d = 0; d < D; ++d) r[d] = 0.f;
 }
 
+// Turns a gradient row back by the rotary angles of position pos (the
+// backward of the rotary embedding applied to q or k; the angles are those
+// of rope_sincos).  Nothing to do when s.rope_base is 0.
+template <typename TI, int D>
+__device__ __forceinline__ void rope_back(const Shape &s, int pos, float *r) {
+    if (!(s.rope_base > 0.f)) return;
+    const double lb = log2((double)s.rope_base);
+#pragma unroll
+    for (int d = 0; d < D / 2; ++d) {
+        float sn, cs;
+        rope_sincos<TI>((double)pos * exp2(-2.0 * d / D * lb) * kInv2Pi, sn, cs);
+        const float a = r[d], b = r[d + D / 2];
+        r[d] = a * cs + b * sn;
+        r[d + D / 2] = b * cs - a * sn;
+    }
+}
+
 // Forward.  Tile = rows [row0, row0+64) of one query block.
 template <typename TI, int D>
 __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restrict__ q,
@@ -150,7 +167,10 @@ __device__ void bwd_dq_tile(const Shape &s, const Tile &t, int row0, const TI *_
     if (!valid) return;
     TI *o = dq + (t.tok0 + i) * rs + (int64_t)t.h * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = from_f32<TI>(acc[d] * s.scale);
+    for (int d = 0; d < D; ++d) acc[d] *= s.scale;
+    rope_back<TI, D>(s, i, acc);
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] = from_f32<TI>(acc[d]);
 }
 
 // Backward, key role: dK_j = scale * sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i
@@ -221,8 +241,11 @@ __device__ void bwd_dkdv_tile(const Shape &s, const Tile &t, int row0,
     if (!valid) return;
     const int64_t g = (t.tok0 + j) * rs + (int64_t)t.h * D;
 #pragma unroll
+    for (int d = 0; d < D; ++d) ak[d] *= s.scale;
+    rope_back<TI, D>(s, j, ak);
+#pragma unroll
     for (int d = 0; d < D; ++d) {
-        dk[g + d] = from_f32<TI>(ak[d] * s.scale);
+        dk[g + d] = from_f32<TI>(ak[d]);
         dv[g + d] = from_f32<TI>(av[d]);
     }
 }

@@ -52,6 +52,7 @@ class Workload:
     backward: bool
     fixed_length: int = 0    # >0: every user has this length
     dout_wid: int = 0        # seed id of the dO stream (backward only)
+    rope_base: float = 0.0   # >0: rotary embedding of q and k with this base
 
     @property
     def scale(self) -> float:
@@ -107,6 +108,11 @@ WORKLOADS = {
     6: Workload(3, "sliding-window-bf16-train", users=256, heads=8, head_dim=64,
                 block_size=1, window_blocks=194, dtype="bf16", backward=True,
                 dout_wid=5),
+    # The training step with the rotary embedding the production kernel
+    # carries: rotate q and k, attend, and take the gradients through both.
+    7: Workload(3, "jagged-bf16-train-rope", users=256, heads=8, head_dim=64,
+                block_size=128, window_blocks=2, dtype="bf16", backward=True,
+                dout_wid=5, rope_base=10000.0),
 }
 
 # Length sweep of the long-context workload (time should grow linearly).

@@ -196,11 +196,11 @@ def rope_transpose(x, offsets, base: float = 10000.0) -> np.ndarray:
     return _rotate(x, offsets, base, -1.0)
 
 
-def rope_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int,
+def rope_bwd(q_rot, k_rot, v, dout, offsets, block_size: int, window_blocks: int,
              scale: float, base: float = 10000.0):
     """Gradients with respect to the unrotated q and k (and v) of
-    sum(dout * attention(rope(q), rope(k), v)): the chain rule through the
-    rotation, which is its transpose."""
-    dqr, dkr, dv = bwd(rope(q, offsets, base), rope(k, offsets, base), v, dout, offsets,
-                       block_size, window_blocks, scale)
+    sum(dout * attention(q_rot, k_rot, v)) where q_rot and k_rot are the
+    rotated q and k: the attention backward on the rotated inputs, then the
+    chain rule through the rotation, which is its transpose."""
+    dqr, dkr, dv = bwd(q_rot, k_rot, v, dout, offsets, block_size, window_blocks, scale)
     return rope_transpose(dqr, offsets, base), rope_transpose(dkr, offsets, base), dv

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 3
+    assert lsb.blockattn_abi_version() == 4
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -112,6 +112,27 @@ def test_sliding_window_argument_checks():
     assert lsb.blockattn_swa_bwd(*b.values()) == binding.ERR_INVALID_ARGUMENT
     b.update(window_tokens=8, workspace=None)
     assert lsb.blockattn_swa_bwd(*b.values()) == binding.ERR_WORKSPACE
+
+
+def test_rope_argument_checks():
+    a = dict(q=FAKE, k=FAKE, offsets=FAKE, batch=2, total_tokens=100, num_heads=2,
+             head_dim=64, theta_base=0.0, dtype=lsb.BF16, q_rot=FAKE, k_rot=FAKE, stream=None)
+    assert lsb.blockattn_rope(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(theta_base=float("inf"))
+    assert lsb.blockattn_rope(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(theta_base=10000.0, head_dim=80)
+    assert lsb.blockattn_rope(*a.values()) == binding.ERR_UNSUPPORTED
+    a.update(head_dim=64, k_rot=FAKE + 2)
+    assert lsb.blockattn_rope(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(k_rot=FAKE, total_tokens=0)
+    assert lsb.blockattn_rope(*a.values()) == binding.OK
+    b = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, offsets=FAKE,
+             batch=2, total_tokens=100, num_heads=2, head_dim=64, block_size=64,
+             window_blocks=2, scale=0.125, theta_base=-1.0, dtype=lsb.BF16, dq=FAKE,
+             dk=FAKE, dv=FAKE, workspace=FAKE, workspace_bytes=1 << 20, stream=None)
+    assert lsb.blockattn_rope_bwd(*b.values()) == binding.ERR_INVALID_ARGUMENT
+    b.update(theta_base=10000.0, workspace=None)
+    assert lsb.blockattn_rope_bwd(*b.values()) == binding.ERR_WORKSPACE
 
 
 def test_workspace_size():

@@ -512,7 +512,9 @@ def test_rope_backward_matches_central_finite_differences():
                           v, c["offsets"], B, W, sc)
         return float(np.sum(o * c["dout"]))
 
-    grads = oracle.rope_bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], B, W, sc, base)
+    grads = oracle.rope_bwd(oracle.rope(c["q"], c["offsets"], base),
+                            oracle.rope(c["k"], c["offsets"], base), c["v"], c["dout"],
+                            c["offsets"], B, W, sc, base)
     for name, grad in zip("qkv", grads):
         num = np.zeros_like(grad)
         it = np.nditer(grad, flags=["multi_index"])
