@@ -54,6 +54,12 @@ def _load():
     lib.oracle_probs.argtypes = [dp, dp, ip, i32, i64, i32, i32, i32, i32,
                                  f64, i32, i32, dp]
     lib.oracle_probs.restype = ctypes.c_int
+    lib.oracle_gdpa_fwd.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32,
+                                    f64, i32, dp]
+    lib.oracle_gdpa_fwd.restype = ctypes.c_int
+    lib.oracle_gdpa_bwd.argtypes = [dp, dp, dp, dp, ip, i32, i64, i32, i32, i32,
+                                    i32, f64, i32, dp, dp, dp]
+    lib.oracle_gdpa_bwd.restype = ctypes.c_int
     lib.oracle_pair_count.argtypes = [ip, i32, i32, i32]
     lib.oracle_pair_count.restype = ctypes.c_int64
     lib.oracle_num_threads.argtypes = []
@@ -144,6 +150,44 @@ def probs(q, k, offsets, block_size: int, window_blocks: int, scale: float,
     if rc != 0:
         raise ValueError(f"oracle_probs failed with status {rc}")
     return P
+
+
+# ------------------------------------ generalized dot-product attention
+#
+# The activation variant of the block pattern ("GEM (Meta)", section "Custom
+# kernels": GDPA replaces the softmax by an activation such as GELU or SiLU).
+# Definition and readings in blockattn_oracle.c.
+
+GDPA_SILU, GDPA_GELU = 1, 2
+
+
+def gdpa_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
+             act: int) -> np.ndarray:
+    """out [T, H, D] fp64 of sum_j act(scale <q_i, k_j>) v_j over the block
+    window (act 1 = SiLU, 2 = GELU)."""
+    q, k, v, off = _f64(q), _f64(k), _f64(v), _i32(offsets)
+    T, H, D = q.shape
+    out = np.zeros((T, H, D), np.float64)
+    rc = _load().oracle_gdpa_fwd(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
+                                 int(block_size), int(window_blocks), float(scale), int(act),
+                                 _dp(out))
+    if rc != 0:
+        raise ValueError(f"oracle_gdpa_fwd failed with status {rc}")
+    return out
+
+
+def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale: float,
+             act: int):
+    """(dq, dk, dv) of sum(dout * gdpa_fwd(...)), each [T, H, D] fp64."""
+    q, k, v, do, off = _f64(q), _f64(k), _f64(v), _f64(dout), _i32(offsets)
+    T, H, D = q.shape
+    dq, dk, dv = (np.zeros((T, H, D), np.float64) for _ in range(3))
+    rc = _load().oracle_gdpa_bwd(_dp(q), _dp(k), _dp(v), _dp(do), _ip(off), len(off) - 1, T,
+                                 H, D, int(block_size), int(window_blocks), float(scale),
+                                 int(act), _dp(dq), _dp(dk), _dp(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_gdpa_bwd failed with status {rc}")
+    return dq, dk, dv
 
 
 # ------------------------------------------------- rotary position embedding

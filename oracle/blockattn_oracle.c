@@ -268,3 +268,104 @@ int oracle_probs(const double *q, const double *k, const int32_t *offsets,
     }
     return 0;
 }
+
+/*
+ * Generalized dot-product attention on the block pattern.  "GEM (Meta)",
+ * section "Custom kernels", describes GDPA as dot-product attention whose
+ * softmax is replaced by an activation such as GELU or SiLU.  The pages give
+ * no normalisation; the reading taken is none: for each visible pair
+ *     x_ij = scale * <q_i, k_j>,   P_ij = act(x_ij),   O_i = sum_j P_ij v_j,
+ * with act = SiLU (act == 1: x / (1 + exp(-x))) or GELU (act == 2, the erf
+ * form: x * Phi(x), Phi the standard normal CDF).  Backward of sum(dO * O):
+ *     dP_ij = <dO_i, v_j>,  dS_ij = act'(x_ij) dP_ij,
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+ *     dV_j = sum_i P_ij dO_i.
+ * Same layouts, visibility rule, threading and return codes as above;
+ * act outside {1, 2} is an invalid argument.
+ */
+static double act_value(int act, double x)
+{
+    if (act == 1)
+        return x / (1.0 + exp(-x));
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+static double act_slope(int act, double x)
+{
+    if (act == 1) {
+        const double sg = 1.0 / (1.0 + exp(-x));
+        return sg * (1.0 + x * (1.0 - sg));
+    }
+    const double cdf = 0.5 * (1.0 + erf(x / sqrt(2.0)));
+    const double pdf = exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846);
+    return cdf + x * pdf;
+}
+
+int oracle_gdpa_fwd(const double *q, const double *k, const double *v,
+                    const int32_t *offsets, int batch, int64_t T, int H, int D,
+                    int B, int W, double scale, int act, double *out)
+{
+    if (check_args(offsets, batch, T, H, D, B, W) || (act != 1 && act != 2))
+        return -1;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; ++p) {
+        const int u = (int)(p / H), h = (int)(p % H);
+        const int64_t t0 = offsets[u];
+        const int64_t L = (int64_t)offsets[u + 1] - t0;
+        for (int64_t i = 0; i < L; ++i) {
+            const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+            double *oi = out + (t0 + i) * rs + (int64_t)h * D;
+            for (int d = 0; d < D; ++d)
+                oi[d] = 0.0;
+            for (int64_t j = first_visible(i, B, W); j <= i; ++j) {
+                const double *kj = k + (t0 + j) * rs + (int64_t)h * D;
+                const double *vj = v + (t0 + j) * rs + (int64_t)h * D;
+                const double pij = act_value(act, scale * dot(qi, kj, D));
+                for (int d = 0; d < D; ++d)
+                    oi[d] += pij * vj[d];
+            }
+        }
+    }
+    return 0;
+}
+
+int oracle_gdpa_bwd(const double *q, const double *k, const double *v,
+                    const double *dout, const int32_t *offsets, int batch,
+                    int64_t T, int H, int D, int B, int W, double scale, int act,
+                    double *dq, double *dk, double *dv)
+{
+    if (check_args(offsets, batch, T, H, D, B, W) || (act != 1 && act != 2))
+        return -1;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; ++p) {
+        const int u = (int)(p / H), h = (int)(p % H);
+        const int64_t t0 = offsets[u];
+        const int64_t L = (int64_t)offsets[u + 1] - t0;
+        for (int64_t i = 0; i < L; ++i)
+            for (int d = 0; d < D; ++d) {
+                const int64_t o = (t0 + i) * rs + (int64_t)h * D + d;
+                dq[o] = dk[o] = dv[o] = 0.0;
+            }
+        for (int64_t i = 0; i < L; ++i) {
+            const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+            const double *doi = dout + (t0 + i) * rs + (int64_t)h * D;
+            double *dqi = dq + (t0 + i) * rs + (int64_t)h * D;
+            for (int64_t j = first_visible(i, B, W); j <= i; ++j) {
+                const int64_t oj = (t0 + j) * rs + (int64_t)h * D;
+                const double x = scale * dot(qi, k + oj, D);
+                const double pij = act_value(act, x);
+                const double ds = act_slope(act, x) * dot(doi, v + oj, D);
+                for (int d = 0; d < D; ++d) {
+                    dqi[d] += scale * ds * k[oj + d];
+                    dk[oj + d] += scale * ds * qi[d];
+                    dv[oj + d] += pij * doi[d];
+                }
+            }
+        }
+    }
+    return 0;
+}

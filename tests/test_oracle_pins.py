@@ -528,3 +528,64 @@ def test_rope_backward_matches_central_finite_differences():
             num[idx] = (fp - fm) / (2 * eps)
         err = np.abs(num - grad).max() / max(np.abs(grad).max(), 1e-30)
         assert err <= 1e-6, (name, err)
+
+
+# ------------------------------------------ generalized dot-product attention
+#
+# GDPA replaces the softmax by an activation ("GEM (Meta)", section "Custom
+# kernels"); the reading is no normalisation (the oracle's header).
+
+
+def _gdpa_torch(q, k, v, L, B, W, scale, act):
+    """Dense fp64 reference of one user with torch's own SiLU / GELU (exact
+    erf form) and the predicate mask; returns out [L, H, D] as a tensor."""
+    mask = torch.from_numpy(visible_mask(L, B, W))
+    s = torch.einsum("ihd,jhd->hij", q, k) * scale
+    a = torch.nn.functional.silu(s) if act == oracle.GDPA_SILU else \
+        torch.nn.functional.gelu(s, approximate="none")
+    p = torch.where(mask[None], a, torch.zeros_like(a))
+    return torch.einsum("hij,jhd->ihd", p, v)
+
+
+@pytest.mark.parametrize("act", [1, 2])
+@pytest.mark.parametrize("B,W", [(4, 2), (1, 5), (8, 1)])
+def test_gdpa_matches_torch_activations_and_autograd(act, B, W):
+    lengths = [0, 1, 9, 23, 40]
+    c = case(500 + 10 * act + B + W, lengths, H=2, D=6)
+    sc = 0.55
+    out = oracle.gdpa_fwd(c["q"], c["k"], c["v"], c["offsets"], B, W, sc, act)
+    dq, dk, dv = oracle.gdpa_bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], B, W, sc, act)
+    off = c["offsets"]
+    for u, L in enumerate(lengths):
+        a, b = off[u], off[u + 1]
+        if L == 0:
+            continue
+        t = {n: torch.from_numpy(c[n][a:b].copy()).requires_grad_(n in "qkv") for n in
+             ("q", "k", "v", "dout")}
+        ref = _gdpa_torch(t["q"], t["k"], t["v"], L, B, W, sc, act)
+        np.testing.assert_allclose(out[a:b], ref.detach().numpy(), atol=1e-12, rtol=0)
+        (ref * t["dout"]).sum().backward()
+        np.testing.assert_allclose(dq[a:b], t["q"].grad.numpy(), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dk[a:b], t["k"].grad.numpy(), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dv[a:b], t["v"].grad.numpy(), atol=1e-12, rtol=0)
+
+
+def test_gdpa_constant_scores_weight_the_window_sum():
+    """All keys of a user equal and all queries equal: every visible score is
+    the same x, so out_i = act(x) times the sum of the visible v_j (prefix
+    sums), with act written from its definition via math.exp / math.erf."""
+    L, B, W, D = 37, 8, 2, 4
+    rs = np.random.default_rng(9)
+    qv, kv = rs.standard_normal(D), rs.standard_normal(D)
+    v = rs.standard_normal((L, 1, D))
+    q, k = np.tile(qv, (L, 1, 1)), np.tile(kv, (L, 1, 1))
+    off = np.array([0, L], np.int32)
+    x = 0.7 * float(qv @ kv)
+    silu = x / (1 + math.exp(-x))
+    gelu = 0.5 * x * (1 + math.erf(x / math.sqrt(2)))
+    csum = np.concatenate([np.zeros((1, D)), np.cumsum(v[:, 0], axis=0)])
+    for act, a in ((1, silu), (2, gelu)):
+        out = oracle.gdpa_fwd(q, k, v, off, B, W, 0.7, act)
+        for i in range(L):
+            j0 = max(0, i // B - W + 1) * B
+            np.testing.assert_allclose(out[i, 0], a * (csum[i + 1] - csum[j0]), atol=1e-12)
