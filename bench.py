@@ -89,15 +89,20 @@ def cpu_baseline(w, users: int, flops_per_pair_head: float):
             host[key] = t.to(torch.float64).numpy()
     off = host["offsets"]
     t0 = time.perf_counter()
-    q, k = host["q"], host["k"]
-    if w.rope_base:
-        q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
-    oracle.fwd(q, k, host["v"], off, w.block_size, w.window_blocks, w.scale)
-    if w.backward and w.rope_base:
-        oracle.rope_bwd(q, k, host["v"], host["dout"], off, w.block_size, w.window_blocks,
-                        w.scale, w.rope_base)
-    elif w.backward:
-        oracle.bwd(q, k, host["v"], host["dout"], off, w.block_size, w.window_blocks, w.scale)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, W, sc = w.block_size, w.window_blocks, w.scale
+    if w.act:  # activation scores
+        oracle.gdpa_fwd(q, k, v, off, B, W, sc, w.act)
+        if w.backward:
+            oracle.gdpa_bwd(q, k, v, host["dout"], off, B, W, sc, w.act)
+    else:
+        if w.rope_base:
+            q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
+        oracle.fwd(q, k, v, off, B, W, sc)
+        if w.backward and w.rope_base:
+            oracle.rope_bwd(q, k, v, host["dout"], off, B, W, sc, w.rope_base)
+        elif w.backward:
+            oracle.bwd(q, k, v, host["dout"], off, B, W, sc)
     dt = time.perf_counter() - t0
     flops = flops_per_pair_head * pairs_per_head(off, w.block_size, w.window_blocks) * w.heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -138,7 +143,8 @@ def main():
                     help="1 tiny fp32, 2 fixed bf16, 3 jagged bf16, 4 long context, "
                          "5 jagged bf16 training step (default), 6 the same step with a "
                          "194-token sliding window (same visible-pair count), 7 the training "
-                         "step with the rotary embedding (rope, fwd, fused rope backward)")
+                         "step with the rotary embedding (rope, fwd, fused rope backward), 8 the "
+                         "training step with SiLU scores (generalized dot-product attention)")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,10 +199,16 @@ def main():
             ev[0].record()
         if rb:  # rotary embedding of q and k into qa, ka
             lsb.rope(d["q"], d["k"], d["offsets"], rb, q_rot=qa, k_rot=ka)
-        lsb.fwd(qa, ka, d["v"], d["offsets"], B, W, sc, out=out, lse=lse)
+        if w.act:  # activation scores (GDPA): no lse
+            lsb.gdpa_fwd(qa, ka, d["v"], d["offsets"], B, W, sc, w.act, out=out)
+        else:
+            lsb.fwd(qa, ka, d["v"], d["offsets"], B, W, sc, out=out, lse=lse)
         if ev is not None:
             ev[1].record()
-        if w.backward and rb:  # gradients through attention and the rotation
+        if w.backward and w.act:
+            lsb.gdpa_bwd(qa, ka, d["v"], d["dout"], d["offsets"], B, W, sc, w.act, grads=grads,
+                         workspace=ws)
+        elif w.backward and rb:  # gradients through attention and the rotation
             lsb.rope_bwd(qa, ka, d["v"], out, d["dout"], lse, d["offsets"], B, W, sc, rb,
                          grads=grads, workspace=ws)
         elif w.backward:
@@ -224,8 +236,9 @@ def main():
     e = 2 if w.dtype == "bf16" else 4
     fwd_flops = 4.0 * D * npair * H
     bwd_flops = 8.0 * D * npair * H if w.backward else 0.0
-    fwd_bytes = T * H * (4.0 * D * e + 4) + (4.0 * T * H * D * e if rb else 0.0)
-    bwd_bytes = T * H * (8.0 * D * e + 4) if w.backward else 0.0
+    fwd_bytes = T * H * (4.0 * D * e + (0 if w.act else 4)) + (4.0 * T * H * D * e if rb else 0.0)
+    # GDPA's backward reads q, k, v, dO and writes dq, dk, dv (no out, no lse)
+    bwd_bytes = (T * H * ((7.0 * D * e) if w.act else (8.0 * D * e + 4))) if w.backward else 0.0
     flops = fwd_flops + bwd_flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -259,6 +272,7 @@ def main():
                    "head_dim": D, "block_size": B, "window_blocks": W,
                    "backward": w.backward, "pairs_per_head": npair,
                    **({"rope_base": rb} if rb else {}),
+                   **({"activation": {1: "silu", 2: "gelu"}[w.act]} if w.act else {}),
                    "parallelism": "single GPU"},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * tflops / peak, 3),

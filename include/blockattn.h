@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 4
+#define BLOCKATTN_ABI_VERSION 5
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -186,6 +186,41 @@ blockattn_status blockattn_rope_bwd(const void *q_rot, const void *k_rot,
                                     void *dq, void *dk, void *dv,
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/*
+ * Generalized dot-product attention (GDPA) on the same block pattern: the
+ * softmax replaced by an activation ("GEM (Meta)", section "Custom kernels":
+ * GDPA replaces the softmax with activations such as GELU or SiLU).  The
+ * pages give no normalisation; the reading is none:
+ *     x_ij = scale * <q_i, k_j>,  P_ij = act(x_ij),  out_i = sum_j P_ij v_j
+ * over the visible keys j of query i, with act SiLU (x / (1 + e^-x)) or GELU
+ * (the erf form, x * Phi(x)).  No lse.  blockattn_gdpa_bwd returns dq, dk,
+ * dv of sum(dout * out) (dS_ij = act'(x_ij) <dout_i, v_j>); it needs neither
+ * out nor lse, and takes the workspace of blockattn_bwd.  activation not in
+ * blockattn_gdpa_act is BLOCKATTN_ERR_INVALID_ARGUMENT; everything else as
+ * for blockattn_fwd / blockattn_bwd.
+ */
+typedef enum {
+    BLOCKATTN_GDPA_SILU = 1,
+    BLOCKATTN_GDPA_GELU = 2
+} blockattn_gdpa_act;
+
+blockattn_status blockattn_gdpa_fwd(const void *q, const void *k, const void *v,
+                                    const int32_t *offsets, int32_t batch,
+                                    int64_t total_tokens, int32_t num_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t window_blocks, float scale,
+                                    int32_t activation, blockattn_dtype dtype,
+                                    void *out, hipStream_t stream);
+blockattn_status blockattn_gdpa_bwd(const void *q, const void *k, const void *v,
+                                    const void *dout, const int32_t *offsets,
+                                    int32_t batch, int64_t total_tokens,
+                                    int32_t num_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t window_blocks,
+                                    float scale, int32_t activation,
+                                    blockattn_dtype dtype, void *dq, void *dk,
+                                    void *dv, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *blockattn_status_string(blockattn_status status);

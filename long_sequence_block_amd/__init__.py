@@ -4,8 +4,9 @@ The computation runs in the HIP library built from ``csrc/`` and exposed
 through the C ABI of ``include/blockattn.h``; ``binding`` is its ctypes
 binding.  ``workloads`` draws the seeded synthetic inputs.
 """
-from .binding import (BF16, FP32, BlockAttnError, blockattn_abi_version,  # noqa: F401
+from .binding import (BF16, FP32, GDPA_GELU, GDPA_SILU, BlockAttnError,  # noqa: F401
+                      blockattn_abi_version, blockattn_gdpa_bwd, blockattn_gdpa_fwd,
                       blockattn_bwd, blockattn_bwd_workspace_size, blockattn_fwd,
                       blockattn_rope, blockattn_rope_bwd, blockattn_status_string,
                       blockattn_swa_bwd, blockattn_swa_fwd, bwd, fwd, library_path, load,
-                      rope, rope_bwd, swa_bwd, swa_fwd)
+                      gdpa_bwd, gdpa_fwd, rope, rope_bwd, swa_bwd, swa_fwd)

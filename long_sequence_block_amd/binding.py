@@ -17,10 +17,12 @@ from .build import LIB, build_library
 
 BF16, FP32 = 0, 1
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+GDPA_SILU, GDPA_GELU = 1, 2  # blockattn_gdpa_act
 
 # Every symbol include/blockattn.h declares.
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
            "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_rope", "blockattn_rope_bwd",
+           "blockattn_gdpa_fwd", "blockattn_gdpa_bwd",
            "blockattn_status_string", "blockattn_abi_version")
 
 _lib = None
@@ -67,6 +69,12 @@ def load() -> ctypes.CDLL:
                                        i32, f32, f32, ctypes.c_int, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
     lib.blockattn_rope_bwd.restype = ctypes.c_int
+    lib.blockattn_gdpa_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32, i32,
+                                       ctypes.c_int, vp, vp]
+    lib.blockattn_gdpa_fwd.restype = ctypes.c_int
+    lib.blockattn_gdpa_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32,
+                                       i32, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.blockattn_gdpa_bwd.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_abi_version.argtypes = []
@@ -120,6 +128,21 @@ def blockattn_rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, batch, total_to
                                      total_tokens, num_heads, head_dim, block_size,
                                      window_blocks, scale, theta_base, dtype, dq, dk, dv,
                                      workspace, workspace_bytes, stream)
+
+
+def blockattn_gdpa_fwd(q, k, v, offsets, batch, total_tokens, num_heads, head_dim,
+                       block_size, window_blocks, scale, activation, dtype, out, stream) -> int:
+    return load().blockattn_gdpa_fwd(q, k, v, offsets, batch, total_tokens, num_heads,
+                                     head_dim, block_size, window_blocks, scale, activation,
+                                     dtype, out, stream)
+
+
+def blockattn_gdpa_bwd(q, k, v, dout, offsets, batch, total_tokens, num_heads, head_dim,
+                       block_size, window_blocks, scale, activation, dtype, dq, dk, dv,
+                       workspace, workspace_bytes, stream) -> int:
+    return load().blockattn_gdpa_bwd(q, k, v, dout, offsets, batch, total_tokens, num_heads,
+                                     head_dim, block_size, window_blocks, scale, activation,
+                                     dtype, dq, dk, dv, workspace, workspace_bytes, stream)
 
 
 def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
@@ -301,4 +324,46 @@ def rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, block_size: int, window_b
                             dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream(stream))
     if rc != OK:
         raise BlockAttnError("blockattn_rope_bwd", rc)
+    return dq, dk, dv
+
+
+def gdpa_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
+             activation: int, out=None, stream=None):
+    """Generalized dot-product attention forward (blockattn_gdpa_fwd): the
+    block pattern with P = act(scale q.k), no normalisation.  Returns out."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    out = torch.empty_like(q) if out is None else out
+    rc = blockattn_gdpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                            offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                            float(scale), int(activation), _dtype_code(q), out.data_ptr(),
+                            _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_gdpa_fwd", rc)
+    return out
+
+
+def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale: float,
+             activation: int, grads=None, workspace=None, stream=None):
+    """Generalized dot-product attention backward (blockattn_gdpa_bwd).
+    Returns (dq, dk, dv)."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q")
+    code = _dtype_code(q)
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = grads
+    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    rc = blockattn_gdpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                            offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
+                            window_blocks, float(scale), int(activation), code, dq.data_ptr(),
+                            dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_gdpa_bwd", rc)
     return dq, dk, dv

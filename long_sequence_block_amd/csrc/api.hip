@@ -8,6 +8,9 @@
 #include "common.h"
 #include "kernels.h"
 
+static_assert(BLOCKATTN_GDPA_SILU == ba::kSilu && BLOCKATTN_GDPA_GELU == ba::kGelu,
+              "activation codes of the ABI and the kernels agree");
+
 namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -51,7 +54,33 @@ ba::Shape make_shape(const int32_t *offsets, int32_t batch, int64_t T, int32_t H
     s.W = W;
     s.scale = scale;
     s.rope_base = 0.f;
+    s.act = ba::kSoftmax;
     return s;
+}
+
+// The forward entry points: block attention (act kSoftmax, writes lse) or
+// its activation variants (no lse).
+blockattn_status forward(const void *q, const void *k, const void *v, const int32_t *offsets,
+                         int32_t batch, int64_t total_tokens, int32_t num_heads,
+                         int32_t head_dim, int32_t block_size, int32_t window_blocks,
+                         float scale, int act, blockattn_dtype dtype, void *out, float *lse,
+                         hipStream_t stream) {
+    bool empty;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
+                                       block_size, window_blocks, scale, dtype, &empty);
+    if (st != BLOCKATTN_OK || empty) return st;
+    const bool stats = act == ba::kSoftmax;
+    if (!q || !k || !v || !out || (stats && !lse)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (stats && !aligned16(lse)))
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, block_size,
+                             window_blocks, scale);
+    s.act = act;
+    hipError_t e = dtype == BLOCKATTN_BF16
+                       ? ba::launch_mfma_fwd(s, q, k, v, out, lse, stream)
+                       : ba::launch_scalar_fwd(s, false, q, k, v, out, lse, stream);
+    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 
 // The backward entry points: plain (rope_base 0) or through a rotary
@@ -60,18 +89,19 @@ blockattn_status backward(const void *q, const void *k, const void *v, const voi
                           const void *dout, const float *lse, const int32_t *offsets,
                           int32_t batch, int64_t total_tokens, int32_t num_heads,
                           int32_t head_dim, int32_t block_size, int32_t window_blocks,
-                          float scale, float rope_base, blockattn_dtype dtype, void *dq,
-                          void *dk, void *dv, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          float scale, float rope_base, int act, blockattn_dtype dtype,
+                          void *dq, void *dk, void *dv, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
     bool empty;
     blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
                                        block_size, window_blocks, scale, dtype, &empty);
     if (st != BLOCKATTN_OK || empty) return st;
-    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    const bool stats = act == ba::kSoftmax;  // out and lse enter only the softmax
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || (stats && (!out || !lse)))
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
-        !aligned16(dv))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (stats && (!aligned16(out) || !aligned16(lse))))
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     const size_t need = blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
@@ -79,6 +109,7 @@ blockattn_status backward(const void *q, const void *k, const void *v, const voi
     ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, block_size,
                              window_blocks, scale);
     s.rope_base = rope_base;
+    s.act = act;
     hipError_t e = dtype == BLOCKATTN_BF16
                        ? ba::launch_mfma_bwd(s, q, k, v, out, dout, lse, dq, dk, dv, workspace,
                                              stream)
@@ -119,19 +150,8 @@ blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
                                int32_t num_heads, int32_t head_dim, int32_t block_size,
                                int32_t window_blocks, float scale, blockattn_dtype dtype,
                                void *out, float *lse, hipStream_t stream) {
-    bool empty;
-    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
-                                       block_size, window_blocks, scale, dtype, &empty);
-    if (st != BLOCKATTN_OK || empty) return st;
-    if (!q || !k || !v || !out || !lse) return BLOCKATTN_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
-        return BLOCKATTN_ERR_INVALID_ARGUMENT;
-    const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim,
-                                   block_size, window_blocks, scale);
-    hipError_t e = dtype == BLOCKATTN_BF16
-                       ? ba::launch_mfma_fwd(s, q, k, v, out, lse, stream)
-                       : ba::launch_scalar_fwd(s, false, q, k, v, out, lse, stream);
-    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+    return forward(q, k, v, offsets, batch, total_tokens, num_heads, head_dim, block_size,
+                   window_blocks, scale, ba::kSoftmax, dtype, out, lse, stream);
 }
 
 blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, const void *out,
@@ -142,8 +162,8 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
                                void *dv, void *workspace, size_t workspace_bytes,
                                hipStream_t stream) {
     return backward(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads, head_dim,
-                    block_size, window_blocks, scale, 0.f, dtype, dq, dk, dv, workspace,
-                    workspace_bytes, stream);
+                    block_size, window_blocks, scale, 0.f, ba::kSoftmax, dtype, dq, dk, dv,
+                    workspace, workspace_bytes, stream);
 }
 
 blockattn_status blockattn_rope(const void *q, const void *k, const int32_t *offsets,
@@ -176,8 +196,33 @@ blockattn_status blockattn_rope_bwd(const void *q_rot, const void *k_rot, const 
                                     hipStream_t stream) {
     if (!isfinite(theta_base) || !(theta_base > 0.f)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
     return backward(q_rot, k_rot, v, out, dout, lse, offsets, batch, total_tokens, num_heads,
-                    head_dim, block_size, window_blocks, scale, theta_base, dtype, dq, dk, dv,
-                    workspace, workspace_bytes, stream);
+                    head_dim, block_size, window_blocks, scale, theta_base, ba::kSoftmax, dtype,
+                    dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+blockattn_status blockattn_gdpa_fwd(const void *q, const void *k, const void *v,
+                                    const int32_t *offsets, int32_t batch, int64_t total_tokens,
+                                    int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t window_blocks, float scale, int32_t activation,
+                                    blockattn_dtype dtype, void *out, hipStream_t stream) {
+    if (activation != BLOCKATTN_GDPA_SILU && activation != BLOCKATTN_GDPA_GELU)
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    return forward(q, k, v, offsets, batch, total_tokens, num_heads, head_dim, block_size,
+                   window_blocks, scale, activation, dtype, out, nullptr, stream);
+}
+
+blockattn_status blockattn_gdpa_bwd(const void *q, const void *k, const void *v,
+                                    const void *dout, const int32_t *offsets, int32_t batch,
+                                    int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t window_blocks, float scale,
+                                    int32_t activation, blockattn_dtype dtype, void *dq,
+                                    void *dk, void *dv, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (activation != BLOCKATTN_GDPA_SILU && activation != BLOCKATTN_GDPA_GELU)
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    return backward(q, k, v, nullptr, dout, nullptr, offsets, batch, total_tokens, num_heads,
+                    head_dim, block_size, window_blocks, scale, 0.f, activation, dtype, dq, dk,
+                    dv, workspace, workspace_bytes, stream);
 }
 
 blockattn_status blockattn_swa_fwd(const void *q, const void *k, const void *v,

@@ -34,7 +34,46 @@ struct Shape {
     float scale;
     float rope_base;  // > 0: the backward returns gradients through a rotary
                       // embedding with this base (see rope_sincos); 0: none
+    int act;          // score function: kSoftmax, or a GDPA activation
 };
+
+// Score functions.  kSoftmax is block attention proper.  The others are
+// generalized dot-product attention ("GEM (Meta)" on aiwiki.ai, section
+// "Custom kernels": the softmax replaced by an activation such as GELU or
+// SiLU), read as P_ij = act(scale <q_i, k_j>) with no normalisation.
+enum { kSoftmax = 0, kSilu = 1, kGelu = 2 };
+
+// act(x) and act'(x) in fp32.  SiLU: x s(x) with the logistic s(x) =
+// 1 / (1 + 2^(-x log2 e)), slope s(x) (1 + x (1 - s(x))); it tends to 0 (and
+// slope 0) for large negative x, where 2^(...) overflows to +inf.  GELU, the
+// erf form: x Phi(x), slope Phi(x) + x phi(x), with Phi the standard normal
+// CDF and phi its density.
+template <int ACT>
+__device__ __forceinline__ void act_value_slope(float x, float &a, float &g) {
+    if constexpr (ACT == kSilu) {
+        const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+        a = x * sg;
+        g = sg * (1.f + x * (1.f - sg));
+    } else {
+        const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752f));
+        const float pdf =
+            0.39894228040143268f * __builtin_amdgcn_exp2f(-0.5f * 1.4426950408889634f * x * x);
+        a = x * cdf;
+        g = cdf + x * pdf;
+    }
+}
+template <int ACT>
+__device__ __forceinline__ float act_value(float x) {
+    float a, g;
+    act_value_slope<ACT>(x, a, g);
+    return a;
+}
+template <int ACT>
+__device__ __forceinline__ float act_slope(float x) {
+    float a, g;
+    act_value_slope<ACT>(x, a, g);
+    return g;
+}
 
 // One tile of work: sub-tile `sub` of row unit `blk` (local to the user), head
 // h, of user `user` whose tokens start at packed index tok0 and who has len

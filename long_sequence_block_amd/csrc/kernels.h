@@ -7,7 +7,8 @@
 
 namespace ba {
 
-// Scalar FMA path (fp32 storage, or bf16 storage with fp32 arithmetic).
+// Scalar FMA path (fp32 storage; bf16_io must be false).  s.act selects the
+// score function, as for the MFMA kernels.
 hipError_t launch_scalar_fwd(const Shape &s, bool bf16_io, const void *q, const void *k,
                              const void *v, void *out, float *lse, hipStream_t st);
 hipError_t launch_scalar_bwd(const Shape &s, bool bf16_io, const void *q, const void *k,

@@ -238,7 +238,7 @@ __device__ __forceinline__ QWin query_win(const Shape &s, const BwdTile &t, int 
 
 // One 64-key chunk of the query role: S^T and dP^T for each 32-key
 // sub-tile, then dQ^T += K^T dS^T.  c0 = first key of the chunk.
-template <int D>
+template <int D, int ACT>
 __device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int lane,
                                             const lds_t *kt, int c0, const Ops<D> &op,
                                             const f32x16 &ndlt, const ReadOffsets<D> &ro,
@@ -264,8 +264,8 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int l
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(ka[ks], op.a[ks], sc);
         // dP^T starts from -delta of the lane's query: the products leave
-        // dP - delta.
-        f32x16 dp = mfma32(va[0], op.b[0], ndlt);
+        // dP - delta (the activation variants have no delta).
+        f32x16 dp = mfma32(va[0], op.b[0], ACT == kSoftmax ? ndlt : f32x16{});
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) dp = mfma32(va[ks], op.b[ks], dp);
         bf16x8 ktr[2][D / 32];
@@ -276,9 +276,12 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int l
                 const lds_t *kr = ks_ + kk * 16 * G::kRowBytes;
                 ktr[kk][dt] = lds_read_tr(kr + ro.trd[0][dt], kr + ro.trd[1][dt]);
             }
+        // dS = pr * dp: pr = P for the softmax, act'(scale s) for GDPA
         float pr[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -op.lse2));
+        for (int r = 0; r < 16; ++r)
+            pr[r] = ACT == kSoftmax ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -op.lse2))
+                                    : act_slope<ACT>(sc[r] * s.scale);
         // Issue order: all operand reads, the S products, the transposed
         // reads, then each dP product followed by a share of the
         // exponentials (which need only S), so one wave keeps both its
@@ -343,7 +346,7 @@ __device__ __forceinline__ KWin key_win(const Shape &s, const BwdTile &t, int wa
 // One 64-query chunk of the key role: S and dP for each 32-query sub-tile,
 // then dV^T += dO^T P and dK^T += Q^T dS.  c0 = first query of the chunk;
 // cb holds the chunk's row statistics.
-template <int D>
+template <int D, int ACT>
 __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lane,
                                           const lds_t *qt, const BwdChunk<D> &cb, int c0,
                                           const Ops<D> &op, const ReadOffsets<D> &ro,
@@ -384,8 +387,9 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lan
         f32x16 sc = mfma32(qa[0], op.a[0], f32x16{});
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(qa[ks], op.a[ks], sc);
-        // dP starts from -delta of each query: the products leave dP - delta.
-        f32x16 dp = mfma32(da[0], op.b[0], nd);
+        // dP starts from -delta of each query: the products leave dP - delta
+        // (the activation variants have no delta).
+        f32x16 dp = mfma32(da[0], op.b[0], ACT == kSoftmax ? nd : f32x16{});
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) dp = mfma32(da[ks], op.b[ks], dp);
         bf16x8 qtr[2][D / 32], dtr[2][D / 32];
@@ -398,9 +402,16 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lan
                 dtr[kk][dt] = lds_read_tr(dr + ro.trd[0][dt], dr + ro.trd[1][dt]);
                 qtr[kk][dt] = lds_read_tr(qr + ro.trd[0][dt], qr + ro.trd[1][dt]);
             }
-        float pf[16];
+        // P, and the factor of dS = gf * dp (P itself for the softmax,
+        // act'(scale s) for GDPA)
+        float pf[16], gf[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pf[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[r]));
+        for (int r = 0; r < 16; ++r) {
+            if constexpr (ACT == kSoftmax)
+                pf[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -ls[r]));
+            else
+                act_value_slope<ACT>(sc[r] * s.scale, pf[r], gf[r]);
+        }
         // Issue order as in the query role.
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16) + 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
@@ -417,10 +428,15 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lan
         if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= w.span) pf[r] = 0.f;
+                if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) >= w.span) pf[r] = gf[r] = 0.f;
         }
-        // P in bf16 (and its largest value, compared as bits since weights
-        // are >= 0), then the dV products, which need only P; dS needs dP.
+        if constexpr (ACT == kSoftmax) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) gf[r] = pf[r];
+        }
+        // P in bf16 (and, for the softmax, its largest value, compared as
+        // bits since the weights are >= 0), then the dV products, which need
+        // only P; dS needs dP.
         uint32_t pmax = 0u;
         bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -442,7 +458,9 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lan
         // part and dV takes a second product; elsewhere each term's rounding
         // error stays below 2^-10 |dO|, well under the bf16 rounding of dV
         // itself.  About 2% of sub-tiles split on N(0,1) inputs.
-        if (__builtin_amdgcn_ballot_w64(pmax > __float_as_uint(0.25f)) != 0) {
+        // (Softmax only: activation weights are O(1) throughout, and their
+        // sums are bounded relative to their own magnitude.)
+        if (ACT == kSoftmax && __builtin_amdgcn_ballot_w64(pmax > __float_as_uint(0.25f)) != 0) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 lo;
@@ -463,7 +481,7 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lan
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = kk * 8 + 2 * j;
-                const bf16x2 s2 = pack_bf16(pf[r] * dp[r], pf[r + 1] * dp[r + 1]);
+                const bf16x2 s2 = pack_bf16(gf[r] * dp[r], gf[r + 1] * dp[r + 1]);
                 dsb[kk][2 * j] = s2[0];
                 dsb[kk][2 * j + 1] = s2[1];
             }
@@ -717,7 +735,7 @@ __device__ __forceinline__ void read_ops(const BwdArgs<D> &A, const BwdTile &t, 
 // Works through tile t (of role ROLE, whose own rows and first chunk are in
 // flight or landed) and sets up the next one: returns false when the queue
 // has run dry, else the next tile in tn with its rows and first chunk issued.
-template <int D, int ROLE>
+template <int D, int ROLE, int ACT>
 __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<D> &ro,
                                          BwdSched &sc, const BwdTile &t, BwdTile &tn) {
     constexpr int NA = ROLE == 0 ? 1 : 2;  // accumulator sets
@@ -780,9 +798,10 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
         const int c0 = t.sbeg + ci * kKC;
         if (live) {
             if (ROLE == 0)
-                query_chunk<D>(A.s, qw, A.lane, b, c0, op, ndlt, ro, acc[0]);
+                query_chunk<D, ACT>(A.s, qw, A.lane, b, c0, op, ndlt, ro, acc[0]);
             else
-                key_chunk<D>(A.s, kw, A.lane, b, A.sm[sc.buf], c0, op, ro, acc[0], acc[NA - 1]);
+                key_chunk<D, ACT>(A.s, kw, A.lane, b, A.sm[sc.buf], c0, op, ro, acc[0],
+                                  acc[NA - 1]);
         }
         sc.buf ^= 1;
     }
@@ -809,7 +828,7 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
     return has_next;
 }
 
-template <int D>
+template <int D, int ACT>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ws_lse2,
@@ -866,17 +885,17 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     BwdSched sc{0, 0, -1};
     for (;;) {
         BwdTile tn;
-        const bool more = t.role == 0 ? run_tile<D, 0>(A, ro, sc, t, tn)
-                                      : run_tile<D, 1>(A, ro, sc, t, tn);
+        const bool more = t.role == 0 ? run_tile<D, 0, ACT>(A, ro, sc, t, tn)
+                                      : run_tile<D, 1, ACT>(A, ro, sc, t, tn);
         if (!more) break;
         t = tn;
     }
 }
 
-// Workgroups of bwd_mfma<D> that fit on the current device at once.
-template <int D>
+// Workgroups of bwd_mfma<D, ACT> that fit on the current device at once.
+template <int D, int ACT>
 int resident_workgroups() {
-    static int cached[64];
+    static int cached[64];  // one per instantiation and device
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
@@ -884,7 +903,7 @@ int resident_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_mfma<D>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_mfma<D, ACT>, kThreads, 0) !=
             hipSuccess ||
         per < 1)
         per = 1;
@@ -893,24 +912,38 @@ int resident_workgroups() {
     return n;
 }
 
-template <int D>
-hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v, const void *out,
-                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                    void *ws, hipStream_t st) {
+template <int D, int ACT>
+hipError_t launch_act(const Shape &s, const void *q, const void *k, const void *v,
+                      const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                      void *dv, void *ws, hipStream_t st) {
     const BwdWorkspace w = bwd_workspace_layout(ws, s.T, s.batch, s.H);
     const int64_t max_tiles = bwd_max_tiles(s.T, s.batch, s.H);
     hipLaunchKernelGGL(bwd_tile_index, dim3(1), dim3(1024), 0, st, s, (int)max_tiles, w.ctr,
                        w.ubase);
-    const int nrs = (int)((s.T * s.H + 255) / 256);
+    // row statistics (lse and delta) only for the softmax; the activation
+    // variants need only the tile table
+    const int nrs = ACT == kSoftmax ? (int)((s.T * s.H + 255) / 256) : 0;
     hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)(nrs + s.batch)), dim3(256), 0, st, s, nrs,
                        (const bf16 *)out, (const bf16 *)dout, lse, w.lse2, w.ndlt,
                        (const int *)w.ubase, w.table);
-    const int64_t grid = std::min<int64_t>(max_tiles, (int64_t)resident_workgroups<D>());
-    hipLaunchKernelGGL((bwd_mfma<D>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
+    const int64_t grid = std::min<int64_t>(max_tiles, (int64_t)resident_workgroups<D, ACT>());
+    hipLaunchKernelGGL((bwd_mfma<D, ACT>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
                        (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)dout,
                        (const float *)w.lse2, (const float *)w.ndlt, w.ctr,
                        (const int4 *)w.table, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v, const void *out,
+                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                    void *ws, hipStream_t st) {
+    switch (s.act) {
+    case kSoftmax: return launch_act<D, kSoftmax>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    case kSilu: return launch_act<D, kSilu>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    case kGelu: return launch_act<D, kGelu>(s, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

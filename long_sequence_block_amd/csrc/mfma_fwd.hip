@@ -58,7 +58,7 @@ struct FwdChunk {
     bf16 v[kKC * D];
 };
 
-template <int D>
+template <int D, int ACT>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     bf16 *__restrict__ out, float *__restrict__ lse) {
@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     // c is kept away from 0 so that masked scores (-inf) stay -inf.
     const float c = fmaxf(fabsf(s.scale) * kLog2e, 1e-30f);
     const float grow_thr = 8.f / c;
-    const uint32_t qsign = s.scale < 0.f ? 0x80008000u : 0u;
+    // (the activation variants take the signed scale instead)
+    const uint32_t qsign = ACT == kSoftmax && s.scale < 0.f ? 0x80008000u : 0u;
 
     const int kbeg = window_start(row0, s.B, s.W);
     const int nch = (row_end - kbeg + kKC - 1) / kKC;
@@ -168,6 +169,33 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
                 for (int dt = 0; dt < D / 32; ++dt)
                     vtr[kk][dt] = lds_read_tr(vr + trd[0][dt], vr + trd[1][dt]);
             }
+            if constexpr (ACT != kSoftmax) {
+                // P = act(scale s), zero outside the window; no normalisation
+                float pv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pv[r] = act_value<ACT>(sc[r] * s.scale);
+                if (a + 31 > wr0 || a < wave_klo_max) {
+                    const int x = a + 8 * g - my_klo;
+                    const uint32_t span = (uint32_t)(my_row - my_klo);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > span) pv[r] = 0.f;
+                }
+                bf16x8 pa[2];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int r = 2 * j;
+                    const bf16x2 p2 = pack_bf16(pv[r], pv[r + 1]);
+                    pa[r >> 3][r & 7] = p2[0];
+                    pa[r >> 3][(r & 7) + 1] = p2[1];
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        acc[dt] = mfma32(vtr[kk][dt], pa[kk], acc[dt]);
+                return;
+            }
             if (a + 31 > wr0 || a < wave_klo_max) {
                 // key of register r: a + 8g + 16(r/8) + r%8; visible iff
                 // my_klo <= key <= my_row
@@ -239,7 +267,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
 
     const float lt = swap_sum(l);
     if (!wave_live || my_row >= row_end) return;
-    const float inv = 1.f / lt;
+    const float inv = ACT == kSoftmax ? 1.f / lt : 1.f;
     bf16 *o = out + base + (int64_t)my_row * rs;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -251,16 +279,28 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
             *(bf16x8 *)(o + dt * 32 + half * 16 + g * 8) = x;
         }
     }
-    if (g == 0) lse[(int64_t)t.h * s.T + t.tok0 + my_row] = (m * c + log2f(lt)) * kLn2;
+    if (ACT == kSoftmax && g == 0)
+        lse[(int64_t)t.h * s.T + t.tok0 + my_row] = (m * c + log2f(lt)) * kLn2;
+}
+
+template <int D, int ACT>
+hipError_t launch_act(const Shape &s, const void *q, const void *k, const void *v, void *out,
+                      float *lse, hipStream_t st) {
+    const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 1, s.H);
+    hipLaunchKernelGGL((fwd_mfma<D, ACT>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse);
+    return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v, void *out,
                     float *lse, hipStream_t st) {
-    const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 1, s.H);
-    hipLaunchKernelGGL((fwd_mfma<D>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse);
-    return hipGetLastError();
+    switch (s.act) {
+    case kSoftmax: return launch_act<D, kSoftmax>(s, q, k, v, out, lse, st);
+    case kSilu: return launch_act<D, kSilu>(s, q, k, v, out, lse, st);
+    case kGelu: return launch_act<D, kGelu>(s, q, k, v, out, lse, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

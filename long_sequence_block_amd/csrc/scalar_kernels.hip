@@ -44,8 +44,9 @@ __device__ __forceinline__ void rope_back(const Shape &s, int pos, float *r) {
     }
 }
 
-// Forward.  Tile = rows [row0, row0+64) of one query block.
-template <typename TI, int D>
+// Forward.  Tile = rows [row0, row0+64) of one query block.  ACT != kSoftmax:
+// P = act(scale s) with no normalisation (generalized dot-product attention).
+template <typename TI, int D, int ACT>
 __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restrict__ q,
                                                     const TI *__restrict__ k,
                                                     const TI *__restrict__ v,
@@ -87,6 +88,12 @@ __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restric
             float dot = 0.f;
 #pragma unroll
             for (int d = 0; d < D; ++d) dot = fmaf(qr[d], ks[r][d], dot);
+            if constexpr (ACT != kSoftmax) {
+                const float p = act_value<ACT>(dot * s.scale);
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[r][d], acc[d]);
+                continue;
+            }
             const float x = dot * c;
             if (x > m) {
                 const float a = exp2f(m - x);
@@ -102,16 +109,17 @@ __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restric
         }
     }
     if (!valid) return;
-    const float inv = 1.f / l;
+    const float inv = ACT == kSoftmax ? 1.f / l : 1.f;
     TI *o = out + (t.tok0 + i) * rs + (int64_t)t.h * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) o[d] = from_f32<TI>(acc[d] * inv);
-    lse[(int64_t)t.h * s.T + t.tok0 + i] = (m + log2f(l)) * kLn2;
+    if (ACT == kSoftmax) lse[(int64_t)t.h * s.T + t.tok0 + i] = (m + log2f(l)) * kLn2;
 }
 
 // Backward, query role: dQ_i = scale * sum_j P_ij (dP_ij - delta_i) k_j with
-// delta_i = <dO_i, O_i>.
-template <typename TI, int D>
+// delta_i = <dO_i, O_i>; for ACT != kSoftmax, dQ_i = scale * sum_j
+// act'(scale s_ij) dP_ij k_j (out and lse are not read).
+template <typename TI, int D, int ACT>
 __device__ void bwd_dq_tile(const Shape &s, const Tile &t, int row0, const TI *__restrict__ q,
                             const TI *__restrict__ k, const TI *__restrict__ v,
                             const TI *__restrict__ out, const TI *__restrict__ dout,
@@ -132,9 +140,11 @@ __device__ void bwd_dq_tile(const Shape &s, const Tile &t, int row0, const TI *_
         const int64_t g = (t.tok0 + i) * rs + (int64_t)t.h * D;
         load_row<TI, D>(q + g, qr);
         load_row<TI, D>(dout + g, dor);
+        if constexpr (ACT == kSoftmax) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) dlt = fmaf(dor[d], to_f32(out[g + d]), dlt);
-        lse2 = lse[(int64_t)t.h * s.T + t.tok0 + i] * kLog2e;
+            for (int d = 0; d < D; ++d) dlt = fmaf(dor[d], to_f32(out[g + d]), dlt);
+            lse2 = lse[(int64_t)t.h * s.T + t.tok0 + i] * kLog2e;
+        }
     } else {
         zero_row<D>(qr);
         zero_row<D>(dor);
@@ -158,8 +168,8 @@ __device__ void bwd_dq_tile(const Shape &s, const Tile &t, int row0, const TI *_
                 sdot = fmaf(qr[d], ks[r][d], sdot);
                 pdot = fmaf(dor[d], vs[r][d], pdot);
             }
-            const float p = exp2f(sdot * c - lse2);
-            const float ds = p * (pdot - dlt);
+            const float ds = ACT == kSoftmax ? exp2f(sdot * c - lse2) * (pdot - dlt)
+                                             : act_slope<ACT>(sdot * s.scale) * pdot;
 #pragma unroll
             for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, ks[r][d], acc[d]);
         }
@@ -176,7 +186,7 @@ __device__ void bwd_dq_tile(const Shape &s, const Tile &t, int row0, const TI *_
 // Backward, key role: dK_j = scale * sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i
 // over the queries that see key j: i in [j, min(L, (kb+W)*B)).  delta_i is
 // recomputed from O and dO for each staged query chunk.
-template <typename TI, int D>
+template <typename TI, int D, int ACT>
 __device__ void bwd_dkdv_tile(const Shape &s, const Tile &t, int row0,
                               const TI *__restrict__ q, const TI *__restrict__ k,
                               const TI *__restrict__ v, const TI *__restrict__ out,
@@ -211,7 +221,7 @@ __device__ void bwd_dkdv_tile(const Shape &s, const Tile &t, int row0,
             qs[r][d] = to_f32(q[g]);
             dos[r][d] = to_f32(dout[g]);
         }
-        if (lane < n) {
+        if (ACT == kSoftmax && lane < n) {
             const int64_t g = (t.tok0 + c0 + lane) * rs + (int64_t)t.h * D;
             float dlt = 0.f;
 #pragma unroll
@@ -229,8 +239,15 @@ __device__ void bwd_dkdv_tile(const Shape &s, const Tile &t, int row0,
                 sdot = fmaf(qs[r][d], kr[d], sdot);
                 pdot = fmaf(dos[r][d], vr[d], pdot);
             }
-            const float p = exp2f(sdot * c - ls[r]);
-            const float ds = p * (pdot - dls[r]);
+            float p, ds;
+            if constexpr (ACT == kSoftmax) {
+                p = exp2f(sdot * c - ls[r]);
+                ds = p * (pdot - dls[r]);
+            } else {
+                float gr;
+                act_value_slope<ACT>(sdot * s.scale, p, gr);
+                ds = gr * pdot;
+            }
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 ak[d] = fmaf(ds, qs[r][d], ak[d]);
@@ -252,7 +269,7 @@ __device__ void bwd_dkdv_tile(const Shape &s, const Tile &t, int row0,
 
 // Backward: one launch.  Every block has 2*tpb sub-tiles: the first tpb
 // compute dQ rows, the next tpb compute dK/dV rows of the same block.
-template <typename TI, int D>
+template <typename TI, int D, int ACT>
 __global__ __launch_bounds__(kRows) void bwd_scalar(
     Shape s, const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
     const TI *__restrict__ out, const TI *__restrict__ dout, const float *__restrict__ lse,
@@ -265,44 +282,68 @@ __global__ __launch_bounds__(kRows) void bwd_scalar(
     if (!decode_tile<kRows>(s, s.B, 2 * tpb, t, sh)) return;
     const int row0 = t.blk * s.B + (t.sub % tpb) * kRows;
     if (t.sub < tpb)
-        bwd_dq_tile<TI, D>(s, t, row0, q, k, v, out, dout, lse, dq, as, bs);
+        bwd_dq_tile<TI, D, ACT>(s, t, row0, q, k, v, out, dout, lse, dq, as, bs);
     else
-        bwd_dkdv_tile<TI, D>(s, t, row0, q, k, v, out, dout, lse, dk, dv, as, bs, ls, dls);
+        bwd_dkdv_tile<TI, D, ACT>(s, t, row0, q, k, v, out, dout, lse, dk, dv, as, bs, ls, dls);
 }
 
-template <typename TI, int D>
-hipError_t launch_scalar_fwd_t(const Shape &s, const void *q, const void *k, const void *v,
-                               void *out, float *lse, hipStream_t st) {
+template <typename TI, int D, int ACT>
+hipError_t launch_fwd_act(const Shape &s, const void *q, const void *k, const void *v, void *out,
+                          float *lse, hipStream_t st) {
     const int tpb = (s.B + kRows - 1) / kRows;
     const int64_t grid = grid_upper_bound(s.T, s.batch, s.B, tpb, s.H);
-    hipLaunchKernelGGL((fwd_scalar<TI, D>), dim3((unsigned)grid), dim3(kRows), 0, st, s,
+    hipLaunchKernelGGL((fwd_scalar<TI, D, ACT>), dim3((unsigned)grid), dim3(kRows), 0, st, s,
                        (const TI *)q, (const TI *)k, (const TI *)v, (TI *)out, lse, tpb);
     return hipGetLastError();
 }
 
-template <typename TI, int D>
-hipError_t launch_scalar_bwd_t(const Shape &s, const void *q, const void *k, const void *v,
-                               const void *out, const void *dout, const float *lse,
-                               void *dq, void *dk, void *dv, hipStream_t st) {
+template <typename TI, int D, int ACT>
+hipError_t launch_bwd_act(const Shape &s, const void *q, const void *k, const void *v,
+                          const void *out, const void *dout, const float *lse, void *dq,
+                          void *dk, void *dv, hipStream_t st) {
     const int tpb = (s.B + kRows - 1) / kRows;
     const int64_t grid = grid_upper_bound(s.T, s.batch, s.B, 2 * tpb, s.H);
-    hipLaunchKernelGGL((bwd_scalar<TI, D>), dim3((unsigned)grid), dim3(kRows), 0, st, s,
+    hipLaunchKernelGGL((bwd_scalar<TI, D, ACT>), dim3((unsigned)grid), dim3(kRows), 0, st, s,
                        (const TI *)q, (const TI *)k, (const TI *)v, (const TI *)out,
                        (const TI *)dout, lse, (TI *)dq, (TI *)dk, (TI *)dv, tpb);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_d(const Shape &s, const void *q, const void *k, const void *v, void *out,
+                        float *lse, hipStream_t st) {
+    switch (s.act) {
+    case kSoftmax: return launch_fwd_act<float, D, kSoftmax>(s, q, k, v, out, lse, st);
+    case kSilu: return launch_fwd_act<float, D, kSilu>(s, q, k, v, out, lse, st);
+    case kGelu: return launch_fwd_act<float, D, kGelu>(s, q, k, v, out, lse, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_bwd_d(const Shape &s, const void *q, const void *k, const void *v,
+                        const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                        void *dv, hipStream_t st) {
+    switch (s.act) {
+    case kSoftmax:
+        return launch_bwd_act<float, D, kSoftmax>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
+    case kSilu:
+        return launch_bwd_act<float, D, kSilu>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
+    case kGelu:
+        return launch_bwd_act<float, D, kGelu>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_scalar_fwd(const Shape &s, bool bf16_io, const void *q, const void *k,
                              const void *v, void *out, float *lse, hipStream_t st) {
+    if (bf16_io) return hipErrorInvalidValue;  // bf16 storage runs on the MFMA kernels
     switch (s.D) {
-#define BA_CASE(DD)                                                              \
-    case DD:                                                                     \
-        return bf16_io ? launch_scalar_fwd_t<bf16, DD>(s, q, k, v, out, lse, st) \
-                       : launch_scalar_fwd_t<float, DD>(s, q, k, v, out, lse, st);
-        BA_CASE(32) BA_CASE(64) BA_CASE(128)
-#undef BA_CASE
+    case 32: return launch_fwd_d<32>(s, q, k, v, out, lse, st);
+    case 64: return launch_fwd_d<64>(s, q, k, v, out, lse, st);
+    case 128: return launch_fwd_d<128>(s, q, k, v, out, lse, st);
     }
     return hipErrorInvalidValue;
 }
@@ -311,15 +352,11 @@ hipError_t launch_scalar_bwd(const Shape &s, bool bf16_io, const void *q, const 
                              const void *v, const void *out, const void *dout,
                              const float *lse, void *dq, void *dk, void *dv,
                              hipStream_t st) {
+    if (bf16_io) return hipErrorInvalidValue;
     switch (s.D) {
-#define BA_CASE(DD)                                                                     \
-    case DD:                                                                            \
-        return bf16_io ? launch_scalar_bwd_t<bf16, DD>(s, q, k, v, out, dout, lse, dq,  \
-                                                       dk, dv, st)                      \
-                       : launch_scalar_bwd_t<float, DD>(s, q, k, v, out, dout, lse, dq, \
-                                                        dk, dv, st);
-        BA_CASE(32) BA_CASE(64) BA_CASE(128)
-#undef BA_CASE
+    case 32: return launch_bwd_d<32>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
+    case 64: return launch_bwd_d<64>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
+    case 128: return launch_bwd_d<128>(s, q, k, v, out, dout, lse, dq, dk, dv, st);
     }
     return hipErrorInvalidValue;
 }

@@ -53,6 +53,7 @@ class Workload:
     fixed_length: int = 0    # >0: every user has this length
     dout_wid: int = 0        # seed id of the dO stream (backward only)
     rope_base: float = 0.0   # >0: rotary embedding of q and k with this base
+    act: int = 0             # 0 softmax; 1 SiLU, 2 GELU (generalized dot-product attention)
 
     @property
     def scale(self) -> float:
@@ -113,6 +114,11 @@ WORKLOADS = {
     7: Workload(3, "jagged-bf16-train-rope", users=256, heads=8, head_dim=64,
                 block_size=128, window_blocks=2, dtype="bf16", backward=True,
                 dout_wid=5, rope_base=10000.0),
+    # The training step with SiLU scores in place of the softmax (generalized
+    # dot-product attention on the block pattern).
+    8: Workload(3, "jagged-bf16-train-gdpa-silu", users=256, heads=8, head_dim=64,
+                block_size=128, window_blocks=2, dtype="bf16", backward=True,
+                dout_wid=5, act=1),
 }
 
 # Length sweep of the long-context workload (time should grow linearly).

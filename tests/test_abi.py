@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 4
+    assert lsb.blockattn_abi_version() == 5
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -133,6 +133,26 @@ def test_rope_argument_checks():
     assert lsb.blockattn_rope_bwd(*b.values()) == binding.ERR_INVALID_ARGUMENT
     b.update(theta_base=10000.0, workspace=None)
     assert lsb.blockattn_rope_bwd(*b.values()) == binding.ERR_WORKSPACE
+
+
+def test_gdpa_argument_checks():
+    a = dict(q=FAKE, k=FAKE, v=FAKE, offsets=FAKE, batch=2, total_tokens=100, num_heads=2,
+             head_dim=64, block_size=64, window_blocks=2, scale=0.125, activation=0,
+             dtype=lsb.BF16, out=FAKE, stream=None)
+    assert lsb.blockattn_gdpa_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(activation=3)
+    assert lsb.blockattn_gdpa_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(activation=lsb.GDPA_GELU, out=None)
+    assert lsb.blockattn_gdpa_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(out=FAKE, total_tokens=0)
+    assert lsb.blockattn_gdpa_fwd(*a.values()) == binding.OK
+    b = dict(q=FAKE, k=FAKE, v=FAKE, dout=FAKE, offsets=FAKE, batch=2, total_tokens=100,
+             num_heads=2, head_dim=64, block_size=64, window_blocks=2, scale=0.125,
+             activation=lsb.GDPA_SILU, dtype=lsb.BF16, dq=FAKE, dk=FAKE, dv=None,
+             workspace=FAKE, workspace_bytes=1 << 20, stream=None)
+    assert lsb.blockattn_gdpa_bwd(*b.values()) == binding.ERR_INVALID_ARGUMENT
+    b.update(dv=FAKE, workspace=None)
+    assert lsb.blockattn_gdpa_bwd(*b.values()) == binding.ERR_WORKSPACE
 
 
 def test_workspace_size():
