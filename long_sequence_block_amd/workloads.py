@@ -32,6 +32,7 @@ import math
 import numpy as np
 
 STREAM_LENGTHS, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = 0, 1, 2, 3, 4
+STREAM_QMX, STREAM_QSC, STREAM_KMX, STREAM_KSC = 5, 6, 7, 8
 
 
 def rng(workload: int, stream: int) -> np.random.Generator:
@@ -54,6 +55,7 @@ class Workload:
     dout_wid: int = 0        # seed id of the dO stream (backward only)
     rope_base: float = 0.0   # >0: rotary embedding of q and k with this base
     act: int = 0             # 0 softmax; 1 SiLU, 2 GELU (generalized dot-product attention)
+    mx: bool = False         # q and k as MXFP8 codes and block scales
 
     @property
     def scale(self) -> float:
@@ -82,6 +84,25 @@ def offsets_from_lengths(lengths) -> np.ndarray:
     if off[-1] > np.iinfo(np.int32).max:
         raise ValueError("total token count does not fit int32 offsets")
     return off.astype(np.int32)
+
+
+def mx_codes(wid: int, stream: int, shape) -> np.ndarray:
+    """Random MXFP8 element codes (OCP E4M3 bytes: sign, 4-bit exponent field,
+    3-bit mantissa).  Sign and mantissa uniform, exponent field uniform in
+    [9, 15], the NaN code excluded: magnitudes 4 .. 448, the range an MX block
+    of N(0, 1) values fills once its scale maps the block maximum near 448."""
+    g = rng(wid, stream)
+    sign = g.integers(0, 2, size=shape, dtype=np.uint8)
+    expo = g.integers(9, 16, size=shape, dtype=np.uint8)
+    mant = g.integers(0, 8, size=shape, dtype=np.uint8)
+    mant = np.where((expo == 15) & (mant == 7), np.uint8(6), mant)
+    return ((sign << 7) | (expo << 3) | mant).astype(np.uint8)
+
+
+def mx_scales(wid: int, stream: int, shape) -> np.ndarray:
+    """Random E8M0 block scales (biased exponents) in 119 .. 121, i.e.
+    2^-8 .. 2^-6: with the codes above, values of magnitude 0.016 .. 3.5."""
+    return rng(wid, stream).integers(119, 122, size=shape, dtype=np.uint8)
 
 
 def normal(wid: int, stream: int, shape) -> np.ndarray:
@@ -114,6 +135,13 @@ WORKLOADS = {
     7: Workload(3, "jagged-bf16-train-rope", users=256, heads=8, head_dim=64,
                 block_size=128, window_blocks=2, dtype="bf16", backward=True,
                 dout_wid=5, rope_base=10000.0),
+    # The long-context and jagged forwards with q and k in MXFP8 (the score
+    # product on the block-scaled fp8 matrix cores; v stays bf16).
+    9: Workload(4, "long-context-mxfp8qk", users=32, heads=8, head_dim=128,
+                block_size=256, window_blocks=4, dtype="bf16", backward=False,
+                fixed_length=16384, mx=True),
+    10: Workload(3, "jagged-mxfp8qk", users=256, heads=8, head_dim=64, block_size=128,
+                 window_blocks=2, dtype="bf16", backward=False, mx=True),
     # The training step with SiLU scores in place of the softmax (generalized
     # dot-product attention on the block pattern).
     8: Workload(3, "jagged-bf16-train-gdpa-silu", users=256, heads=8, head_dim=64,
@@ -142,10 +170,19 @@ def draw(w: Workload, users=None):
     off = w.offsets()
     T = int(off[-1])
     shape = (T, w.heads, w.head_dim)
-    out = {"offsets": off,
-           "q": normal(w.wid, STREAM_Q, shape),
-           "k": normal(w.wid, STREAM_K, shape),
-           "v": normal(w.wid, STREAM_V, shape)}
+    if w.mx:
+        sshape = (T, w.heads, w.head_dim // 32)
+        out = {"offsets": off,
+               "q_mx": mx_codes(w.wid, STREAM_QMX, shape),
+               "q_sc": mx_scales(w.wid, STREAM_QSC, sshape),
+               "k_mx": mx_codes(w.wid, STREAM_KMX, shape),
+               "k_sc": mx_scales(w.wid, STREAM_KSC, sshape),
+               "v": normal(w.wid, STREAM_V, shape)}
+    else:
+        out = {"offsets": off,
+               "q": normal(w.wid, STREAM_Q, shape),
+               "k": normal(w.wid, STREAM_K, shape),
+               "v": normal(w.wid, STREAM_V, shape)}
     if w.backward:
         out["dout"] = normal(w.dout_wid, STREAM_DO, shape)
     if users is not None:
@@ -184,3 +221,16 @@ def random_case(seed: int, lengths, heads: int, head_dim: int, with_dout=True):
     if with_dout:
         out["dout"] = g.standard_normal(size=shape, dtype=np.float32)
     return out
+
+
+def random_mx_case(seed: int, lengths, heads: int, head_dim: int):
+    """Small seeded case with q and k as MXFP8 codes and block scales (the
+    draws of mx_codes / mx_scales) and v as N(0, 1)."""
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    shape, sshape = (T, heads, head_dim), (T, heads, head_dim // 32)
+    wid = 2000 + seed
+    return {"offsets": off,
+            "q_mx": mx_codes(wid, STREAM_QMX, shape), "q_sc": mx_scales(wid, STREAM_QSC, sshape),
+            "k_mx": mx_codes(wid, STREAM_KMX, shape), "k_sc": mx_scales(wid, STREAM_KSC, sshape),
+            "v": normal(wid, STREAM_V, shape)}

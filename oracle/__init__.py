@@ -190,6 +190,39 @@ def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale:
     return dq, dk, dv
 
 
+# ------------------------------------------------------------------ MXFP8
+#
+# "GEM (Meta)", section "Custom kernels", says production attention runs in
+# MXFP8, a block-scaled FP8 format, and names nothing more.  The reading is
+# the OCP Microscaling format: elements are E4M3 bytes (sign, 4-bit exponent
+# with bias 7, 3-bit mantissa; exponent field 0 is subnormal, m * 2^-9; the
+# code with all exponent and mantissa bits set is NaN; no infinities), and
+# every 32 consecutive elements along the head dim share one E8M0 scale
+# byte, 2^(s - 127) (255 is NaN).  Decoding is exact in fp64.
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 byte, from its bit fields."""
+    s, e, m = (code >> 7) & 1, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    v = m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+_E4M3 = np.array([e4m3_value(c) for c in range(256)], np.float64)
+
+
+def mx_decode(codes, scales) -> np.ndarray:
+    """fp64 values of MXFP8 data: codes uint8 [..., D], scales uint8
+    [..., D/32] (scale j covers elements 32j .. 32j + 31)."""
+    codes, scales = np.asarray(codes, np.uint8), np.asarray(scales, np.uint8)
+    if codes.shape[-1] != 32 * scales.shape[-1] or codes.shape[:-1] != scales.shape[:-1]:
+        raise ValueError("one scale per 32 elements of the last axis")
+    f = np.where(scales == 255, np.nan, np.ldexp(1.0, scales.astype(np.int64) - 127))
+    return _E4M3[codes] * np.repeat(f, 32, axis=-1)
+
+
 # ------------------------------------------------- rotary position embedding
 #
 # The production block-attention kernel fuses the backward of a rotary
