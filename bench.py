@@ -31,6 +31,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -80,13 +81,16 @@ def cpu_baseline(w, users: int, flops_per_pair_head: float):
     c = wl.draw(w, users=slice(0, users))
     host = {}
     for key, val in c.items():
-        if key == "offsets":
+        if key == "offsets" or key.endswith("_mx") or key.endswith("_sc"):
             host[key] = val
         else:
             t = torch.from_numpy(val)
             if w.dtype == "bf16":
                 t = t.to(torch.bfloat16)
             host[key] = t.to(torch.float64).numpy()
+    if w.mx:  # the oracle attends on the decoded MXFP8 values
+        host["q"] = oracle.mx_decode(host.pop("q_mx"), host.pop("q_sc"))
+        host["k"] = oracle.mx_decode(host.pop("k_mx"), host.pop("k_sc"))
     off = host["offsets"]
     t0 = time.perf_counter()
     q, k, v = host["q"], host["k"], host["v"]
@@ -180,14 +184,20 @@ def main():
     c = wl.draw(w)
     off_np = c["offsets"]
     T = int(off_np[-1])
-    d = {k: torch.from_numpy(v).to(dev) if k == "offsets" else
-         torch.from_numpy(v).to(tdt).to(dev) for k, v in c.items()}
+    if w.mx:  # fp8 codes as is, scales head-major [H, T, D/32]
+        d = {k: torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)) if k.endswith("_sc")
+                                 else v).to(dev) for k, v in c.items() if k != "v"}
+        d["v"] = torch.from_numpy(c["v"]).to(tdt).to(dev)
+        d["q"], d["k"] = d.pop("q_mx"), d.pop("k_mx")
+    else:
+        d = {k: torch.from_numpy(v).to(dev) if k == "offsets" else
+             torch.from_numpy(v).to(tdt).to(dev) for k, v in c.items()}
     del c
     B, W, sc = w.block_size, w.window_blocks, w.scale
     H, D = w.heads, w.head_dim
-    out = torch.empty_like(d["q"])
+    out = torch.empty_like(d["v"])
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
-    grads = tuple(torch.empty_like(d["q"]) for _ in range(3)) if w.backward else None
+    grads = tuple(torch.empty_like(d["v"]) for _ in range(3)) if w.backward else None
     ws_n = lsb.blockattn_bwd_workspace_size(T, d["offsets"].numel() - 1, H,
                                            lsb.BF16 if w.dtype == "bf16" else lsb.FP32)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
@@ -199,7 +209,10 @@ def main():
             ev[0].record()
         if rb:  # rotary embedding of q and k into qa, ka
             lsb.rope(d["q"], d["k"], d["offsets"], rb, q_rot=qa, k_rot=ka)
-        if w.act:  # activation scores (GDPA): no lse
+        if w.mx:  # q, k in MXFP8
+            lsb.mx_fwd(qa, d["q_sc"], ka, d["k_sc"], d["v"], d["offsets"], B, W, sc, out=out,
+                       lse=lse)
+        elif w.act:  # activation scores (GDPA): no lse
             lsb.gdpa_fwd(qa, ka, d["v"], d["offsets"], B, W, sc, w.act, out=out)
         else:
             lsb.fwd(qa, ka, d["v"], d["offsets"], B, W, sc, out=out, lse=lse)
@@ -237,11 +250,15 @@ def main():
     fwd_flops = 4.0 * D * npair * H
     bwd_flops = 8.0 * D * npair * H if w.backward else 0.0
     fwd_bytes = T * H * (4.0 * D * e + (0 if w.act else 4)) + (4.0 * T * H * D * e if rb else 0.0)
+    if w.mx:  # q, k one byte per element plus one scale byte per 32
+        fwd_bytes = T * H * (2.0 * D * (1 + 1 / 32) + 2.0 * D * e + 4)
     # GDPA's backward reads q, k, v, dO and writes dq, dk, dv (no out, no lse)
     bwd_bytes = (T * H * ((7.0 * D * e) if w.act else (8.0 * D * e + 4))) if w.backward else 0.0
     flops = fwd_flops + bwd_flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    if w.mx:  # half the products at the fp8 rate, half (P.V) at the bf16 rate
+        peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 
     # dominant kernel: the entry point (one launch each) with the larger time
     if w.backward and bwd_ms >= fwd_ms:
@@ -267,7 +284,9 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic (seeded; lognormal jagged lengths, N(0,1) values)",
+        "dtype": "mxfp8(qk)+bf16" if w.mx else w.dtype,
+        "data": "synthetic (seeded; lognormal jagged lengths, N(0,1) values"
+                + ("; random E4M3 codes and E8M0 scales for q, k)" if w.mx else ")"),
         "config": {"workload": w.name, "users": w.users, "tokens": T, "heads": H,
                    "head_dim": D, "block_size": B, "window_blocks": W,
                    "backward": w.backward, "pairs_per_head": npair,

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 5
+#define BLOCKATTN_ABI_VERSION 6
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -221,6 +221,31 @@ blockattn_status blockattn_gdpa_bwd(const void *q, const void *k, const void *v,
                                     blockattn_dtype dtype, void *dq, void *dk,
                                     void *dv, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Forward with q and k in MXFP8.  The pages say production attention runs in
+ * MXFP8, a block-scaled FP8 format ("GEM (Meta)", section "Custom kernels"),
+ * and give nothing more; the reading is the OCP Microscaling format: each
+ * element an E4M3 byte (bias 7, subnormals, no infinities, S.1111.111 NaN),
+ * every 32 consecutive head-dim elements sharing one E8M0 scale byte,
+ * 2^(e - 127).  Here the score product q.k runs on the block-scaled fp8
+ * matrix cores; v, out and the softmax are as in blockattn_fwd (bf16, fp32).
+ *   q, k       E4M3 bytes [T, H, D], 16-byte aligned
+ *   q_scale,   E8M0 bytes [H, T, D/32] (head-major, like lse), 4-byte
+ *   k_scale    aligned; element (t, h, d) has scale [h][t][d / 32]
+ *   v          bf16 [T, H, D];  out bf16 [T, H, D];  lse fp32 [H, T]
+ * D must be 64 or 128, and T * H * D / 32 a multiple of 4 (the scales are
+ * read in dword windows), else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments
+ * and errors as for blockattn_fwd.  There is no MXFP8 backward.
+ */
+blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
+                                  const void *k, const void *k_scale,
+                                  const void *v, const int32_t *offsets,
+                                  int32_t batch, int64_t total_tokens,
+                                  int32_t num_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t window_blocks,
+                                  float scale, void *out, float *lse,
+                                  hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *blockattn_status_string(blockattn_status status);

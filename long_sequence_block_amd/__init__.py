@@ -6,6 +6,7 @@ binding.  ``workloads`` draws the seeded synthetic inputs.
 """
 from .binding import (BF16, FP32, GDPA_GELU, GDPA_SILU, BlockAttnError,  # noqa: F401
                       blockattn_abi_version, blockattn_gdpa_bwd, blockattn_gdpa_fwd,
+                      blockattn_mx_fwd, mx_fwd,
                       blockattn_bwd, blockattn_bwd_workspace_size, blockattn_fwd,
                       blockattn_rope, blockattn_rope_bwd, blockattn_status_string,
                       blockattn_swa_bwd, blockattn_swa_fwd, bwd, fwd, library_path, load,

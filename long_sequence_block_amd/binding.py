@@ -22,7 +22,7 @@ GDPA_SILU, GDPA_GELU = 1, 2  # blockattn_gdpa_act
 # Every symbol include/blockattn.h declares.
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
            "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_rope", "blockattn_rope_bwd",
-           "blockattn_gdpa_fwd", "blockattn_gdpa_bwd",
+           "blockattn_gdpa_fwd", "blockattn_gdpa_bwd", "blockattn_mx_fwd",
            "blockattn_status_string", "blockattn_abi_version")
 
 _lib = None
@@ -75,6 +75,9 @@ def load() -> ctypes.CDLL:
     lib.blockattn_gdpa_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32,
                                        i32, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.blockattn_gdpa_bwd.restype = ctypes.c_int
+    lib.blockattn_mx_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32,
+                                     vp, vp, vp]
+    lib.blockattn_mx_fwd.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_abi_version.argtypes = []
@@ -143,6 +146,13 @@ def blockattn_gdpa_bwd(q, k, v, dout, offsets, batch, total_tokens, num_heads, h
     return load().blockattn_gdpa_bwd(q, k, v, dout, offsets, batch, total_tokens, num_heads,
                                      head_dim, block_size, window_blocks, scale, activation,
                                      dtype, dq, dk, dv, workspace, workspace_bytes, stream)
+
+
+def blockattn_mx_fwd(q, q_scale, k, k_scale, v, offsets, batch, total_tokens, num_heads,
+                     head_dim, block_size, window_blocks, scale, out, lse, stream) -> int:
+    return load().blockattn_mx_fwd(q, q_scale, k, k_scale, v, offsets, batch, total_tokens,
+                                   num_heads, head_dim, block_size, window_blocks, scale, out,
+                                   lse, stream)
 
 
 def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
@@ -367,3 +377,28 @@ def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale:
     if rc != OK:
         raise BlockAttnError("blockattn_gdpa_bwd", rc)
     return dq, dk, dv
+
+
+def mx_fwd(q, q_scale, k, k_scale, v, offsets, block_size: int, window_blocks: int,
+           scale: float, out=None, lse=None, stream=None):
+    """Forward with q and k in MXFP8 (blockattn_mx_fwd): q, k uint8 [T, H, D]
+    E4M3 codes; q_scale, k_scale uint8 [H, T, D/32] E8M0 scales; v bf16.
+    Returns (out bf16 [T, H, D], lse fp32 [H, T])."""
+    T, H, D = q.shape
+    for t in (q, k):
+        if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q and k must be contiguous uint8 [T, H, D] device tensors")
+    for t in (q_scale, k_scale):
+        if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
+            raise ValueError("q_scale and k_scale must be contiguous uint8 [H, T, D/32]")
+    if v.dtype != torch.bfloat16 or v.shape != (T, H, D) or not v.is_contiguous():
+        raise ValueError("v must be a contiguous bf16 [T, H, D] tensor")
+    out = torch.empty_like(v) if out is None else out
+    lse = torch.empty((H, T), dtype=torch.float32, device=v.device) if lse is None else lse
+    rc = blockattn_mx_fwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
+                          v.data_ptr(), offsets.data_ptr(), offsets.numel() - 1, T, H, D,
+                          block_size, window_blocks, float(scale), out.data_ptr(),
+                          lse.data_ptr(), _stream(stream))
+    if rc != OK:
+        raise BlockAttnError("blockattn_mx_fwd", rc)
+    return out, lse

@@ -24,6 +24,12 @@ hipError_t launch_rope(const Shape &s, bool bf16_io, const void *q, const void *
 hipError_t launch_mfma_fwd(const Shape &s, const void *q, const void *k, const void *v,
                            void *out, float *lse, hipStream_t st);
 
+// Forward with q and k in MXFP8: E4M3 bytes [T, H, D] and E8M0 block scales
+// [H, T, D/32]; v, out bf16.  D 64 or 128.
+hipError_t launch_mfma_fwd_mx(const Shape &s, const void *q, const void *q_scale, const void *k,
+                              const void *k_scale, const void *v, void *out, float *lse,
+                              hipStream_t st);
+
 // bf16 MFMA backward.  Workspace (caller-owned device memory, 256-byte
 // aligned): per-(head, token) row statistics lse * log2(e) and -delta, a
 // 256-byte block of counters (tile queues, tile count), per-user tile prefix

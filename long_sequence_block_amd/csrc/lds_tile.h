@@ -125,6 +125,27 @@ __device__ __forceinline__ int tr_read_offset(int lane, int h, int dt) {
     return TileGeom<D>::at(p, col >> 3) + ((col >> 2) & 1) * 8;
 }
 
+// LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr_of(const lds_t *p) { return (uint32_t)(uintptr_t)p; }
+
+// One dword per lane from `src` (4-byte aligned; `bytes` valid, the rest
+// zero) into LDS at byte address `dst`: 64 lanes x 4 bytes.
+__device__ __forceinline__ void dma_dwords_lds(const void *src, uint32_t bytes, uint32_t dst,
+                                               int lane) {
+    const uint64_t a = (uint64_t)src;
+    const i32x4 desc{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                     __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
+                     __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+    const uint32_t d = __builtin_amdgcn_readfirstlane(dst);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(d), "v"((uint32_t)lane * 4u), "s"(desc)
+        : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 lds_read16(const lds_t *p) {
     return *(const __attribute__((address_space(3))) bf16x8 *)p;
 }

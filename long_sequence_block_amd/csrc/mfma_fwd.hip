@@ -58,11 +58,21 @@ struct FwdChunk {
     bf16 v[kKC * D];
 };
 
-template <int D, int ACT>
+// MX: q and k are MXFP8 (E4M3 bytes [T, H, D], E8M0 block scales [H, T,
+// D/32], one per 32 head-dim elements) and the scores come from the
+// block-scaled fp8 products (v_mfma_scale_f32_32x32x64_f8f6f4: 64 head-dim
+// elements, i.e. two scale blocks, per product).  Its operand layout, from
+// an in-bounds probe on gfx950: lane (m, g) holds 16 bytes of each of the
+// two blocks, and the scale of (row m, block j) comes from lane m + 32j.
+// Those 16-byte reads are exactly the granule reads of a bf16 tile of D/2
+// columns, so the fp8 K tile uses that geometry and its DMA offsets as is.
+template <int D, int ACT, bool MX>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    bf16 *__restrict__ out, float *__restrict__ lse) {
+    bf16 *__restrict__ out, float *__restrict__ lse, const uint8_t *__restrict__ qsc,
+    const uint8_t *__restrict__ ksc) {
     using G = TileGeom<D>;
+    using G8 = TileGeom<(D >= 64 ? D / 2 : 32)>;  // an fp8 row of D bytes
     constexpr int NB = kBufs<D>;
     constexpr int kDma = 2 * G::kDmaPerWave;  // DMA instructions per wave per chunk
     __shared__ int sh[8];
@@ -91,25 +101,68 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     const float c = fmaxf(fabsf(s.scale) * kLog2e, 1e-30f);
     const float grow_thr = 8.f / c;
     // (the activation variants take the signed scale instead)
-    const uint32_t qsign = ACT == kSoftmax && s.scale < 0.f ? 0x80008000u : 0u;
+    const uint32_t qsign = MX ? (s.scale < 0.f ? 0x80808080u : 0u)
+                              : (ACT == kSoftmax && s.scale < 0.f ? 0x80008000u : 0u);
 
     const int kbeg = window_start(row0, s.B, s.W);
     const int nch = (row_end - kbeg + kKC - 1) / kKC;
-    const bf16 *kb = k + base + (int64_t)kbeg * rs;
+    // fp8 rows are addressed in bf16 units (half their byte offsets)
+    const int64_t rs8 = rs / 2;
+    const bf16 *kb = MX ? k + (t.tok0 + kbeg) * rs8 + (int64_t)t.h * (D / 2)
+                        : k + base + (int64_t)kbeg * rs;
     const bf16 *vb = v + base + (int64_t)kbeg * rs;
+    // byte offset of the first K scale of the tile, [H, T, D/32] layout
+    const int64_t ks0 = ((int64_t)t.h * s.T + t.tok0 + kbeg) * (D / 32);
     lds_t *lds = (lds_t *)sm;
     uint32_t voff[G::kDmaPerWave];
     dma_offsets<D>(voff, wave, lane, rsb);
+    uint32_t voff8[G8::kDmaPerWave];
+    if constexpr (MX) dma_offsets<G8::kRowBytes / 2>(voff8, wave, lane, (uint32_t)(rs8 * 2));
+    // Scales of chunk ci: a dword-aligned window starts `mis` bytes before
+    // them and lands in LDS after the fp8 K tile.
+    auto scale_mis = [&](int ci) { return (int)((ks0 + (int64_t)ci * kKC * (D / 32)) & 3); };
     auto issue = [&](int ci, int buf) {
         const int off = ci * kKC, rows = min(kKC, row_end - kbeg - off);
         lds_t *b = lds + buf * (int)sizeof(FwdChunk<D>);
-        dma_tile<D>(row_desc<D>(kb + off * rs, rows, rs), b, voff, wave);
+        if constexpr (MX) {
+            dma_tile<G8::kRowBytes / 2>(row_desc<G8::kRowBytes / 2>(kb + off * rs8, rows, rs8), b,
+                                        voff8, wave);
+            if (wave == 0) {
+                const uint8_t *sp = ksc + ks0 + (int64_t)off * (D / 32);
+                const int mis = scale_mis(ci);
+                dma_dwords_lds(sp - mis, (uint32_t)((rows * (D / 32) + mis + 3) & ~3),
+                               lds_addr_of(b + kKC * D), lane);
+            }
+        } else {
+            dma_tile<D>(row_desc<D>(kb + off * rs, rows, rs), b, voff, wave);
+        }
         dma_tile<D>(row_desc<D>(vb + off * rs, rows, rs), b + G::kBytes, voff, wave);
     };
 
     if (nch > 0) issue(0, 0);
-    bf16x8 qreg[D / 16];
-    {
+    bf16x8 qreg[MX ? 1 : D / 16];
+    i32x8 qf8[D >= 64 ? D / 64 : 1];
+    int qs8[D >= 64 ? D / 64 : 1];
+    if constexpr (MX) {
+        // lane (row, g): bytes 64i + 16g .. and 64i + 32 + 16g .. of its row,
+        // and the scale of block 2i + g
+        const uint8_t *qrow = (const uint8_t *)q + ((t.tok0 + my_row) * rs8 * 2 + (int64_t)t.h * D);
+        const uint8_t *srow = qsc + ((int64_t)t.h * s.T + t.tok0 + my_row) * (D / 32);
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+            int sc8 = 127;
+            if (my_row < row_end) {
+                lo = *(const uint4 *)(qrow + 64 * i + 16 * g);
+                hi = *(const uint4 *)(qrow + 64 * i + 32 + 16 * g);
+                sc8 = srow[2 * i + g];
+            }
+            qf8[i] = i32x8{(int)(lo.x ^ qsign), (int)(lo.y ^ qsign), (int)(lo.z ^ qsign),
+                           (int)(lo.w ^ qsign), (int)(hi.x ^ qsign), (int)(hi.y ^ qsign),
+                           (int)(hi.z ^ qsign), (int)(hi.w ^ qsign)};
+            qs8[i] = sc8;
+        }
+    } else {
         const bf16 *qrow = q + base + (int64_t)my_row * rs;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
@@ -132,7 +185,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     // chunk, sub-tile and 16-key offsets are added as immediates.
     int rd[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) rd[ks] = row_read_offset<D>(qi, g) ^ (ks << 5);
+    for (int ks = 0; ks < D / 16; ++ks)
+        rd[ks] = MX ? row_read_offset<G8::kRowBytes / 2>(qi, g) ^ (ks << 5)
+                    : row_read_offset<D>(qi, g) ^ (ks << 5);
+    // MX: byte offset of the lane's key row in the chunk's scale window
+    // (physical row m of the tile holds key sigma(m))
+    const int srd = sigma32(qi) * (D / 32);
     int trd[2][D / 32];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -248,14 +306,36 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
         for (int sub = 0; sub < 2; ++sub) {
             const int a = c0 + sub * 32;
             if (!(a <= w_last && a + 31 >= wave_klo)) continue;
-            // All K reads of the sub-tile first, then the S products.
-            bf16x8 ka[D / 16];
+            f32x16 sc;
+            if constexpr (MX) {
+                // fp8 K rows and their scales, then the block-scaled products
+                const lds_t *k8 = kt + sub * 32 * G8::kRowBytes;
+                const lds_t *sp = kt + kKC * D + scale_mis(ci) + sub * 32 * (D / 32) + srd + g;
+                i32x8 kf[D / 64];
+                int ksc8[D / 64];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                ka[ks] = lds_read16(kt + sub * 32 * G::kRowBytes + rd[ks]);
-            f32x16 sc = mfma32(ka[0], qreg[0], f32x16{});
+                for (int i = 0; i < D / 64; ++i) {
+                    const uint4 lo = __builtin_bit_cast(uint4, lds_read16(k8 + rd[2 * i]));
+                    const uint4 hi = __builtin_bit_cast(uint4, lds_read16(k8 + rd[2 * i + 1]));
+                    kf[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    ksc8[i] = *(const __attribute__((address_space(3))) uint8_t *)(sp + 2 * i);
+                }
+                sc = f32x16{};
 #pragma unroll
-            for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(ka[ks], qreg[ks], sc);
+                for (int i = 0; i < D / 64; ++i)
+                    sc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], qf8[i], sc, 0, 0,
+                                                                        0, ksc8[i], 0, qs8[i]);
+            } else {
+                // All K reads of the sub-tile first, then the S products.
+                bf16x8 ka[D / 16];
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    ka[ks] = lds_read16(kt + sub * 32 * G::kRowBytes + rd[ks]);
+                sc = mfma32(ka[0], qreg[0], f32x16{});
+#pragma unroll
+                for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(ka[ks], qreg[ks], sc);
+            }
             finish(sc, sub, a);
         }
     };
@@ -283,12 +363,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
         lse[(int64_t)t.h * s.T + t.tok0 + my_row] = (m * c + log2f(lt)) * kLn2;
 }
 
-template <int D, int ACT>
+template <int D, int ACT, bool MX = false>
 hipError_t launch_act(const Shape &s, const void *q, const void *k, const void *v, void *out,
-                      float *lse, hipStream_t st) {
+                      float *lse, hipStream_t st, const uint8_t *qsc = nullptr,
+                      const uint8_t *ksc = nullptr) {
     const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 1, s.H);
-    hipLaunchKernelGGL((fwd_mfma<D, ACT>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse);
+    hipLaunchKernelGGL((fwd_mfma<D, ACT, MX>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse, qsc,
+                       ksc);
     return hipGetLastError();
 }
 
@@ -304,6 +386,17 @@ hipError_t launch_t(const Shape &s, const void *q, const void *k, const void *v,
 }
 
 }  // namespace
+
+hipError_t launch_mfma_fwd_mx(const Shape &s, const void *q, const void *q_scale, const void *k,
+                              const void *k_scale, const void *v, void *out, float *lse,
+                              hipStream_t st) {
+    const uint8_t *qs = (const uint8_t *)q_scale, *ks = (const uint8_t *)k_scale;
+    switch (s.D) {
+    case 64: return launch_act<64, kSoftmax, true>(s, q, k, v, out, lse, st, qs, ks);
+    case 128: return launch_act<128, kSoftmax, true>(s, q, k, v, out, lse, st, qs, ks);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_mfma_fwd(const Shape &s, const void *q, const void *k, const void *v,
                            void *out, float *lse, hipStream_t st) {

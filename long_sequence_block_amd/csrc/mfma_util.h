@@ -39,6 +39,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const bf16 *base, int
 // from inline assembly): base address, 16-bit high part and stride 0, byte
 // count, and the dword-format word of gfx9 raw buffers.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ i32x4 row_desc(const bf16 *base, int rows, int64_t rs) {

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 5
+    assert lsb.blockattn_abi_version() == 6
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -153,6 +153,21 @@ def test_gdpa_argument_checks():
     assert lsb.blockattn_gdpa_bwd(*b.values()) == binding.ERR_INVALID_ARGUMENT
     b.update(dv=FAKE, workspace=None)
     assert lsb.blockattn_gdpa_bwd(*b.values()) == binding.ERR_WORKSPACE
+
+
+def test_mx_argument_checks():
+    a = dict(q=FAKE, q_scale=FAKE, k=FAKE, k_scale=FAKE, v=FAKE, offsets=FAKE, batch=2,
+             total_tokens=100, num_heads=2, head_dim=32, block_size=64, window_blocks=2,
+             scale=0.125, out=FAKE, lse=FAKE, stream=None)
+    assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_UNSUPPORTED    # D = 32
+    a.update(head_dim=64, total_tokens=101, num_heads=1)
+    assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_UNSUPPORTED    # 202 scale bytes
+    a.update(total_tokens=100, num_heads=2, k_scale=FAKE + 2)
+    assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(k_scale=FAKE, q=None)
+    assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(q=FAKE, total_tokens=0)
+    assert lsb.blockattn_mx_fwd(*a.values()) == binding.OK
 
 
 def test_workspace_size():
