@@ -94,3 +94,57 @@ def test_heads_independent(D, B, W, dtype):
     for x, y in zip(got[:1] + got[2:], base[:1] + base[2:]):
         assert torch.equal(x[:, [0, 2]], y[:, [0, 2]])
     assert torch.equal(got[1][[0, 2]], base[1][[0, 2]])
+
+
+def _variants(case, mxcase):
+    """One call of every variant entry point (bf16): sliding window, rotary
+    embedding with its fused backward, both GDPA activations, MXFP8."""
+    import long_sequence_block_amd as lsb
+    dev, _ = to_device(case, "bf16")
+    q, k, v, do, off = dev["q"], dev["k"], dev["v"], dev["dout"], dev["offsets"]
+    res = []
+    o, l = lsb.swa_fwd(q, k, v, off, 45, 0.125)
+    res += [o, l, *lsb.swa_bwd(q, k, v, o, do, l, off, 45, 0.125)]
+    qr, kr = lsb.rope(q, k, off, 10000.0)
+    o, l = lsb.fwd(qr, kr, v, off, 64, 2, 0.125)
+    res += [qr, kr, o, l, *lsb.rope_bwd(qr, kr, v, o, do, l, off, 64, 2, 0.125)]
+    for act in (lsb.GDPA_SILU, lsb.GDPA_GELU):
+        o = lsb.gdpa_fwd(q, k, v, off, 64, 2, 0.125, act)
+        res += [o, *lsb.gdpa_bwd(q, k, v, do, off, 64, 2, 0.125, act)]
+    m = {n: torch.from_numpy(np.ascontiguousarray(mxcase[n].transpose(1, 0, 2)) if n.endswith("_sc")
+                             else mxcase[n]).cuda() for n in ("q_mx", "q_sc", "k_mx", "k_sc")}
+    vm = torch.from_numpy(mxcase["v"]).to(torch.bfloat16).cuda()
+    om = torch.from_numpy(mxcase["offsets"]).cuda()
+    res += list(lsb.mx_fwd(m["q_mx"], m["q_sc"], m["k_mx"], m["k_sc"], vm, om, 64, 2, 0.125))
+    torch.cuda.synchronize()
+    return [r.cpu() for r in res]
+
+
+def test_variant_entry_points_are_deterministic():
+    """Every variant entry point gives the same bits on a second call (the
+    header's determinism promise covers them all)."""
+    print("variant determinism", flush=True)
+    case = wl.random_case(32, [700, 33, 260], 2, 64)
+    mxcase = wl.random_mx_case(7, [700, 33, 260], 2, 64)
+    a, b = _variants(case, mxcase), _variants(case, mxcase)
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x, y), i
+
+
+def test_gdpa_locality_outside_window():
+    """GDPA on the block pattern: keys and values outside every window of a
+    set of queries do not change their outputs, bit for bit."""
+    import long_sequence_block_amd as lsb
+    print("gdpa locality", flush=True)
+    B, W, L = 64, 2, 600
+    case = wl.random_case(33, [L], 2, 64)
+    dev, _ = to_device(case, "bf16")
+    o1 = lsb.gdpa_fwd(dev["q"], dev["k"], dev["v"], dev["offsets"], B, W, 0.125, lsb.GDPA_GELU)
+    k2, v2 = dev["k"].clone(), dev["v"].clone()
+    # rows 448.. (blocks 7, 8, 9) see keys from block 6 on: perturb blocks 0..5
+    k2[:384] += 1.0
+    v2[:384] -= 2.0
+    o2 = lsb.gdpa_fwd(dev["q"], k2, v2, dev["offsets"], B, W, 0.125, lsb.GDPA_GELU)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[448:], o2[448:])
+    assert not torch.equal(o1[:448], o2[:448])
