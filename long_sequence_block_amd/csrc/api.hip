@@ -28,8 +28,9 @@ blockattn_status check_common(const int32_t *offsets, int32_t batch, int64_t T,
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     if (D != 32 && D != 64 && D != 128) return BLOCKATTN_ERR_UNSUPPORTED;
     if (T > INT32_MAX) return BLOCKATTN_ERR_UNSUPPORTED;
-    // every launch's grid is bounded by H * (T/B + batch) * ceil(B/32)
-    const int64_t tiles = ((T + B - 1) / B + batch) * (int64_t)((B + 31) / 32) * H;
+    // the largest grid is the fp32 backward's: 2 * ceil(B/64) row tiles per
+    // block, at most ceil(T/B) + batch blocks, times H
+    const int64_t tiles = ((T + B - 1) / B + batch) * 2 * (int64_t)((B + 63) / 64) * H;
     if (tiles > (int64_t)INT32_MAX - 1024) return BLOCKATTN_ERR_UNSUPPORTED;
     // and the backward's tile table by (ceil(T/128) + batch) * 2 * H
     if (ba::bwd_max_tiles(T, batch, H) > (int64_t)INT32_MAX - 1024)

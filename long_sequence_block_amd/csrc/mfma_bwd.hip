@@ -35,6 +35,7 @@
 // and streams Q, dO and the two row statistics.  Chunks of 64 rows go from
 // HBM straight into two LDS buffers in turn, one barrier per chunk.
 #include <algorithm>
+#include <atomic>
 
 #include "kernels.h"
 #include "lds_tile.h"
@@ -895,10 +896,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
 // Workgroups of bwd_mfma<D, ACT> that fit on the current device at once.
 template <int D, int ACT>
 int resident_workgroups() {
-    static int cached[64];  // one per instantiation and device
+    // one per instantiation and device; concurrent first calls may both
+    // compute it, and store the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev >= 0 && dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
@@ -908,7 +914,7 @@ int resident_workgroups() {
         per < 1)
         per = 1;
     const int n = cus * per;
-    if (dev >= 0 && dev < 64) cached[dev] = n;
+    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
