@@ -18,6 +18,7 @@ oracle on a bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -151,6 +152,8 @@ def main():
                          "training step with SiLU scores (generalized dot-product attention)")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
+    ap.add_argument("--window-blocks", type=int, default=0,
+                    help="override the workload's window W (e.g. L/B: full causal attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-users", type=int, default=0,
                     help="users timed for the oracle baseline (default: all)")
@@ -178,6 +181,9 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.length:
         w = wl.long_context(args.length)
+    if args.window_blocks:
+        w = dataclasses.replace(w, window_blocks=args.window_blocks,
+                                name=f"{w.name}-W{args.window_blocks}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
