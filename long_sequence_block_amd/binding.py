@@ -195,6 +195,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _workspace(q, offsets, code, workspace):
+    """(pointer, bytes) of the backward's workspace: the caller's, or a new
+    device buffer of blockattn_bwd_workspace_size bytes (None, 0 if none is
+    needed)."""
+    T, H, _ = q.shape
+    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel()
+
+
 def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
         out=None, lse=None, stream=None):
     """Forward block attention.  Returns (out [T,H,D], lse fp32 [H,T])."""
@@ -227,11 +240,7 @@ def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
     dq, dk, dv = grads
-    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace(q, offsets, code, workspace)
     rc = blockattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                        dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
                        offsets.numel() - 1, T, H, D, block_size, window_blocks,
@@ -273,11 +282,7 @@ def swa_bwd(q, k, v, out, dout, lse, offsets, window_tokens: int, scale: float,
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
     dq, dk, dv = grads
-    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace(q, offsets, code, workspace)
     rc = blockattn_swa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
                            offsets.numel() - 1, T, H, D, window_tokens, float(scale), code,
@@ -322,11 +327,7 @@ def rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, block_size: int, window_b
     if grads is None:
         grads = tuple(torch.empty_like(q_rot) for _ in range(3))
     dq, dk, dv = grads
-    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_rot.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace(q_rot, offsets, code, workspace)
     rc = blockattn_rope_bwd(q_rot.data_ptr(), k_rot.data_ptr(), v.data_ptr(), out.data_ptr(),
                             dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
                             offsets.numel() - 1, T, H, D, block_size, window_blocks,
@@ -365,11 +366,7 @@ def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale:
     if grads is None:
         grads = tuple(torch.empty_like(q) for _ in range(3))
     dq, dk, dv = grads
-    need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace(q, offsets, code, workspace)
     rc = blockattn_gdpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                             offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
                             window_blocks, float(scale), int(activation), code, dq.data_ptr(),
