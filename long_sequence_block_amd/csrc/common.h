@@ -135,7 +135,7 @@ __device__ __forceinline__ int logical_tile() {
 // head).  Tiles exist only for rows that exist: a jagged batch costs no
 // padding.  Returns false for a workgroup beyond the last tile (the grid is
 // an upper bound, since the host never reads the offsets).  `sh` must hold
-// NT/64 + 3 ints in LDS.  All results are wave-uniform.
+// NT/64 + 4 ints in LDS.  All results are wave-uniform.
 template <int NT>
 __device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
     const int tid = threadIdx.x;
@@ -144,17 +144,22 @@ __device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
     int base = 0;
     for (int c0 = 0; c0 < s.batch; c0 += NT) {
         const int u = c0 + tid;
-        int n = 0;
+        int n = 0, a = 0, L = 0;
         if (u < s.batch) {
-            const int a = clamp_off(s.offsets[u], T), b = clamp_off(s.offsets[u + 1], T);
-            const int L = b > a ? b - a : 0;
+            a = clamp_off(s.offsets[u], T);
+            const int b = clamp_off(s.offsets[u + 1], T);
+            L = b > a ? b - a : 0;
             n = (L + R - 1) / R * tpb * s.H;
         }
         int chunk;
         const int incl = wg_inclusive_scan<NT>(n, sh, chunk);
+        // the thread of the owning user passes on its rows (no second read
+        // of the offsets)
         if (n > 0 && lt >= base + incl - n && lt < base + incl) {
             sh[NT / 64] = u;
             sh[NT / 64 + 1] = lt - (base + incl - n);
+            sh[NT / 64 + 2] = a;
+            sh[NT / 64 + 3] = L;
         }
         base += chunk;
         if (lt < base) break;  // uniform: base and lt are the same in every thread
@@ -163,8 +168,8 @@ __device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
     __syncthreads();
     const int u = __builtin_amdgcn_readfirstlane(sh[NT / 64]);
     const int local = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 1]);
-    const int a = clamp_off(s.offsets[u], T), b = clamp_off(s.offsets[u + 1], T);
-    const int L = b > a ? b - a : 0;
+    const int a = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 2]);
+    const int L = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 3]);
     const int per_head = (L + R - 1) / R * tpb;
     t.user = u;
     t.h = local / per_head;
