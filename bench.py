@@ -74,6 +74,31 @@ def measured_traffic(kernel: str, workload: str):
     return float(m_val.group(1))
 
 
+def measured_counters(kernel: str, workload: str):
+    """Shader clock and MFMA busy share of the dominant kernel from the
+    committed rocprofv3 counter summary (fwd_mfma for the forward, the main
+    kernel bwd_mfma for the backward), or None if there is none for the
+    current kernel sources."""
+    files = ([f"fwd_{workload}_counters.md", f"fwd-bwd_{workload}_counters.md"]
+             if kernel == "fwd" else [f"fwd-bwd_{workload}_counters.md"])
+    row_key = "fwd_mfma" if kernel == "fwd" else "bwd_mfma"
+    for f in files:
+        path = os.path.join(ROOT, "profiles", f)
+        if not os.path.exists(path):
+            continue
+        text = open(path).read()
+        m_src = re.search(r"kernel_source_hash\s*([0-9a-f]{16})", text)
+        if not m_src or m_src.group(1) != kernel_source_hash():
+            return None
+        for line in text.splitlines():
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if cells and cells[0].startswith(row_key) and len(cells) > 4:
+                return {"kernel": cells[0], "clock_ghz": float(cells[3]),
+                        "mfma_busy_pct": float(cells[4]),
+                        "source": os.path.join("profiles", f)}
+    return None
+
+
 def cpu_baseline(w, users: int, flops_per_pair_head: float):
     """The fp64 oracle, as it stands, on users [0, users) of the workload."""
     import oracle
@@ -155,6 +180,8 @@ def main():
     ap.add_argument("--window-blocks", type=int, default=0,
                     help="override the workload's window W (e.g. L/B: full causal attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold pass (steps after an L2 / Infinity Cache flush)")
     ap.add_argument("--cpu-users", type=int, default=0,
                     help="users timed for the oracle baseline (default: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -251,6 +278,29 @@ def main():
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd_ms = (sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps) if w.backward else 0.0
 
+    def spread(times):
+        t = sorted(times)
+        return {"median": round(t[len(t) // 2], 4), "min": round(t[0], 4)}
+
+    # Per-call medians and minima: warm (the back-to-back steps above) and
+    # cold (each step after a 512 MiB write that evicts L2 and the
+    # Infinity Cache; the write is outside the events).
+    calls = {"warm": {"fwd_ms": spread([e[0].elapsed_time(e[1]) for e in evs])}}
+    if w.backward:
+        calls["warm"]["bwd_ms"] = spread([e[1].elapsed_time(e[2]) for e in evs])
+    if not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            step(cold[i])
+        torch.cuda.synchronize()
+        del flush
+        calls["cold"] = {"fwd_ms": spread([e[0].elapsed_time(e[1]) for e in cold])}
+        if w.backward:
+            calls["cold"]["bwd_ms"] = spread([e[1].elapsed_time(e[2]) for e in cold])
+
     npair = pairs_per_head(off_np, B, W)
     e = 2 if w.dtype == "bf16" else 4
     fwd_flops = 4.0 * D * npair * H
@@ -281,6 +331,7 @@ def main():
         roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(ach, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     roof["traffic"] = measured_traffic(kname, w.name)
+    roof["counters"] = measured_counters(kname, w.name)
     roof["kernel"] = kname
     roof["avg_launch_ms"] = round(k_ms, 4)
     roof["algorithmic_bytes"] = k_bytes
@@ -302,6 +353,7 @@ def main():
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * tflops / peak, 3),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "calls": calls,
         "roofline": roof,
         "cpu_baseline": None,
         "kernel_source_hash": kernel_source_hash(),
