@@ -174,7 +174,9 @@ def main():
                          "5 jagged bf16 training step (default), 6 the same step with a "
                          "194-token sliding window (same visible-pair count), 7 the training "
                          "step with the rotary embedding (rope, fwd, fused rope backward), 8 the "
-                         "training step with SiLU scores (generalized dot-product attention)")
+                         "training step with SiLU scores (generalized dot-product attention), "
+                         "9 and 10 the long-context and jagged forwards with q, k in MXFP8, "
+                         "11 the long-context shape as a training step")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--window-blocks", type=int, default=0,

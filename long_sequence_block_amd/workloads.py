@@ -142,6 +142,11 @@ WORKLOADS = {
                 fixed_length=16384, mx=True),
     10: Workload(3, "jagged-mxfp8qk", users=256, heads=8, head_dim=64, block_size=128,
                  window_blocks=2, dtype="bf16", backward=False, mx=True),
+    # The long-context shape as a training step: forward and backward at
+    # head dimension 128 (dO drawn from its own seed).
+    11: Workload(4, "long-context-bf16-train", users=32, heads=8, head_dim=128,
+                 block_size=256, window_blocks=4, dtype="bf16", backward=True,
+                 fixed_length=16384, dout_wid=11),
     # The training step with SiLU scores in place of the softmax (generalized
     # dot-product attention on the block pattern).
     8: Workload(3, "jagged-bf16-train-gdpa-silu", users=256, heads=8, head_dim=64,

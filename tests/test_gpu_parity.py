@@ -153,7 +153,7 @@ def _samples(off, B, rng, n_users=6):
     return out
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 11])
 def test_workload_full_size_sampled(wid):
     w = wl.WORKLOADS[wid]
     _print(f"workload {wid} ({w.name}) full size, sampled rows")

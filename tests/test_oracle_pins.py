@@ -414,6 +414,11 @@ def test_workload_generator_shapes():
     # the sliding window of workload 6 matches the block pattern's work to 0.2%
     blk, swa = oracle.pair_count(off, 128, 2), oracle.pair_count(off, 1, 194)
     assert abs(swa / blk - 1) < 2.1e-3
+    # the long-context training step shares the long-context forward's inputs
+    lc, lct = wl.WORKLOADS[4], wl.WORKLOADS[11]
+    assert lct.backward and lct.offsets().tolist() == lc.offsets().tolist()
+    assert (lct.wid, lct.heads, lct.head_dim, lct.block_size, lct.window_blocks) == \
+        (lc.wid, lc.heads, lc.head_dim, lc.block_size, lc.window_blocks)
     # median of a lognormal(ln 600, 0.8) sample of 256 sits near 600
     assert 450 < np.median(L) < 750
 
