@@ -333,6 +333,10 @@ def main():
         roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(ach, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     roof["traffic"] = measured_traffic(kname, w.name)
+    # measured HBM rate of the dominant kernel: counted bytes per launch over
+    # this run's average launch time (null without a traffic measurement)
+    roof["traffic_gbs"] = (round(roof["traffic"] / (k_ms * 1e-3) / 1e9, 1)
+                           if roof["traffic"] else None)
     roof["counters"] = measured_counters(kname, w.name)
     roof["kernel"] = kname
     roof["avg_launch_ms"] = round(k_ms, 4)
