@@ -170,6 +170,14 @@ def blockattn_abi_version() -> int:
 status_string = blockattn_status_string
 
 # ------------------------------------------------------ torch conveniences
+#
+# Streams.  Each call runs on `stream` (default: the current stream).  The
+# outputs and the workspace this module allocates are allocated while that
+# stream is current, so the caching allocator hands their memory to other
+# work only in that stream's order, after the kernels that use it; the
+# workspace tensor stays referenced until the C call has been enqueued.
+# Tensors the caller passes in are the caller's to keep alive and to order
+# (torch's usual rules across streams, e.g. Tensor.record_stream).
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -190,22 +198,39 @@ def _check(q, k, v, offsets):
         raise ValueError("offsets must be a 1-D int32 device tensor")
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+def _check_like(q, *ts, what="out and dout"):
+    for t in ts:
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{what} must match q")
+
+
+def _check_lse(lse, H, T):
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+
+
+def _torch_stream(stream):
+    """The torch stream a call runs on: the given one, else the current."""
+    return torch.cuda.current_stream() if stream is None else stream
 
 
 def _workspace(q, offsets, code, workspace):
-    """(pointer, bytes) of the backward's workspace: the caller's, or a new
-    device buffer of blockattn_bwd_workspace_size bytes (None, 0 if none is
-    needed)."""
+    """The backward's workspace tensor: the caller's, or a new device buffer
+    of blockattn_bwd_workspace_size bytes (None if none is needed).  Called
+    with the call's stream current (see above)."""
     T, H, _ = q.shape
     need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if workspace is None:
-        return None, 0
-    return workspace.data_ptr(), workspace.numel()
+    return workspace
+
+
+def _ws_args(ws):
+    return (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+
+
+def _grads(q, grads):
+    return tuple(torch.empty_like(q) for _ in range(3)) if grads is None else grads
 
 
 def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
@@ -213,14 +238,14 @@ def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
     """Forward block attention.  Returns (out [T,H,D], lse fp32 [H,T])."""
     _check(q, k, v, offsets)
     T, H, D = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    rc = blockattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
-                       offsets.numel() - 1, T, H, D, block_size, window_blocks,
-                       float(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr(),
-                       _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+        rc = blockattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                           offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                           float(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr(),
+                           st.cuda_stream)
     if rc != OK:
         raise BlockAttnError("blockattn_fwd", rc)
     return out, lse
@@ -231,21 +256,20 @@ def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
     """Backward block attention.  Returns (dq, dk, dv), each [T,H,D]."""
     _check(q, k, v, offsets)
     T, H, D = q.shape
-    for t in (out, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("out and dout must match q")
-    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    _check_like(q, out, dout)
+    _check_lse(lse, H, T)
     code = _dtype_code(q)
-    if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
-    dq, dk, dv = grads
-    ws_ptr, ws_len = _workspace(q, offsets, code, workspace)
-    rc = blockattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                       dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
-                       offsets.numel() - 1, T, H, D, block_size, window_blocks,
-                       float(scale), code, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       ws_ptr, ws_len, _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv = _grads(q, grads)
+        ws = _workspace(q, offsets, code, workspace)
+        ws_ptr, ws_len = _ws_args(ws)
+        rc = blockattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
+                           offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                           float(scale), code, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           ws_ptr, ws_len, st.cuda_stream)
+        del ws
     if rc != OK:
         raise BlockAttnError("blockattn_bwd", rc)
     return dq, dk, dv
@@ -256,13 +280,13 @@ def swa_fwd(q, k, v, offsets, window_tokens: int, scale: float, out=None, lse=No
     """Token sliding-window forward (blockattn_swa_fwd).  Returns (out, lse)."""
     _check(q, k, v, offsets)
     T, H, D = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    rc = blockattn_swa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
-                           offsets.numel() - 1, T, H, D, window_tokens, float(scale),
-                           _dtype_code(q), out.data_ptr(), lse.data_ptr(), _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+        rc = blockattn_swa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                               offsets.numel() - 1, T, H, D, window_tokens, float(scale),
+                               _dtype_code(q), out.data_ptr(), lse.data_ptr(), st.cuda_stream)
     if rc != OK:
         raise BlockAttnError("blockattn_swa_fwd", rc)
     return out, lse
@@ -273,21 +297,20 @@ def swa_bwd(q, k, v, out, dout, lse, offsets, window_tokens: int, scale: float,
     """Token sliding-window backward (blockattn_swa_bwd).  Returns (dq, dk, dv)."""
     _check(q, k, v, offsets)
     T, H, D = q.shape
-    for t in (out, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("out and dout must match q")
-    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    _check_like(q, out, dout)
+    _check_lse(lse, H, T)
     code = _dtype_code(q)
-    if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
-    dq, dk, dv = grads
-    ws_ptr, ws_len = _workspace(q, offsets, code, workspace)
-    rc = blockattn_swa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
-                           offsets.numel() - 1, T, H, D, window_tokens, float(scale), code,
-                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len,
-                           _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv = _grads(q, grads)
+        ws = _workspace(q, offsets, code, workspace)
+        ws_ptr, ws_len = _ws_args(ws)
+        rc = blockattn_swa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
+                               offsets.numel() - 1, T, H, D, window_tokens, float(scale), code,
+                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len,
+                               st.cuda_stream)
+        del ws
     if rc != OK:
         raise BlockAttnError("blockattn_swa_bwd", rc)
     return dq, dk, dv
@@ -298,14 +321,14 @@ def rope(q, k, offsets, theta_base: float = 10000.0, q_rot=None, k_rot=None, str
     pass q_rot=q, k_rot=k to rotate in place."""
     _check(q, k, q, offsets)
     T, H, D = q.shape
-    q_rot = torch.empty_like(q) if q_rot is None else q_rot
-    k_rot = torch.empty_like(k) if k_rot is None else k_rot
-    for t in (q_rot, k_rot):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("q_rot and k_rot must match q")
-    rc = blockattn_rope(q.data_ptr(), k.data_ptr(), offsets.data_ptr(), offsets.numel() - 1, T,
-                        H, D, float(theta_base), _dtype_code(q), q_rot.data_ptr(),
-                        k_rot.data_ptr(), _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        q_rot = torch.empty_like(q) if q_rot is None else q_rot
+        k_rot = torch.empty_like(k) if k_rot is None else k_rot
+        _check_like(q, q_rot, k_rot, what="q_rot and k_rot")
+        rc = blockattn_rope(q.data_ptr(), k.data_ptr(), offsets.data_ptr(), offsets.numel() - 1,
+                            T, H, D, float(theta_base), _dtype_code(q), q_rot.data_ptr(),
+                            k_rot.data_ptr(), st.cuda_stream)
     if rc != OK:
         raise BlockAttnError("blockattn_rope", rc)
     return q_rot, k_rot
@@ -318,21 +341,21 @@ def rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, block_size: int, window_b
     (dq, dk, dv) with dq, dk taken with respect to the unrotated q, k."""
     _check(q_rot, k_rot, v, offsets)
     T, H, D = q_rot.shape
-    for t in (out, dout):
-        if t.shape != q_rot.shape or t.dtype != q_rot.dtype or not t.is_contiguous():
-            raise ValueError("out and dout must match q")
-    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+    _check_like(q_rot, out, dout)
+    _check_lse(lse, H, T)
     code = _dtype_code(q_rot)
-    if grads is None:
-        grads = tuple(torch.empty_like(q_rot) for _ in range(3))
-    dq, dk, dv = grads
-    ws_ptr, ws_len = _workspace(q_rot, offsets, code, workspace)
-    rc = blockattn_rope_bwd(q_rot.data_ptr(), k_rot.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
-                            offsets.numel() - 1, T, H, D, block_size, window_blocks,
-                            float(scale), float(theta_base), code, dq.data_ptr(),
-                            dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv = _grads(q_rot, grads)
+        ws = _workspace(q_rot, offsets, code, workspace)
+        ws_ptr, ws_len = _ws_args(ws)
+        rc = blockattn_rope_bwd(q_rot.data_ptr(), k_rot.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
+                                window_blocks, float(scale), float(theta_base), code,
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len,
+                                st.cuda_stream)
+        del ws
     if rc != OK:
         raise BlockAttnError("blockattn_rope_bwd", rc)
     return dq, dk, dv
@@ -344,11 +367,13 @@ def gdpa_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float
     block pattern with P = act(scale q.k), no normalisation.  Returns out."""
     _check(q, k, v, offsets)
     T, H, D = q.shape
-    out = torch.empty_like(q) if out is None else out
-    rc = blockattn_gdpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
-                            offsets.numel() - 1, T, H, D, block_size, window_blocks,
-                            float(scale), int(activation), _dtype_code(q), out.data_ptr(),
-                            _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        out = torch.empty_like(q) if out is None else out
+        rc = blockattn_gdpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                                offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                                float(scale), int(activation), _dtype_code(q), out.data_ptr(),
+                                st.cuda_stream)
     if rc != OK:
         raise BlockAttnError("blockattn_gdpa_fwd", rc)
     return out
@@ -360,17 +385,19 @@ def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale:
     Returns (dq, dk, dv)."""
     _check(q, k, v, offsets)
     T, H, D = q.shape
-    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
-        raise ValueError("dout must match q")
+    _check_like(q, dout, what="dout")
     code = _dtype_code(q)
-    if grads is None:
-        grads = tuple(torch.empty_like(q) for _ in range(3))
-    dq, dk, dv = grads
-    ws_ptr, ws_len = _workspace(q, offsets, code, workspace)
-    rc = blockattn_gdpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                            offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
-                            window_blocks, float(scale), int(activation), code, dq.data_ptr(),
-                            dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv = _grads(q, grads)
+        ws = _workspace(q, offsets, code, workspace)
+        ws_ptr, ws_len = _ws_args(ws)
+        rc = blockattn_gdpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
+                                window_blocks, float(scale), int(activation), code,
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len,
+                                st.cuda_stream)
+        del ws
     if rc != OK:
         raise BlockAttnError("blockattn_gdpa_bwd", rc)
     return dq, dk, dv
@@ -390,12 +417,14 @@ def mx_fwd(q, q_scale, k, k_scale, v, offsets, block_size: int, window_blocks: i
             raise ValueError("q_scale and k_scale must be contiguous uint8 [H, T, D/32]")
     if v.dtype != torch.bfloat16 or v.shape != (T, H, D) or not v.is_contiguous():
         raise ValueError("v must be a contiguous bf16 [T, H, D] tensor")
-    out = torch.empty_like(v) if out is None else out
-    lse = torch.empty((H, T), dtype=torch.float32, device=v.device) if lse is None else lse
-    rc = blockattn_mx_fwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
-                          v.data_ptr(), offsets.data_ptr(), offsets.numel() - 1, T, H, D,
-                          block_size, window_blocks, float(scale), out.data_ptr(),
-                          lse.data_ptr(), _stream(stream))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        out = torch.empty_like(v) if out is None else out
+        lse = torch.empty((H, T), dtype=torch.float32, device=v.device) if lse is None else lse
+        rc = blockattn_mx_fwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(),
+                              k_scale.data_ptr(), v.data_ptr(), offsets.data_ptr(),
+                              offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                              float(scale), out.data_ptr(), lse.data_ptr(), st.cuda_stream)
     if rc != OK:
         raise BlockAttnError("blockattn_mx_fwd", rc)
     return out, lse

@@ -17,20 +17,33 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Checks shared by the forward and backward entry points.  Returns OK when
 // the call is valid and has work to do, OK with *empty set when it is valid
-// and empty, or an error code.
+// and empty, or an error code.  B and W are normalised in place: a block of
+// B >= T tokens holds any user whole, as one of T tokens does, and a window
+// of W >= ceil(T/B) blocks covers any user's whole past, as ceil(T/B) does,
+// so clamping both to those values changes no result and keeps every index
+// the kernels derive from them (W * B <= 2T) far from overflow.
 blockattn_status check_common(const int32_t *offsets, int32_t batch, int64_t T,
-                              int32_t H, int32_t D, int32_t B, int32_t W, float scale,
+                              int32_t H, int32_t D, int32_t *B, int32_t *W, float scale,
                               blockattn_dtype dtype, bool *empty) {
     *empty = false;
-    if (batch < 0 || T < 0 || H < 1 || B < 1 || W < 1 || !isfinite(scale))
+    if (batch < 0 || T < 0 || H < 1 || *B < 1 || *W < 1 || !isfinite(scale))
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     if (dtype != BLOCKATTN_BF16 && dtype != BLOCKATTN_FP32)
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     if (D != 32 && D != 64 && D != 128) return BLOCKATTN_ERR_UNSUPPORTED;
-    if (T > INT32_MAX) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (T > (int64_t)INT32_MAX - 1024) return BLOCKATTN_ERR_UNSUPPORTED;
+    // 32-bit byte offsets within a 128-row tile: 128 rows of H * D elements
+    // (at most 4 bytes each) must span less than 4 GiB
+    if ((int64_t)128 * H * D * 4 >= ((int64_t)1 << 32)) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (T > 0) {
+        if (*B > T) *B = (int32_t)T;
+        const int64_t nb = (T + *B - 1) / *B;
+        if (*W > nb) *W = (int32_t)nb;
+    }
     // the largest grid is the fp32 backward's: 2 * ceil(B/64) row tiles per
     // block, at most ceil(T/B) + batch blocks, times H
-    const int64_t tiles = ((T + B - 1) / B + batch) * 2 * (int64_t)((B + 63) / 64) * H;
+    const int64_t tiles =
+        ((T + *B - 1) / *B + batch) * 2 * (((int64_t)*B + 63) / 64) * (int64_t)H;
     if (tiles > (int64_t)INT32_MAX - 1024) return BLOCKATTN_ERR_UNSUPPORTED;
     // and the backward's tile table by (ceil(T/128) + batch) * 2 * H
     if (ba::bwd_max_tiles(T, batch, H) > (int64_t)INT32_MAX - 1024)
@@ -68,7 +81,7 @@ blockattn_status forward(const void *q, const void *k, const void *v, const int3
                          hipStream_t stream) {
     bool empty;
     blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
-                                       block_size, window_blocks, scale, dtype, &empty);
+                                       &block_size, &window_blocks, scale, dtype, &empty);
     if (st != BLOCKATTN_OK || empty) return st;
     const bool stats = act == ba::kSoftmax;
     if (!q || !k || !v || !out || (stats && !lse)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
@@ -95,7 +108,7 @@ blockattn_status backward(const void *q, const void *k, const void *v, const voi
                           size_t workspace_bytes, hipStream_t stream) {
     bool empty;
     blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
-                                       block_size, window_blocks, scale, dtype, &empty);
+                                       &block_size, &window_blocks, scale, dtype, &empty);
     if (st != BLOCKATTN_OK || empty) return st;
     const bool stats = act == ba::kSoftmax;  // out and lse enter only the softmax
     if (!q || !k || !v || !dout || !dq || !dk || !dv || (stats && (!out || !lse)))
@@ -173,8 +186,9 @@ blockattn_status blockattn_rope(const void *q, const void *k, const int32_t *off
                                 void *q_rot, void *k_rot, hipStream_t stream) {
     bool empty;
     // B and W do not enter the embedding; 1 and 1 pass the shared checks
-    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim, 1, 1,
-                                       1.f, dtype, &empty);
+    int32_t one_b = 1, one_w = 1;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim, &one_b,
+                                       &one_w, 1.f, dtype, &empty);
     if (st != BLOCKATTN_OK) return st;
     if (!isfinite(theta_base) || !(theta_base > 0.f)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
     if (empty) return BLOCKATTN_OK;
@@ -233,11 +247,9 @@ blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale, const void
                                   float scale, void *out, float *lse, hipStream_t stream) {
     bool empty;
     blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
-                                       block_size, window_blocks, scale, BLOCKATTN_BF16, &empty);
+                                       &block_size, &window_blocks, scale, BLOCKATTN_BF16, &empty);
     if (st != BLOCKATTN_OK) return st;
     if (head_dim != 64 && head_dim != 128) return BLOCKATTN_ERR_UNSUPPORTED;
-    // the scale DMA reads dword-aligned windows of the [H, T, D/32] tensors
-    if ((total_tokens * num_heads * (head_dim / 32)) % 4 != 0) return BLOCKATTN_ERR_UNSUPPORTED;
     if (empty) return BLOCKATTN_OK;
     if (!q || !q_scale || !k || !k_scale || !v || !out || !lse)
         return BLOCKATTN_ERR_INVALID_ARGUMENT;

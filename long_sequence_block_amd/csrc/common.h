@@ -149,7 +149,7 @@ __device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
             a = clamp_off(s.offsets[u], T);
             const int b = clamp_off(s.offsets[u + 1], T);
             L = b > a ? b - a : 0;
-            n = (L + R - 1) / R * tpb * s.H;
+            n = (int)(((int64_t)L + R - 1) / R * tpb * s.H);
         }
         int chunk;
         const int incl = wg_inclusive_scan<NT>(n, sh, chunk);
@@ -170,7 +170,7 @@ __device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
     const int local = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 1]);
     const int a = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 2]);
     const int L = __builtin_amdgcn_readfirstlane(sh[NT / 64 + 3]);
-    const int per_head = (L + R - 1) / R * tpb;
+    const int per_head = (int)(((int64_t)L + R - 1) / R * tpb);
     t.user = u;
     t.h = local / per_head;
     const int rem = local - t.h * per_head;

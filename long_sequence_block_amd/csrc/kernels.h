@@ -31,9 +31,11 @@ hipError_t launch_mfma_fwd_mx(const Shape &s, const void *q, const void *q_scale
                               hipStream_t st);
 
 // bf16 MFMA backward.  Workspace (caller-owned device memory, 256-byte
-// aligned): per-(head, token) row statistics lse * log2(e) and -delta, a
-// 256-byte block of counters (tile queues, tile count), per-user tile prefix
-// sums, and the tile table.  Each region starts on a 256-byte boundary.
+// aligned): per-(head, token) row statistics lse * log2(e) and -delta, which
+// the query pass writes for the key pass, a
+// 256-byte block of counters (the tile queues of the query and key passes,
+// the tile count), per-user tile prefix sums, and the tile table.  Each
+// region starts on a 256-byte boundary.
 constexpr int kBwdTileRows = 128;
 
 inline int64_t bwd_max_tiles(int64_t T, int batch, int H) {

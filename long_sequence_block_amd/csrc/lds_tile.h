@@ -146,6 +146,23 @@ __device__ __forceinline__ void dma_dwords_lds(const void *src, uint32_t bytes, 
         : "memory", "m0");
 }
 
+// The same 64 dwords as dma_dwords_lds, for a window whose last dword would
+// pass the end of its tensor: `bytes` (< 256) are valid.  Each lane loads its
+// 4 bytes one by one through a range-checked buffer (bytes past the range
+// read as zero) and writes the dword to LDS.  The loads are visible to the
+// compiler, which waits for them (and for everything issued before them)
+// before the write, so this path is for the rare window at a tensor's end.
+__device__ __forceinline__ void bytes_to_lds(const void *src, uint32_t bytes, uint32_t dst,
+                                             int lane) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, bytes, 0x00020000);
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (uint32_t)lane * 4u + b, 0, 0)
+             << (8 * b);
+    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(dst + (uint32_t)lane * 4u) = w;
+}
+
 __device__ __forceinline__ bf16x8 lds_read16(const lds_t *p) {
     return *(const __attribute__((address_space(3))) bf16x8 *)p;
 }

@@ -9,22 +9,35 @@
 //                                    dV_j = sum_i P_ij dO_i
 //
 // with P_ij = exp(scale <q_i,k_j> - lse_i), dP_ij = <dO_i, v_j>,
-// dS_ij = P_ij (dP_ij - delta_i) and delta_i = <dO_i, O_i>.  Each output
+// dS_ij = P_ij (dP_ij - delta_i) and delta_i = sum_j P_ij dP_ij.  Each output
 // element has exactly one owner, so there are no atomics on outputs and the
 // result is deterministic.  Visibility is the block window: local query i
 // sees local key j iff j <= i and floor(i/B) - floor(j/B) < W, so key j is
 // seen by queries j <= i < (floor(j/B) + W) * B.
 //
-// Three launches:
+// delta.  <dO_i, O_i> equals delta_i only for the exact O; the forward's O
+// is rounded to bf16, and with near-one-hot weights that rounding moves dS
+// enough to show in dQ and dK.  So the query role starts from delta'_i =
+// <dO_i, O_i> of the bf16 O and, from the same fp32 values that form dS,
+// sums eps_i = sum_j P_ij (dP_ij - delta'_i) = delta_i - delta'_i (the P_ij
+// of a row sum to 1) together with C_i = sum_j P_ij k_j (one more product,
+// on the transposed K it already reads).  Then
+//     dQ_i = scale sum_j P_ij (dP_ij - delta'_i) k_j - scale eps_i C_i,
+// and it writes delta_i and lse_i * log2(e) for the key role, which
+// therefore runs after it.
+//
+// Launches (softmax):
 //   1. bwd_tile_index (one workgroup): per-user tile counts from the jagged
-//      offsets, their prefix sums, the total, and a zeroed queue counter.
-//   2. bwd_prep: delta and lse * log2(e) of every row (memory bound), and the
-//      tile table (one 16-byte entry per (user, head, unit, role)).
-//   3. bwd_mfma: as many workgroups as fit on the GPU at once; each takes
-//      tiles from the queue counter until it runs dry.  While it works on one
-//      tile it already holds the next tile's table entry, has issued the next
-//      tile's first chunk and operand rows, and has requested the index of
-//      the tile after that, so per-tile set-up latency is hidden.
+//      offsets, their prefix sums, the total, and zeroed queue counters.
+//   2. bwd_table: the tile table (one 16-byte entry per (user, head, unit,
+//      role)).
+//   3. bwd_mfma, query pass, then 4. bwd_mfma, key pass: as many workgroups
+//      as fit on the GPU at once; each takes tiles of its pass from a queue
+//      counter until it runs dry.  While it works on one tile it already
+//      holds the next tile's table entry, has issued the next tile's first
+//      chunk and operand rows, and has requested the index of the tile after
+//      that, so per-tile set-up latency is hidden.
+// The activation variants (no delta) run both roles in one bwd_mfma launch.
 //
 // Layouts follow the forward kernel: 32x32x16 bf16 MFMAs, one query (query
 // role) or one key (key role) per lane column; streamed rows sit in LDS
@@ -32,7 +45,7 @@
 // of the next product, and the products that contract along the streamed
 // rows read them with transposed LDS reads.  The query role keeps its Q and
 // dO rows in registers and streams K and V; the key role keeps K and V rows
-// and streams Q, dO and the two row statistics.  Chunks of 64 rows go from
+// and streams Q, dO and the two row statistics of each query.  Chunks of 64 rows go from
 // HBM straight into two LDS buffers in turn, one barrier per chunk.
 #include <algorithm>
 #include <atomic>
@@ -54,6 +67,10 @@ constexpr int kKC = 64;        // rows per streamed chunk
 // in that XCD's L2.  Any placement of workgroups gives the same result.
 constexpr int kQueues = 8;
 constexpr int kRunTiles = 16;
+// The key pass's queue counters start here in the counter block (the query
+// pass, or a launch running both roles, uses ctr[0 .. kQueues); ctr[kQueues]
+// holds the tile count).
+constexpr int kPass1Ctr = 16;
 
 // Waves per SIMD the register budget is sized for.
 template <int D>
@@ -155,8 +172,10 @@ struct OpsLds {
 // Output store instructions per wave and tile.  The counts are fixed
 // (buffer instructions clip rows past the tile instead of branching around
 // them), so the next tile's first wait can allow for exactly these.
-template <int D>
-constexpr int kStores(int role) { return role == 0 ? D / 16 : D / 8; }
+// The softmax query role also stores its rows' exact -delta and
+// lse * log2(e) for the key pass (two more).
+template <int D, int ACT>
+constexpr int kStores(int role) { return role == 0 ? D / 16 + (ACT == kSoftmax ? 2 : 0) : D / 8; }
 
 // Writes a wave's 32 rows of one output (scaled by mul) as bf16; rows past
 // the tile are clipped by the buffer range.  With a rotary table (rrev, in
@@ -239,11 +258,18 @@ __device__ __forceinline__ QWin query_win(const Shape &s, const BwdTile &t, int 
 
 // One 64-key chunk of the query role: S^T and dP^T for each 32-key
 // sub-tile, then dQ^T += K^T dS^T.  c0 = first key of the chunk.
+//
+// Softmax: dP starts from -delta' (delta' = <dO, O> of the forward's bf16 O),
+// and the chunk also accumulates, for the exact delta, the lane's share of
+// eps = sum_j P_ij (dP_ij - delta'_i) (fp32, from the same values as dS) and
+// acc_c = C^T = K^T P^T, i.e. C_i = sum_j P_ij k_j, with the transposed K
+// operand the dQ product already reads.
 template <int D, int ACT>
 __device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int lane,
                                             const lds_t *kt, int c0, const Ops<D> &op,
                                             const f32x16 &ndlt, const ReadOffsets<D> &ro,
-                                            f32x16 (&acc)[D / 32]) {
+                                            f32x16 (&acc)[D / 32], f32x16 (&acc_c)[D / 32],
+                                            float &eps) {
     using G = TileGeom<D>;
     const float c = s.scale * kLog2e;
     const lds_t *vt = kt + G::kBytes;
@@ -305,12 +331,15 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int l
                 if ((uint32_t)(x + 16 * (r >> 3) + (r & 7)) > w.span) pr[r] = 0.f;
         }
         bf16x8 dsb[2];
+        float es[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = kk * 8 + 2 * j;
-                const bf16x2 v2 = pack_bf16(pr[r] * dp[r], pr[r + 1] * dp[r + 1]);
+                const float d0 = pr[r] * dp[r], d1 = pr[r + 1] * dp[r + 1];
+                if (ACT == kSoftmax) es[j] += d0 + d1;
+                const bf16x2 v2 = pack_bf16(d0, d1);
                 dsb[kk][2 * j] = v2[0];
                 dsb[kk][2 * j + 1] = v2[1];
             }
@@ -318,6 +347,24 @@ __device__ __forceinline__ void query_chunk(const Shape &s, const QWin &w, int l
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma32(ktr[kk][dt], dsb[kk], acc[dt]);
+        if constexpr (ACT == kSoftmax) {
+            eps += (es[0] + es[1]) + (es[2] + es[3]);
+            bf16x8 pb[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = kk * 8 + 2 * j;
+                    const bf16x2 p2 = pack_bf16(pr[r], pr[r + 1]);
+                    pb[kk][2 * j] = p2[0];
+                    pb[kk][2 * j + 1] = p2[1];
+                }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+                    acc_c[dt] = mfma32(ktr[kk][dt], pb[kk], acc_c[dt]);
+        }
     }
 }
 
@@ -497,7 +544,8 @@ __device__ __forceinline__ void key_chunk(const Shape &s, const KWin &w, int lan
 
 // Tile counts per user (ceil(L / 128) units x 2 roles x H heads), their
 // exclusive prefix sums into ubase[0..batch], the total into ctr[kQueues],
-// and the queue counters ctr[0 .. kQueues) = 0.  One workgroup.  Sums are
+// and the queue counters of both passes ctr[0 .. kQueues) and
+// ctr[kPass1Ctr .. kPass1Ctr + kQueues) = 0.  One workgroup.  Sums are
 // capped at `cap` (the table's capacity, which well-formed offsets never
 // reach), so malformed offsets cannot make the table writes overrun.
 __global__ __launch_bounds__(1024) void bwd_tile_index(Shape s, int cap, int *__restrict__ ctr,
@@ -521,61 +569,16 @@ __global__ __launch_bounds__(1024) void bwd_tile_index(Shape s, int cap, int *__
     if (threadIdx.x == 0) {
         const int n = (int)min(run, (long long)cap);
         ubase[s.batch] = n;
-        for (int i = 0; i < kQueues; ++i) ctr[i] = 0;
+        for (int i = 0; i < kQueues; ++i) ctr[i] = ctr[kPass1Ctr + i] = 0;
         ctr[kQueues] = n;
     }
 }
 
-// Workgroups [0, nrs) write the row statistics of 256 consecutive rows of
-// the [T*H, D] tensors (contiguous memory): delta = <dO, O> (fp32 from bf16
-// products), stored negated, and lse * log2(e), into [H, T] arrays.  Each
-// row is read by D/8 consecutive lanes, one 16-byte granule each.
-// Workgroup nrs + u writes the table entries of user u in the order head,
-// unit, role.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep(Shape s, int nrs, const bf16 *__restrict__ out,
-                                                const bf16 *__restrict__ dout,
-                                                const float *__restrict__ lse,
-                                                float *__restrict__ ws_lse2,
-                                                float *__restrict__ ws_ndlt,
-                                                const int *__restrict__ ubase,
-                                                int4 *__restrict__ table) {
-    const int b = (int)blockIdx.x;
-    if (b < nrs) {
-        constexpr int kLanes = D / 8;        // lanes per row
-        constexpr int kRows = 256 / kLanes;  // rows per pass of the workgroup
-        constexpr int kPass = 256 / kRows;
-        const int64_t nrow = s.T * s.H;
-        const int part = threadIdx.x % kLanes, rr = threadIdx.x / kLanes;
-        // all loads first, so each lane has 2 * kPass 16-byte loads in flight
-        bf16x8 xo[kPass], xd[kPass];
-#pragma unroll
-        for (int p = 0; p < kPass; ++p) {
-            const int64_t row = (int64_t)b * 256 + p * kRows + rr;  // = t * H + h
-            const int64_t o = min(row, nrow - 1) * D + part * 8;
-            xd[p] = *(const bf16x8 *)(dout + o);
-            xo[p] = *(const bf16x8 *)(out + o);
-        }
-        // row b * 256 + k is (token t0 + (h0 + k) / H, head (h0 + k) % H)
-        const int64_t r0 = (int64_t)b * 256;
-        const int64_t t0 = r0 / s.H;
-        const int h0 = (int)(r0 - t0 * s.H);
-#pragma unroll
-        for (int p = 0; p < kPass; ++p) {
-            const int k = p * kRows + rr;
-            float d = dot8(xd[p], xo[p], 0.f);
-#pragma unroll
-            for (int m = 1; m < kLanes; m <<= 1) d += __shfl_xor(d, m, kLanes);
-            if (part == 0 && r0 + k < nrow) {
-                const int q = (h0 + k) / s.H;
-                const int64_t o = (int64_t)(h0 + k - q * s.H) * s.T + t0 + q;
-                ws_ndlt[o] = -d;
-                ws_lse2[o] = lse[o] * kLog2e;
-            }
-        }
-        return;
-    }
-    const int u = b - nrs;
+// Workgroup u writes the table entries of user u in the order head, unit,
+// role.
+__global__ __launch_bounds__(256) void bwd_table(Shape s, const int *__restrict__ ubase,
+                                                 int4 *__restrict__ table) {
+    const int u = (int)blockIdx.x;
     const int j0 = ubase[u], j1 = ubase[u + 1];
     if (j1 <= j0) return;
     const int T = (int)s.T;
@@ -595,9 +598,14 @@ template <int D>
 struct BwdArgs {
     Shape s;
     const bf16 *q, *k, *v, *dout;
+    const bf16 *out;     // the forward's O (softmax query role: delta' = <dO, O>)
+    const float *lse;    // the forward's lse [H, T]
     const float *ws_lse2, *ws_ndlt;
     int *ctr;         // this group's queue counter
     const int4 *table;
+    int tstride, toff;  // tile n of this launch is table[n * tstride + toff]
+    float *ndlt_out;    // where the query role writes its rows' exact -delta
+    float *lse2_out;    // and their lse * log2(e)
     bf16 *dq, *dk, *dv;
     int ntiles;
     int group, ngroups;
@@ -679,7 +687,7 @@ __device__ __forceinline__ void issue_chunk(const BwdArgs<D> &A, const BwdTile &
 
 // Issues this wave's share of tile t's own rows (and, for the query role,
 // their row statistics) into the operand staging area.
-template <int D>
+template <int D, int ACT>
 __device__ __forceinline__ void issue_ops(const BwdArgs<D> &A, const BwdTile &t) {
     const int64_t rs = (int64_t)A.s.H * D;
     const int64_t base = ((int64_t)t.tok0 + t.row0) * rs + (int64_t)t.h * D;
@@ -695,14 +703,12 @@ __device__ __forceinline__ void issue_ops(const BwdArgs<D> &A, const BwdTile &t)
     if (t.role == 0) {
         rows_of(A.q, A.ol->a);
         rows_of(A.dout, A.ol->b);
-        // wave w: statistic w & 1 of rows 64 (w >> 1) ..
+        // waves 0 and 2: the forward's lse of rows 64 (w >> 1) ..
         const int half = A.wave >> 1;
         const int r = max(0, min(kKC, rows - half * kKC));
         const int64_t so = (int64_t)t.h * A.s.T + t.tok0 + t.row0 + half * kKC;
-        if (A.wave & 1)
-            dma_dwords(A.ws_ndlt + so, (uint32_t)r * 4u, lds_addr(A.ol->ndlt + half * kKC), A.lane);
-        else
-            dma_dwords(A.ws_lse2 + so, (uint32_t)r * 4u, lds_addr(A.ol->lse2 + half * kKC), A.lane);
+        if (ACT == kSoftmax && !(A.wave & 1))
+            dma_dwords(A.lse + so, (uint32_t)r * 4u, lds_addr(A.ol->lse2 + half * kKC), A.lane);
     } else {
         rows_of(A.k, A.ol->a);
         rows_of(A.v, A.ol->b);
@@ -725,37 +731,66 @@ __device__ __forceinline__ void read_ops(const BwdArgs<D> &A, const BwdTile &t, 
         op.a[ks] = lds_read16(ta + o);
         op.b[ks] = lds_read16(tb + o);
     }
-    if (t.role == 0) {
-        op.lse2 = A.ol->lse2[lr];
-        op.ndlt = A.ol->ndlt[lr];
-    } else {
-        op.lse2 = op.ndlt = 0.f;
-    }
+    // (query role: the forward's lse; -delta' is set by the caller)
+    op.lse2 = t.role == 0 ? A.ol->lse2[lr] * kLog2e : 0.f;
+    op.ndlt = 0.f;
+}
+
+// The lane's 16-byte granules 2ks + g (ks < D/16) of its own row of the
+// forward's O for query-role tile t, by plain buffer loads (rows past the
+// tile read as zero): the granules of dO that read_ops gives the lane, so
+// the lane's dot product covers half of the row and its lane^32 partner the
+// other half.  Issued before a tile's output stores, so the next tile's
+// first wait covers them.
+template <int D>
+__device__ __forceinline__ void load_orows(const BwdArgs<D> &A, const BwdTile &t,
+                                           bf16x8 (&o)[D / 16]) {
+    const int64_t rs = (int64_t)A.s.H * D;
+    const auto r = row_rsrc<D>(A.out + ((int64_t)t.tok0 + t.row0) * rs + (int64_t)t.h * D,
+                               t.row_end - t.row0, rs);
+    const uint32_t lr = (uint32_t)(wave_rows(t, A.wave) - t.row0 + (A.lane & 31));
+    const uint32_t off = lr * (uint32_t)(rs * 2) + (uint32_t)(A.lane >> 5) * 16u;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        o[ks] = __builtin_bit_cast(bf16x8, buf_load16(r, off + (uint32_t)ks * 32u));
 }
 
 // Works through tile t (of role ROLE, whose own rows and first chunk are in
 // flight or landed) and sets up the next one: returns false when the queue
 // has run dry, else the next tile in tn with its rows and first chunk issued.
+//
+// orow: the softmax query role's O granules of tile t's rows on entry (see
+// load_orows), and of the next tile's rows on return.
 template <int D, int ROLE, int ACT>
 __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<D> &ro,
-                                         BwdSched &sc, const BwdTile &t, BwdTile &tn) {
-    constexpr int NA = ROLE == 0 ? 1 : 2;  // accumulator sets
+                                         BwdSched &sc, const BwdTile &t, BwdTile &tn,
+                                         bf16x8 (&orow)[D / 16]) {
+    // accumulator sets: dQ (and C, softmax) or dK and dV
+    constexpr int NA = ROLE == 0 && ACT != kSoftmax ? 1 : 2;
     const int tid = threadIdx.x, g = A.lane >> 5;
     // The tile's rows and first chunk have landed; only the previous tile's
     // output stores may still be in flight.
     if (sc.prev_role < 0)
         wait_vm_barrier<0>();
     else if (sc.prev_role == 0)
-        wait_vm_barrier<kStores<D>(0)>();
+        wait_vm_barrier<kStores<D, ACT>(0)>();
     else
-        wait_vm_barrier<kStores<D>(1)>();
+        wait_vm_barrier<kStores<D, ACT>(1)>();
     Ops<D> op;
     read_ops<D>(A, t, op);
+    if (ROLE == 0 && ACT == kSoftmax) {
+        // delta' = <dO, O> of the lane's row (fp32 sums of bf16 products)
+        float d = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) d = dot8(op.b[ks], orow[ks], d);
+        op.ndlt = -swap_sum(d);
+    }
     // Index of the next tile (published at the end of the previous one).
     const int jn = __builtin_amdgcn_readfirstlane(A.ring[(sc.kt + 1) & 1]);
     // The next tile's 16-byte entry goes straight into LDS (lanes 0..3 one
     // dword each, the rest past the range); the chunk waits cover it.
-    if (jn < A.ntiles && A.wave == 0) dma_dwords(A.table + jn, 16u, lds_addr(A.entry), A.lane);
+    if (jn < A.ntiles && A.wave == 0)
+        dma_dwords(A.table + ((int64_t)jn * A.tstride + A.toff), 16u, lds_addr(A.entry), A.lane);
     // A one-chunk tile needs the entry in this same step, and must not
     // overwrite the staging area before every wave has read its rows.
     if (t.nch == 1) wait_vm_barrier<0>();
@@ -783,6 +818,7 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
         qw = query_win(A.s, t, A.wave, A.lane);
     else
         kw = key_win(A.s, t, A.wave, A.lane);
+    float eps = 0.f;  // softmax query role: this lane's share of delta - delta'
     bool has_next = false;
     for (int ci = 0; ci < t.nch; ++ci) {
         if (ci > 0) wait_vm_barrier<0>();  // chunk ci has landed
@@ -792,14 +828,15 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
             const int *e = A.entry;
             tn = make_tile(A.s, make_int4(e[0], e[1], e[2], e[3]));
             issue_chunk<D>(A, tn, 0, sc.buf ^ 1);
-            issue_ops<D>(A, tn);
+            issue_ops<D, ACT>(A, tn);
             has_next = true;
         }
         const lds_t *b = A.lds + sc.buf * (int)sizeof(BwdChunk<D>);
         const int c0 = t.sbeg + ci * kKC;
         if (live) {
             if (ROLE == 0)
-                query_chunk<D, ACT>(A.s, qw, A.lane, b, c0, op, ndlt, ro, acc[0]);
+                query_chunk<D, ACT>(A.s, qw, A.lane, b, c0, op, ndlt, ro, acc[0], acc[NA - 1],
+                                    eps);
             else
                 key_chunk<D, ACT>(A.s, kw, A.lane, b, A.sm[sc.buf], c0, op, ro, acc[0],
                                   acc[NA - 1]);
@@ -818,6 +855,25 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
     const int rows = t.row_end - t.row0;
     const uint32_t lrow = (uint32_t)(wave_rows(t, A.wave) - t.row0 + (A.lane & 31));
     const int pos = t.row0 + (int)lrow;  // local index of the lane's row
+    if (ROLE == 0 && ACT == kSoftmax && has_next) load_orows<D>(A, tn, orow);
+    if (ROLE == 0 && ACT == kSoftmax) {
+        // The exact delta_i = delta'_i + eps_i (sum_j P_ij = 1), and
+        // dQ_i = scale sum_j P_ij (dP_ij - delta_i) k_j
+        //      = (the dS-with-delta' sum) - scale eps_i C_i.
+        // (query i's keys are split between lanes i and i + 32)
+        const float e = swap_sum(eps);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[0][dt][r] = fmaf(-e, acc[NA - 1][dt][r], acc[0][dt][r]);
+        // -delta and lse * log2(e) of the lane's row for the key pass (lanes
+        // g = 1 and rows past the tile fall outside the buffer range: two
+        // stores per wave)
+        const int64_t so = (int64_t)t.h * A.s.T + t.tok0 + t.row0;
+        const uint32_t sb = g == 0 ? lrow * 4u : 0x80000000u;
+        buf_store4(op.ndlt - e, bytes_rsrc(A.ndlt_out + so, (uint32_t)rows * 4u), sb);
+        buf_store4(op.lse2, bytes_rsrc(A.lse2_out + so, (uint32_t)rows * 4u), sb);
+    }
     if (ROLE == 0) {
         store_rows<D>(A.dq + obase, rows, rs, lrow, acc[0], A.s.scale, g, A.rrev, pos);
     } else {
@@ -829,12 +885,19 @@ __device__ __forceinline__ bool run_tile(const BwdArgs<D> &A, const ReadOffsets<
     return has_next;
 }
 
-template <int D, int ACT>
+// PASS 0 runs the query-role tiles, PASS 1 the key-role tiles, PASS 2 both.
+// The softmax backward runs PASS 0 and then PASS 1 as two launches: the
+// query role computes each row's exact delta, which the key role needs.
+// The activation variants have no delta and run PASS 2.
+template <int D, int ACT, int PASS>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ dout, const float *__restrict__ ws_lse2,
-    const float *__restrict__ ws_ndlt, int *__restrict__ ctr, const int4 *__restrict__ table,
-    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+    const bf16 *__restrict__ dout, const bf16 *__restrict__ out, const float *__restrict__ lse,
+    float *__restrict__ ws_lse2, float *__restrict__ ws_ndlt, int *__restrict__ ctr,
+    const int4 *__restrict__ table, bf16 *__restrict__ dq, bf16 *__restrict__ dk,
+    bf16 *__restrict__ dv) {
+    static_assert(!(ACT == kSoftmax && PASS == 2),
+                  "the softmax key role must run after every query role has written delta");
     __shared__ __align__(1024) BwdChunk<D> sm[2];
     __shared__ __align__(1024) OpsLds<D> ol;
     __shared__ int ring[2];  // the next tile's index, by tile parity
@@ -847,12 +910,18 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
     A.k = k;
     A.v = v;
     A.dout = dout;
+    A.out = out;
+    A.lse = lse;
     A.ws_lse2 = ws_lse2;
     A.ws_ndlt = ws_ndlt;
+    A.lse2_out = ws_lse2;
     A.ngroups = min((int)gridDim.x, kQueues);
     A.group = (int)blockIdx.x % A.ngroups;
-    A.ctr = ctr + A.group;
+    A.ctr = ctr + (PASS == 1 ? kPass1Ctr : 0) + A.group;
     A.table = table;
+    A.tstride = PASS == 2 ? 1 : 2;
+    A.toff = PASS == 2 ? 0 : PASS;
+    A.ndlt_out = ws_ndlt;
     A.dq = dq;
     A.dk = dk;
     A.dv = dv;
@@ -876,25 +945,36 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void bwd_mfma(
         ring[1] = queue_tile(atomicAdd(A.ctr, 1), A.group, A.ngroups);
     }
     __syncthreads();
-    A.ntiles = __builtin_amdgcn_readfirstlane(ctr[kQueues]);
+    // (every unit has one tile of each role, so a single-role pass has half
+    // the table's tiles)
+    const int ntab = __builtin_amdgcn_readfirstlane(ctr[kQueues]);
+    A.ntiles = PASS == 2 ? ntab : ntab / 2;
     const int j0 = __builtin_amdgcn_readfirstlane(ring[0]);
     if (j0 >= A.ntiles) return;
-    BwdTile t = make_tile(s, table[j0]);
+    BwdTile t = make_tile(s, table[(int64_t)j0 * A.tstride + A.toff]);
     issue_chunk<D>(A, t, 0, 0);
-    issue_ops<D>(A, t);
+    issue_ops<D, ACT>(A, t);
+    bf16x8 orow[D / 16];
+    if (PASS == 0 && ACT == kSoftmax) load_orows<D>(A, t, orow);
 
     BwdSched sc{0, 0, -1};
     for (;;) {
         BwdTile tn;
-        const bool more = t.role == 0 ? run_tile<D, 0, ACT>(A, ro, sc, t, tn)
-                                      : run_tile<D, 1, ACT>(A, ro, sc, t, tn);
+        bool more;
+        if constexpr (PASS == 0)
+            more = run_tile<D, 0, ACT>(A, ro, sc, t, tn, orow);
+        else if constexpr (PASS == 1)
+            more = run_tile<D, 1, ACT>(A, ro, sc, t, tn, orow);
+        else
+            more = t.role == 0 ? run_tile<D, 0, ACT>(A, ro, sc, t, tn, orow)
+                               : run_tile<D, 1, ACT>(A, ro, sc, t, tn, orow);
         if (!more) break;
         t = tn;
     }
 }
 
-// Workgroups of bwd_mfma<D, ACT> that fit on the current device at once.
-template <int D, int ACT>
+// Workgroups of bwd_mfma<D, ACT, PASS> that fit on the current device at once.
+template <int D, int ACT, int PASS>
 int resident_workgroups() {
     // one per instantiation and device; concurrent first calls may both
     // compute it, and store the same value
@@ -909,7 +989,7 @@ int resident_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_mfma<D, ACT>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_mfma<D, ACT, PASS>, kThreads, 0) !=
             hipSuccess ||
         per < 1)
         per = 1;
@@ -926,17 +1006,24 @@ hipError_t launch_act(const Shape &s, const void *q, const void *k, const void *
     const int64_t max_tiles = bwd_max_tiles(s.T, s.batch, s.H);
     hipLaunchKernelGGL(bwd_tile_index, dim3(1), dim3(1024), 0, st, s, (int)max_tiles, w.ctr,
                        w.ubase);
-    // row statistics (lse and delta) only for the softmax; the activation
-    // variants need only the tile table
-    const int nrs = ACT == kSoftmax ? (int)((s.T * s.H + 255) / 256) : 0;
-    hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)(nrs + s.batch)), dim3(256), 0, st, s, nrs,
-                       (const bf16 *)out, (const bf16 *)dout, lse, w.lse2, w.ndlt,
+    hipLaunchKernelGGL(bwd_table, dim3((unsigned)s.batch), dim3(256), 0, st, s,
                        (const int *)w.ubase, w.table);
-    const int64_t grid = std::min<int64_t>(max_tiles, (int64_t)resident_workgroups<D, ACT>());
-    hipLaunchKernelGGL((bwd_mfma<D, ACT>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)dout,
-                       (const float *)w.lse2, (const float *)w.ndlt, w.ctr,
-                       (const int4 *)w.table, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv);
+    auto main_pass = [&](auto pass_c) {
+        constexpr int PASS = decltype(pass_c)::value;
+        const int64_t grid = std::min<int64_t>(PASS == 2 ? max_tiles : max_tiles / 2,
+                                               (int64_t)resident_workgroups<D, ACT, PASS>());
+        hipLaunchKernelGGL((bwd_mfma<D, ACT, PASS>), dim3((unsigned)std::max<int64_t>(grid, 1)),
+                           dim3(kThreads), 0, st, s, (const bf16 *)q, (const bf16 *)k,
+                           (const bf16 *)v, (const bf16 *)dout, (const bf16 *)out, lse, w.lse2,
+                           w.ndlt, w.ctr, (const int4 *)w.table, (bf16 *)dq, (bf16 *)dk,
+                           (bf16 *)dv);
+    };
+    if constexpr (ACT == kSoftmax) {
+        main_pass(std::integral_constant<int, 0>{});
+        main_pass(std::integral_constant<int, 1>{});
+    } else {
+        main_pass(std::integral_constant<int, 2>{});
+    }
     return hipGetLastError();
 }
 

@@ -130,8 +130,17 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
             if (wave == 0) {
                 const uint8_t *sp = ksc + ks0 + (int64_t)off * (D / 32);
                 const int mis = scale_mis(ci);
-                dma_dwords_lds(sp - mis, (uint32_t)((rows * (D / 32) + mis + 3) & ~3),
-                               lds_addr_of(b + kKC * D), lane);
+                const uint32_t nb = (uint32_t)(rows * (D / 32) + mis);
+                // The dword window ends at most 3 bytes past the chunk's last
+                // scale; only on the last head can that pass the tensor's
+                // end, and then the window is read byte by byte instead.
+                const int64_t wbeg = ks0 + (int64_t)off * (D / 32) - mis;
+                const int64_t total = (int64_t)s.H * s.T * (D / 32);
+                if (wbeg + ((nb + 3) & ~3u) <= total)
+                    dma_dwords_lds(sp - mis, (nb + 3) & ~3u, lds_addr_of(b + kKC * D), lane);
+                else
+                    bytes_to_lds(sp - mis, (uint32_t)(total - wbeg), lds_addr_of(b + kKC * D),
+                                 lane);
             }
         } else {
             dma_tile<D>(row_desc<D>(kb + off * rs, rows, rs), b, voff, wave);

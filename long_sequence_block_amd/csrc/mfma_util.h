@@ -22,7 +22,7 @@ __device__ __forceinline__ int window_start(int row, int B, int W) {
 }
 // One past the last local query that sees local key `key` (queries end at L).
 __device__ __forceinline__ int window_end(int key, int B, int W, int L) {
-    return (int)min((int64_t)(key / B + W) * B, (int64_t)L);
+    return (int)min(((int64_t)(key / B) + W) * B, (int64_t)L);
 }
 
 // Buffer resource over `rows` rows of stride `rs` elements starting at

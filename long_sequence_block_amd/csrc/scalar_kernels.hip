@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kRows) void fwd_scalar(Shape s, const TI *__restric
     const int lane = threadIdx.x;
     const int64_t rs = (int64_t)s.H * D;
     const int row0 = t.blk * s.B + t.sub * kRows;
-    const int row_end = min(row0 + kRows, min(t.blk * s.B + s.B, t.len));
+    const int row_end = min(row0 + kRows, (int)min((int64_t)t.blk * s.B + s.B, (int64_t)t.len));
     const int i = row0 + lane;  // local query row of this lane
     const bool valid = i < row_end;
     const int kstart = max(0, t.blk - s.W + 1) * s.B;
@@ -127,7 +127,7 @@ __device__ void bwd_dq_tile(const Shape &s, const Tile &t, int row0, const TI *_
                             float (*ks)[D + 1], float (*vs)[D + 1]) {
     const int lane = threadIdx.x;
     const int64_t rs = (int64_t)s.H * D;
-    const int row_end = min(row0 + kRows, min(t.blk * s.B + s.B, t.len));
+    const int row_end = min(row0 + kRows, (int)min((int64_t)t.blk * s.B + s.B, (int64_t)t.len));
     const int i = row0 + lane;
     const bool valid = i < row_end;
     const int kstart = max(0, t.blk - s.W + 1) * s.B;
@@ -195,10 +195,10 @@ __device__ void bwd_dkdv_tile(const Shape &s, const Tile &t, int row0,
                               float (*dos)[D + 1], float *ls, float *dls) {
     const int lane = threadIdx.x;
     const int64_t rs = (int64_t)s.H * D;
-    const int row_end = min(row0 + kRows, min(t.blk * s.B + s.B, t.len));
+    const int row_end = min(row0 + kRows, (int)min((int64_t)t.blk * s.B + s.B, (int64_t)t.len));
     const int j = row0 + lane;  // local key row of this lane
     const bool valid = j < row_end;
-    const int qend = (int)min((int64_t)(t.blk + s.W) * s.B, (int64_t)t.len);
+    const int qend = (int)min(((int64_t)t.blk + s.W) * s.B, (int64_t)t.len);
     const float c = s.scale * kLog2e;
 
     float kr[D], vr[D], ak[D], av[D];
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kRows) void bwd_scalar(
 template <typename TI, int D, int ACT>
 hipError_t launch_fwd_act(const Shape &s, const void *q, const void *k, const void *v, void *out,
                           float *lse, hipStream_t st) {
-    const int tpb = (s.B + kRows - 1) / kRows;
+    const int tpb = (int)(((int64_t)s.B + kRows - 1) / kRows);
     const int64_t grid = grid_upper_bound(s.T, s.batch, s.B, tpb, s.H);
     hipLaunchKernelGGL((fwd_scalar<TI, D, ACT>), dim3((unsigned)grid), dim3(kRows), 0, st, s,
                        (const TI *)q, (const TI *)k, (const TI *)v, (TI *)out, lse, tpb);
@@ -301,7 +301,7 @@ template <typename TI, int D, int ACT>
 hipError_t launch_bwd_act(const Shape &s, const void *q, const void *k, const void *v,
                           const void *out, const void *dout, const float *lse, void *dq,
                           void *dk, void *dv, hipStream_t st) {
-    const int tpb = (s.B + kRows - 1) / kRows;
+    const int tpb = (int)(((int64_t)s.B + kRows - 1) / kRows);
     const int64_t grid = grid_upper_bound(s.T, s.batch, s.B, 2 * tpb, s.H);
     hipLaunchKernelGGL((bwd_scalar<TI, D, ACT>), dim3((unsigned)grid), dim3(kRows), 0, st, s,
                        (const TI *)q, (const TI *)k, (const TI *)v, (const TI *)out,

@@ -99,10 +99,19 @@ def mx_codes(wid: int, stream: int, shape) -> np.ndarray:
     return ((sign << 7) | (expo << 3) | mant).astype(np.uint8)
 
 
-def mx_scales(wid: int, stream: int, shape) -> np.ndarray:
-    """Random E8M0 block scales (biased exponents) in 119 .. 121, i.e.
-    2^-8 .. 2^-6: with the codes above, values of magnitude 0.016 .. 3.5."""
-    return rng(wid, stream).integers(119, 122, size=shape, dtype=np.uint8)
+def mx_scales(wid: int, stream: int, shape, lo: int = 119, hi: int = 121) -> np.ndarray:
+    """Random E8M0 block scales (biased exponents) uniform in lo .. hi; the
+    default 119 .. 121 is 2^-8 .. 2^-6, which with the codes above gives
+    values of magnitude 0.016 .. 3.5."""
+    return rng(wid, stream).integers(lo, hi + 1, size=shape, dtype=np.uint8)
+
+
+def mx_codes_all(wid: int, stream: int, shape) -> np.ndarray:
+    """Random E4M3 codes uniform over all 254 finite codes: both zeros, the
+    subnormals (exponent field 0) and every normal exponent up to 448; only
+    the two NaN codes (0x7F, 0xFF) are left out."""
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    return finite[rng(wid, stream).integers(0, finite.size, size=shape)]
 
 
 def normal(wid: int, stream: int, shape) -> np.ndarray:
@@ -228,13 +237,25 @@ def random_case(seed: int, lengths, heads: int, head_dim: int, with_dout=True):
     return out
 
 
-def random_mx_case(seed: int, lengths, heads: int, head_dim: int):
+def random_mx_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
     """Small seeded case with q and k as MXFP8 codes and block scales (the
-    draws of mx_codes / mx_scales) and v as N(0, 1)."""
+    draws of mx_codes / mx_scales) and v as N(0, 1).
+
+    wide = ((q_lo, q_hi), (k_lo, k_hi)): codes from all finite E4M3 codes
+    (mx_codes_all) and block scales uniform in those biased-exponent ranges
+    instead."""
     off = offsets_from_lengths(lengths)
     T = int(off[-1])
     shape, sshape = (T, heads, head_dim), (T, heads, head_dim // 32)
     wid = 2000 + seed
+    if wide is not None:
+        (qlo, qhi), (klo, khi) = wide
+        return {"offsets": off,
+                "q_mx": mx_codes_all(wid, STREAM_QMX, shape),
+                "q_sc": mx_scales(wid, STREAM_QSC, sshape, qlo, qhi),
+                "k_mx": mx_codes_all(wid, STREAM_KMX, shape),
+                "k_sc": mx_scales(wid, STREAM_KSC, sshape, klo, khi),
+                "v": normal(wid, STREAM_V, shape)}
     return {"offsets": off,
             "q_mx": mx_codes(wid, STREAM_QMX, shape), "q_sc": mx_scales(wid, STREAM_QSC, sshape),
             "k_mx": mx_codes(wid, STREAM_KMX, shape), "k_sc": mx_scales(wid, STREAM_KSC, sshape),

@@ -60,6 +60,10 @@ def _load():
     lib.oracle_gdpa_bwd.argtypes = [dp, dp, dp, dp, ip, i32, i64, i32, i32, i32,
                                     i32, f64, i32, dp, dp, dp]
     lib.oracle_gdpa_bwd.restype = ctypes.c_int
+    lib.oracle_gdpa_fwd_abs.argtypes = lib.oracle_gdpa_fwd.argtypes
+    lib.oracle_gdpa_fwd_abs.restype = ctypes.c_int
+    lib.oracle_gdpa_bwd_abs.argtypes = lib.oracle_gdpa_bwd.argtypes
+    lib.oracle_gdpa_bwd_abs.restype = ctypes.c_int
     lib.oracle_pair_count.argtypes = [ip, i32, i32, i32]
     lib.oracle_pair_count.restype = ctypes.c_int64
     lib.oracle_num_threads.argtypes = []
@@ -162,13 +166,16 @@ GDPA_SILU, GDPA_GELU = 1, 2
 
 
 def gdpa_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
-             act: int) -> np.ndarray:
+             act: int, absolute: bool = False) -> np.ndarray:
     """out [T, H, D] fp64 of sum_j act(scale <q_i, k_j>) v_j over the block
-    window (act 1 = SiLU, 2 = GELU)."""
+    window (act 1 = SiLU, 2 = GELU).  absolute=True sums |terms| instead:
+    sum_j |act(.)| |v_j|, the magnitude a per-term rounding error scales
+    with."""
     q, k, v, off = _f64(q), _f64(k), _f64(v), _i32(offsets)
     T, H, D = q.shape
     out = np.zeros((T, H, D), np.float64)
-    rc = _load().oracle_gdpa_fwd(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
+    fn = _load().oracle_gdpa_fwd_abs if absolute else _load().oracle_gdpa_fwd
+    rc = fn(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
                                  int(block_size), int(window_blocks), float(scale), int(act),
                                  _dp(out))
     if rc != 0:
@@ -177,12 +184,14 @@ def gdpa_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float
 
 
 def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale: float,
-             act: int):
-    """(dq, dk, dv) of sum(dout * gdpa_fwd(...)), each [T, H, D] fp64."""
+             act: int, absolute: bool = False):
+    """(dq, dk, dv) of sum(dout * gdpa_fwd(...)), each [T, H, D] fp64.
+    absolute=True sums |terms| instead (|scale| sum_j |dS_ij| |k_j|, ...)."""
     q, k, v, do, off = _f64(q), _f64(k), _f64(v), _f64(dout), _i32(offsets)
     T, H, D = q.shape
     dq, dk, dv = (np.zeros((T, H, D), np.float64) for _ in range(3))
-    rc = _load().oracle_gdpa_bwd(_dp(q), _dp(k), _dp(v), _dp(do), _ip(off), len(off) - 1, T,
+    fn = _load().oracle_gdpa_bwd_abs if absolute else _load().oracle_gdpa_bwd
+    rc = fn(_dp(q), _dp(k), _dp(v), _dp(do), _ip(off), len(off) - 1, T,
                                  H, D, int(block_size), int(window_blocks), float(scale),
                                  int(act), _dp(dq), _dp(dk), _dp(dv))
     if rc != 0:

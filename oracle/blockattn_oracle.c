@@ -66,6 +66,20 @@ static int check_args(const int32_t *offsets, int batch, int64_t T, int H, int D
     return 0;
 }
 
+/* Scratch length for one query's visible scores: at most W * B keys, and
+ * never more than the longest user (so huge B or W cost nothing). */
+static size_t visible_max(const int32_t *offsets, int batch, int B, int W)
+{
+    int64_t lmax = 1;
+    for (int u = 0; u < batch; ++u) {
+        const int64_t L = (int64_t)offsets[u + 1] - offsets[u];
+        if (L > lmax)
+            lmax = L;
+    }
+    const int64_t wb = (int64_t)W * (int64_t)B;
+    return (size_t)(wb < lmax ? wb : lmax);
+}
+
 static double dot(const double *a, const double *b, int D)
 {
     double s = 0.0;
@@ -107,9 +121,10 @@ int oracle_fwd(const double *q, const double *k, const double *v,
     int status = 0;
     const int64_t npairs = (int64_t)batch * H;
     const int64_t rs = (int64_t)H * D; /* token stride */
+    const size_t nvis = visible_max(offsets, batch, B, W);
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)W * (size_t)B);
+        double *s = (double *)malloc(sizeof(double) * nvis);
         if (!s) {
 #pragma omp atomic write
             status = -2;
@@ -165,10 +180,11 @@ int oracle_bwd(const double *q, const double *k, const double *v,
     int status = 0;
     const int64_t npairs = (int64_t)batch * H;
     const int64_t rs = (int64_t)H * D;
+    const size_t nvis = visible_max(offsets, batch, B, W);
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)W * (size_t)B);
-        double *dp = (double *)malloc(sizeof(double) * (size_t)W * (size_t)B);
+        double *s = (double *)malloc(sizeof(double) * nvis);
+        double *dp = (double *)malloc(sizeof(double) * nvis);
         if (!s || !dp) {
 #pragma omp atomic write
             status = -2;
@@ -301,9 +317,12 @@ static double act_slope(int act, double x)
     return cdf + x * pdf;
 }
 
-int oracle_gdpa_fwd(const double *q, const double *k, const double *v,
-                    const int32_t *offsets, int batch, int64_t T, int H, int D,
-                    int B, int W, double scale, int act, double *out)
+/* The forward sum, or (absolute != 0) the same sum of absolute terms,
+ * sum_j |P_ij| |v_j|: the magnitude a rounding error of each term is
+ * relative to, which the GPU parity tests scale their bound by. */
+static int gdpa_fwd_sum(const double *q, const double *k, const double *v,
+                        const int32_t *offsets, int batch, int64_t T, int H, int D,
+                        int B, int W, double scale, int act, int absolute, double *out)
 {
     if (check_args(offsets, batch, T, H, D, B, W) || (act != 1 && act != 2))
         return -1;
@@ -324,17 +343,34 @@ int oracle_gdpa_fwd(const double *q, const double *k, const double *v,
                 const double *vj = v + (t0 + j) * rs + (int64_t)h * D;
                 const double pij = act_value(act, scale * dot(qi, kj, D));
                 for (int d = 0; d < D; ++d)
-                    oi[d] += pij * vj[d];
+                    oi[d] += absolute ? fabs(pij) * fabs(vj[d]) : pij * vj[d];
             }
         }
     }
     return 0;
 }
 
-int oracle_gdpa_bwd(const double *q, const double *k, const double *v,
-                    const double *dout, const int32_t *offsets, int batch,
-                    int64_t T, int H, int D, int B, int W, double scale, int act,
-                    double *dq, double *dk, double *dv)
+int oracle_gdpa_fwd(const double *q, const double *k, const double *v,
+                    const int32_t *offsets, int batch, int64_t T, int H, int D,
+                    int B, int W, double scale, int act, double *out)
+{
+    return gdpa_fwd_sum(q, k, v, offsets, batch, T, H, D, B, W, scale, act, 0, out);
+}
+
+int oracle_gdpa_fwd_abs(const double *q, const double *k, const double *v,
+                        const int32_t *offsets, int batch, int64_t T, int H, int D,
+                        int B, int W, double scale, int act, double *out)
+{
+    return gdpa_fwd_sum(q, k, v, offsets, batch, T, H, D, B, W, scale, act, 1, out);
+}
+
+/* The backward sums, or (absolute != 0) the same sums of absolute terms:
+ * |scale| sum_j |dS_ij| |k_j|, |scale| sum_i |dS_ij| |q_i| and
+ * sum_i |P_ij| |dO_i|. */
+static int gdpa_bwd_sum(const double *q, const double *k, const double *v,
+                        const double *dout, const int32_t *offsets, int batch,
+                        int64_t T, int H, int D, int B, int W, double scale, int act,
+                        int absolute, double *dq, double *dk, double *dv)
 {
     if (check_args(offsets, batch, T, H, D, B, W) || (act != 1 && act != 2))
         return -1;
@@ -360,12 +396,36 @@ int oracle_gdpa_bwd(const double *q, const double *k, const double *v,
                 const double pij = act_value(act, x);
                 const double ds = act_slope(act, x) * dot(doi, v + oj, D);
                 for (int d = 0; d < D; ++d) {
-                    dqi[d] += scale * ds * k[oj + d];
-                    dk[oj + d] += scale * ds * qi[d];
-                    dv[oj + d] += pij * doi[d];
+                    if (absolute) {
+                        dqi[d] += fabs(scale * ds) * fabs(k[oj + d]);
+                        dk[oj + d] += fabs(scale * ds) * fabs(qi[d]);
+                        dv[oj + d] += fabs(pij) * fabs(doi[d]);
+                    } else {
+                        dqi[d] += scale * ds * k[oj + d];
+                        dk[oj + d] += scale * ds * qi[d];
+                        dv[oj + d] += pij * doi[d];
+                    }
                 }
             }
         }
     }
     return 0;
+}
+
+int oracle_gdpa_bwd(const double *q, const double *k, const double *v,
+                    const double *dout, const int32_t *offsets, int batch,
+                    int64_t T, int H, int D, int B, int W, double scale, int act,
+                    double *dq, double *dk, double *dv)
+{
+    return gdpa_bwd_sum(q, k, v, dout, offsets, batch, T, H, D, B, W, scale, act, 0, dq,
+                        dk, dv);
+}
+
+int oracle_gdpa_bwd_abs(const double *q, const double *k, const double *v,
+                        const double *dout, const int32_t *offsets, int batch,
+                        int64_t T, int H, int D, int B, int W, double scale, int act,
+                        double *dq, double *dk, double *dv)
+{
+    return gdpa_bwd_sum(q, k, v, dout, offsets, batch, T, H, D, B, W, scale, act, 1, dq,
+                        dk, dv);
 }

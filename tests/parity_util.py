@@ -2,10 +2,20 @@
 HIP path through the C ABI binding, and check it against the fp64 oracle.
 
 Tolerances (from the arithmetic and the stated targets):
-* bf16 workloads: O, dQ, dK, dV max |gpu - oracle| <= 2e-2 and mean <= 2e-3;
-  lse max |gpu - oracle| <= 1e-3.  The oracle sees the bf16-rounded inputs.
+* bf16 workloads: O, dQ, dK, dV per element |gpu - oracle| <= 2e-2 of
+  arithmetic error plus the rounding of the result to the bf16 output
+  format, 2^-8 |oracle| (a correctly rounded bf16 value can sit that far from
+  the exact one: 1/64 for values in [4, 8), 1/32 in [8, 16), so a plain 2e-2
+  cannot hold for outputs of magnitude 8 and up); mean |gpu - oracle| <= 2e-3
+  over each whole tensor; lse max <= 1e-3.  The oracle sees the bf16-rounded
+  inputs.
 * fp32 workloads: normwise ||gpu - oracle||_inf / ||oracle||_inf <= 1e-5 for
-  every output.
+  every output tensor.
+
+Full-size workloads are compared on every element too: the GPU runs the
+whole workload once, in the launch configuration the benchmark times, and the
+oracle recomputes it in contiguous user ranges (users are independent, so a
+range re-based to its first token is an exact sub-problem).
 """
 from __future__ import annotations
 
@@ -16,11 +26,7 @@ import long_sequence_block_amd as lsb
 import oracle
 
 BF16_MAX, BF16_MEAN, LSE_MAX, FP32_REL = 2e-2, 2e-3, 1e-3, 1e-5
-# GDPA (activation scores, no normalisation): outputs are not bounded by the
-# values' magnitude as a softmax average is, so the bf16 bounds scale with
-# the reference: max |err| <= 1e-2 max|ref|, mean |err| <= 1e-3 max|ref|
-# (the ratio of the softmax bounds to those outputs' magnitude, about 2-4)
-GDPA_MAX, GDPA_MEAN = 1e-2, 1e-3
+BF16_ROUND = 2.0 ** -8  # bound of round-to-nearest-even to bf16, relative
 
 
 def to_device(case: dict, dtype: str, device="cuda"):
@@ -39,6 +45,34 @@ def to_device(case: dict, dtype: str, device="cuda"):
     return dev, host
 
 
+def to_device_lazy(case: dict, dtype: str, device="cuda"):
+    """Like to_device, but the host side keeps the rounded values in their
+    storage dtype (torch CPU tensors); chunks are widened to fp64 on demand
+    (see host_rows).  For workloads whose fp64 copies would be large."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev, host = {}, {}
+    for key, val in case.items():
+        if key == "offsets":
+            dev[key] = torch.from_numpy(np.ascontiguousarray(val)).to(device)
+            host[key] = np.asarray(val, np.int32)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(val)).to(tdt)
+            host[key] = t
+            dev[key] = t.to(device)
+    return dev, host
+
+
+def host_rows(x, t0: int, t1: int) -> np.ndarray:
+    """Token rows [t0, t1) of a host tensor as contiguous fp64 (integer
+    arrays, such as MXFP8 codes and scales, keep their dtype)."""
+    if isinstance(x, torch.Tensor):
+        return x[t0:t1].to(torch.float64).numpy()
+    x = np.asarray(x)
+    if np.issubdtype(x.dtype, np.integer):
+        return np.ascontiguousarray(x[t0:t1])
+    return np.ascontiguousarray(x[t0:t1], dtype=np.float64)
+
+
 def run_fwd(dev, B, W, scale):
     out, lse = lsb.fwd(dev["q"], dev["k"], dev["v"], dev["offsets"], B, W, scale)
     return out, lse
@@ -53,45 +87,202 @@ def np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def assert_close(name, got, ref, dtype, is_lse=False, ulp_slack=False):
-    """The stated bounds.  ulp_slack (bf16 only) adds one bf16 ulp of the
-    reference value (2^-7 relative) to the per-element bound, for stress
-    cases whose gradients carry near-one-hot weights: there the backward's
-    delta comes from the forward's bf16 O, and dS = P (dP - delta) passes that
-    rounding on at full size."""
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    if got.size == 0:
-        return
-    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    err = np.abs(got - ref)
-    if dtype == "fp32":
-        rel = err.max() / max(np.abs(ref).max(), 1e-30)
-        assert rel <= FP32_REL, f"{name}: normwise rel err {rel:.3e} > {FP32_REL}"
-    elif is_lse:
-        assert err.max() <= LSE_MAX, f"{name}: max abs err {err.max():.3e} > {LSE_MAX}"
-    else:
-        bound = BF16_MAX + (np.abs(ref) * 2.0 ** -7 if ulp_slack else 0.0)
-        worst = (err - bound).max()
-        assert worst <= 0, f"{name}: max abs err {err.max():.3e} exceeds its bound by {worst:.3e}"
-        assert err.mean() <= BF16_MEAN, f"{name}: mean abs err {err.mean():.3e} > {BF16_MEAN}"
+class Parity:
+    """Accumulates the comparison of several output tensors, each possibly
+    added in pieces (user ranges): per-element bounds are checked as pieces
+    arrive, whole-tensor bounds (the bf16 mean, the fp32 normwise ratio) at
+    finish().  Every element of every piece is compared."""
+
+    def __init__(self, dtype: str):
+        self.dtype = dtype
+        self.acc = {}
+
+    def add(self, name, got, ref, is_lse=False, tag="", extra=None):
+        """extra: an additional per-element allowance (broadcast against ref)
+        for a stated error source outside the bf16 arithmetic, such as the
+        reduced-precision sums of the block-scaled fp8 products."""
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, (name, tag, got.shape, ref.shape)
+        a = self.acc.setdefault(name, {"n": 0, "sum": 0.0, "max": 0.0, "refmax": 0.0,
+                                       "arith": 0.0, "lse": is_lse})
+        if got.size == 0:
+            return
+        assert np.all(np.isfinite(got)), f"{name} {tag}: non-finite values"
+        err = np.abs(got - ref)
+        emax = float(err.max())
+        a["n"] += err.size
+        a["sum"] += float(err.sum())
+        a["max"] = max(a["max"], emax)
+        a["refmax"] = max(a["refmax"], float(np.abs(ref).max()))
+        if self.dtype == "fp32":
+            return  # normwise: needs the whole tensor's reference magnitude
+        if extra is not None:
+            err = err - np.broadcast_to(np.asarray(extra, np.float64), err.shape)
+            emax = float(err.max())
+        if is_lse:
+            assert emax <= LSE_MAX, f"{name} {tag}: max abs err {emax:.3e} > {LSE_MAX}"
+        else:
+            # the error beyond the output format's own rounding
+            arith = err - BF16_ROUND * np.abs(ref)
+            worst = int(np.argmax(arith))
+            a["arith"] = max(a["arith"], float(arith.flat[worst]))
+            assert arith.flat[worst] <= BF16_MAX, (
+                f"{name} {tag}: err {err.flat[worst]:.3e} at ref {ref.flat[worst]:.3e} exceeds "
+                f"{BF16_MAX} + 2^-8 |ref| by {arith.flat[worst] - BF16_MAX:.3e}")
+
+    def finish(self):
+        for name, a in self.acc.items():
+            if a["n"] == 0:
+                continue
+            if self.dtype == "fp32":
+                rel = a["max"] / max(a["refmax"], 1e-30)
+                assert rel <= FP32_REL, f"{name}: normwise rel err {rel:.3e} > {FP32_REL}"
+            elif not a["lse"]:
+                mean = a["sum"] / a["n"]
+                assert mean <= BF16_MEAN, f"{name}: mean abs err {mean:.3e} > {BF16_MEAN}"
+
+    def summary(self) -> str:
+        return ", ".join(f"{n} max {a['max']:.2e} (beyond rounding {a['arith']:.2e}) "
+                         f"mean {a['sum'] / max(a['n'], 1):.1e}"
+                         for n, a in self.acc.items())
 
 
-def check_full(case, dtype, B, W, scale, backward=True, ulp_slack=False):
+# Generalized dot-product attention (activation scores, no normalisation):
+# each output is an unnormalised sum of terms whose magnitudes are unrelated
+# to the output's own size, so its bound is per element and scaled by
+# A = the same sum over |terms| (oracle.gdpa_fwd/gdpa_bwd with absolute=True).
+# The GPU rounds each term's weight (P, or dS) to bf16 before the matrix
+# product, error <= 2^-8 |weight|, accumulates in fp32 and rounds the result
+# to bf16, error <= 2^-8 |result|: |gpu - ref| <= 2^-8 (A + |ref|), plus fp32
+# rounding of the scores and activations (GDPA_ATOL).  The mean over a
+# tensor is held to a quarter of that bound's mean (rounding errors of many
+# terms do not all align).
+GDPA_REL, GDPA_ATOL, GDPA_MEAN_FRAC = 2.0 ** -8, 1e-5, 0.25
+
+
+class GdpaParity:
+    """Like Parity, with the GDPA bounds above for bf16 and the normwise
+    FP32_REL for fp32 outputs."""
+
+    def __init__(self, dtype: str):
+        self.dtype = dtype
+        self.acc = {}
+
+    def add(self, name, got, ref, mag, tag=""):
+        got, ref, mag = (np.asarray(x, np.float64) for x in (got, ref, mag))
+        assert got.shape == ref.shape == mag.shape, (name, tag, got.shape, ref.shape)
+        a = self.acc.setdefault(name, {"n": 0, "sum": 0.0, "bsum": 0.0, "max": 0.0,
+                                       "refmax": 0.0, "ratio": 0.0})
+        if got.size == 0:
+            return
+        assert np.all(np.isfinite(got)), f"{name} {tag}: non-finite values"
+        err = np.abs(got - ref)
+        bound = GDPA_REL * (mag + np.abs(ref)) + GDPA_ATOL
+        a["n"] += err.size
+        a["sum"] += float(err.sum())
+        a["bsum"] += float(bound.sum())
+        a["max"] = max(a["max"], float(err.max()))
+        a["refmax"] = max(a["refmax"], float(np.abs(ref).max()))
+        a["ratio"] = max(a["ratio"], float((err / bound).max()))
+        if self.dtype == "bf16":
+            worst = int(np.argmax(err - bound))
+            assert err.flat[worst] <= bound.flat[worst], (
+                f"{name} {tag}: err {err.flat[worst]:.3e} > bound {bound.flat[worst]:.3e} "
+                f"(ref {ref.flat[worst]:.3e}, |terms| {mag.flat[worst]:.3e})")
+
+    def finish(self):
+        for name, a in self.acc.items():
+            if a["n"] == 0:
+                continue
+            if self.dtype == "fp32":
+                rel = a["max"] / max(a["refmax"], 1e-30)
+                assert rel <= FP32_REL, f"{name}: normwise rel err {rel:.3e} > {FP32_REL}"
+            else:
+                assert a["sum"] <= GDPA_MEAN_FRAC * a["bsum"], (
+                    f"{name}: mean err {a['sum'] / a['n']:.3e} > {GDPA_MEAN_FRAC} x mean bound "
+                    f"{a['bsum'] / a['n']:.3e}")
+
+    def summary(self) -> str:
+        return ", ".join(f"{n} max {a['max']:.2e} max err/bound {a['ratio']:.2f} "
+                         f"mean err/bound {a['sum'] / max(a['bsum'], 1e-300):.3f}"
+                         for n, a in self.acc.items())
+
+
+def assert_close(name, got, ref, dtype, is_lse=False):
+    """The stated bounds on one whole tensor."""
+    p = Parity(dtype)
+    p.add(name, got, ref, is_lse=is_lse)
+    p.finish()
+
+
+def check_full(case, dtype, B, W, scale, backward=True):
     """Whole-case parity: every output element against the oracle."""
     dev, host = to_device(case, dtype)
     out, lse = run_fwd(dev, B, W, scale)
     o_ref, l_ref = oracle.fwd(host["q"], host["k"], host["v"], host["offsets"], B, W, scale)
-    assert_close("out", np64(out), o_ref, dtype)
-    assert_close("lse", np64(lse), l_ref, dtype, is_lse=True)
+    p = Parity(dtype)
+    p.add("out", np64(out), o_ref)
+    p.add("lse", np64(lse), l_ref, is_lse=True)
     if backward:
         dq, dk, dv = run_bwd(dev, out, lse, B, W, scale)
         r = oracle.bwd(host["q"], host["k"], host["v"], host["dout"], host["offsets"], B, W,
                        scale)
         for name, g, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), r):
-            assert_close(name, np64(g), ref, dtype, ulp_slack=ulp_slack)
+            p.add(name, np64(g), ref)
     torch.cuda.synchronize()
+    p.finish()
+    return p
+
+
+def user_ranges(offsets, max_tokens: int):
+    """Contiguous user ranges [u0, u1) holding at most max_tokens tokens each
+    (a single longer user gets a range of its own)."""
+    off = np.asarray(offsets, np.int64)
+    batch = len(off) - 1
+    u0 = 0
+    while u0 < batch:
+        u1 = u0 + 1
+        while u1 < batch and off[u1 + 1] - off[u0] <= max_tokens:
+            u1 += 1
+        yield u0, u1
+        u0 = u1
+
+
+def compare_by_users(host, gpu, offsets, reference, dtype, max_tokens, log=None):
+    """(reference may also return, under "extra:<name>", a per-element
+    allowance for output <name>; see Parity.add.)"""
+    return _compare_by_users(host, gpu, offsets, reference, dtype, max_tokens, log)
+
+
+def _compare_by_users(host, gpu, offsets, reference, dtype, max_tokens, log=None):
+    """Every element of the GPU outputs against the oracle, user range by
+    user range.
+
+    host: the inputs (host tensors or arrays, [T, H, D]); gpu: name -> GPU
+    output already copied to the host ([T, H, D], or [H, T] for names that
+    start with "lse"); reference(sub, rows) -> name -> oracle output of the
+    range, given sub = {input name: fp64 rows of the range, "offsets": the
+    re-based offsets}."""
+    off = np.asarray(offsets, np.int64)
+    p = Parity(dtype)
+    for u0, u1 in user_ranges(off, max_tokens):
+        t0, t1 = int(off[u0]), int(off[u1])
+        if t1 == t0:
+            continue
+        sub = {k: host_rows(v, t0, t1) for k, v in host.items() if k != "offsets"}
+        sub["offsets"] = (off[u0:u1 + 1] - t0).astype(np.int32)
+        ref = reference(sub)
+        for name, g in gpu.items():
+            is_lse = name.startswith("lse")
+            got = g[:, t0:t1] if is_lse else g[t0:t1]
+            got = got.to(torch.float64).numpy() if isinstance(got, torch.Tensor) else got
+            p.add(name, got, ref[name], is_lse=is_lse, tag=f"users [{u0},{u1})",
+                  extra=ref.get("extra:" + name))
+        if log is not None:
+            log(f"  users [{u0},{u1}) tokens [{t0},{t1}): {p.summary()}")
+    p.finish()
+    return p
 
 
 def row_slice(L: int, a: int, b: int, B: int, W: int):
@@ -106,48 +297,3 @@ def row_slice(L: int, a: int, b: int, B: int, W: int):
     s0 = max(0, a // B - W + 1) * B
     e = min(L, ((b - 1) // B + W) * B)
     return s0, e
-
-
-def check_sampled(dev, host, out, lse, grads, B, W, scale, dtype, samples):
-    """Parity on sampled rows: samples = [(user, a, b)] local row ranges.
-    The oracle runs on the slice of the user that those rows depend on."""
-    off = host["offsets"]
-    o_g, l_g = np64(out), np64(lse)
-    g_g = [np64(g) for g in grads] if grads is not None else None
-    for (u, a, b) in samples:
-        t0, L = int(off[u]), int(off[u + 1] - off[u])
-        a, b = min(a, L), min(b, L)
-        if a >= b:
-            continue
-        s0, e = row_slice(L, a, b, B, W)
-        sl = slice(t0 + s0, t0 + e)
-        rows = slice(t0 + a, t0 + b)
-        loc = slice(a - s0, b - s0)
-        o_r, l_r = oracle.fwd(host["q"][sl], host["k"][sl], host["v"][sl],
-                              [0, e - s0], B, W, scale)
-        tag = f"user {u} rows [{a},{b})"
-        assert_close(f"out {tag}", o_g[rows], o_r[loc], dtype)
-        assert_close(f"lse {tag}", l_g[:, rows], l_r[:, loc], dtype, is_lse=True)
-        if g_g is not None:
-            r = oracle.bwd(host["q"][sl], host["k"][sl], host["v"][sl], host["dout"][sl],
-                           [0, e - s0], B, W, scale)
-            for name, g, ref in zip(("dq", "dk", "dv"), g_g, r):
-                assert_close(f"{name} {tag}", g[rows], ref[loc], dtype)
-
-
-def assert_close_scaled(name, got, ref, dtype):
-    """The GDPA bounds (see GDPA_MAX): relative to the largest reference
-    magnitude for bf16, normwise FP32_REL for fp32."""
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    if got.size == 0:
-        return
-    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    err = np.abs(got - ref)
-    mag = max(np.abs(ref).max(), 1e-30)
-    if dtype == "fp32":
-        assert err.max() / mag <= FP32_REL, f"{name}: normwise rel err {err.max() / mag:.3e}"
-        return
-    assert err.max() <= GDPA_MAX * mag, f"{name}: max err {err.max():.3e} vs {GDPA_MAX * mag:.3e}"
-    assert err.mean() <= GDPA_MEAN * mag, f"{name}: mean err {err.mean():.3e} vs {GDPA_MEAN * mag:.3e}"

@@ -64,6 +64,13 @@ def fwd_status(**kw):
     (dict(head_dim=48), binding.ERR_UNSUPPORTED),
     (dict(head_dim=256), binding.ERR_UNSUPPORTED),
     (dict(total_tokens=2**31, batch=1), binding.ERR_UNSUPPORTED),
+    (dict(total_tokens=2**31 - 1000, batch=1), binding.ERR_UNSUPPORTED),
+    # 128 rows of H * D elements must span less than 4 GiB (32-bit offsets)
+    (dict(num_heads=200000, head_dim=128), binding.ERR_UNSUPPORTED),
+    (dict(num_heads=2**31 - 1, head_dim=32), binding.ERR_UNSUPPORTED),
+    # huge B and W are valid (clamped to T and ceil(T/B) without changing
+    # the result); an empty call with them returns OK without launching
+    (dict(block_size=2**31 - 1, window_blocks=2**31 - 1, total_tokens=0, q=None), binding.OK),
     (dict(q=None), binding.ERR_INVALID_ARGUMENT),
     (dict(lse=None), binding.ERR_INVALID_ARGUMENT),
     (dict(offsets=None), binding.ERR_INVALID_ARGUMENT),
@@ -88,6 +95,7 @@ def bwd_status(**kw):
     (dict(dout=None), binding.ERR_INVALID_ARGUMENT),
     (dict(dv=FAKE + 4), binding.ERR_INVALID_ARGUMENT),
     (dict(head_dim=16), binding.ERR_UNSUPPORTED),
+    (dict(num_heads=200000, head_dim=128), binding.ERR_UNSUPPORTED),
     (dict(total_tokens=0, q=None, workspace=None), binding.OK),
 ])
 def test_bwd_argument_checks(kw, code):
@@ -160,9 +168,7 @@ def test_mx_argument_checks():
              total_tokens=100, num_heads=2, head_dim=32, block_size=64, window_blocks=2,
              scale=0.125, out=FAKE, lse=FAKE, stream=None)
     assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_UNSUPPORTED    # D = 32
-    a.update(head_dim=64, total_tokens=101, num_heads=1)
-    assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_UNSUPPORTED    # 202 scale bytes
-    a.update(total_tokens=100, num_heads=2, k_scale=FAKE + 2)
+    a.update(head_dim=64, k_scale=FAKE + 2)
     assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
     a.update(k_scale=FAKE, q=None)
     assert lsb.blockattn_mx_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT

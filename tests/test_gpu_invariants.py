@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import long_sequence_block_amd as lsb
 from long_sequence_block_amd import workloads as wl
 from parity_util import run_bwd, run_fwd, to_device
 
@@ -148,3 +149,30 @@ def test_gdpa_locality_outside_window():
     torch.cuda.synchronize()
     assert torch.equal(o1[448:], o2[448:])
     assert not torch.equal(o1[:448], o2[:448])
+
+
+def test_side_stream_calls_match_current_stream():
+    """fwd and bwd issued on a side stream (outputs and workspace allocated by
+    the binding on that stream) give the same bits as on the current stream,
+    while the current stream keeps allocating and writing memory of the
+    workspace's size: a workspace handed back to the allocator too early
+    would be overwritten under the backward's kernels."""
+    print("side stream", flush=True)
+    case = wl.random_case(41, [900, 33, 2000, 129], 4, 64)
+    dev, _ = to_device(case, "bf16")
+    ref = _run(case, "bf16", 128, 2)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out, lse = lsb.fwd(dev["q"], dev["k"], dev["v"], dev["offsets"], 128, 2, 0.125, stream=side)
+    grads = lsb.bwd(dev["q"], dev["k"], dev["v"], out, dev["dout"], lse, dev["offsets"], 128, 2,
+                    0.125, stream=side)
+    T, H, _ = case["q"].shape
+    n = lsb.blockattn_bwd_workspace_size(T, len(case["offsets"]) - 1, H, lsb.BF16)
+    for i in range(64):  # churn on the current stream meanwhile
+        junk = torch.empty(n, dtype=torch.uint8, device="cuda")
+        junk.fill_(i)
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for x, y in zip(ref, [out, lse, *grads]):
+        assert torch.equal(x, y.cpu())

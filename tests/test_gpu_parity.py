@@ -1,11 +1,10 @@
 """GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
 
-Small cases are compared element by element over every output; the five
-workloads are run at their full sizes in the launch configuration the
-benchmark times and compared on sampled rows that the oracle recomputes from
-the slice of the user they depend on (tests/parity_util.py: row_slice).
+Every output element is compared, in small cases and in the workloads at
+their full sizes.  The full-size workloads run on the GPU in the launch
+configuration the benchmark times; the oracle recomputes them in contiguous
+user ranges (tests/parity_util.py: compare_by_users).
 """
-import dataclasses
 import math
 
 import numpy as np
@@ -15,8 +14,8 @@ import torch
 import oracle
 from long_sequence_block_amd import workloads as wl
 import long_sequence_block_amd as lsb
-from parity_util import (assert_close, check_full, check_sampled, np64, run_bwd, run_fwd,
-                         to_device)
+from parity_util import (assert_close, check_full, compare_by_users, np64, run_bwd, run_fwd,
+                         to_device, to_device_lazy)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +44,11 @@ SMALL = [
     ([600, 5], 1, 128, 100, 2, "bf16"),
     ([513, 20], 2, 64, 300, 1, "bf16"),
     ([77, 130], 2, 32, 5, 4, "fp32"),
+    # the largest block and window the ABI takes: one block per user, every
+    # earlier key visible (the library clamps B to T and W to ceil(T/B))
+    ([300, 77, 0, 5], 2, 64, 2**31 - 1, 2**31 - 1, "bf16"),
+    ([100, 37], 1, 32, 2**31 - 1, 2**31 - 1, "fp32"),
+    ([260, 1000], 1, 128, 64, 2**31 - 1, "bf16"),
 ]
 
 
@@ -108,14 +112,15 @@ def test_negative_scale_every_element(idx):
 
 def test_many_users_every_element():
     """1500 users of 0-40 tokens: the backward's tile-index scan runs over
-    several 1024-user passes, and most tiles are one-chunk tiles.  Windows
-    this short give near-one-hot weights, so the gradients are checked with
-    one bf16 ulp of slack (parity_util.assert_close)."""
+    several 1024-user passes, most tiles are one-chunk tiles, and windows this
+    short give near-one-hot weights, the hardest case for the gradients'
+    precision."""
     rng = np.random.default_rng(77)
     lengths = [int(x) for x in rng.integers(0, 41, 1500)]
     _print(f"many users: {len(lengths)} users, T={sum(lengths)}")
     case = wl.random_case(601, lengths, 2, 64)
-    check_full(case, "bf16", 32, 2, 0.125, backward=True, ulp_slack=True)
+    p = check_full(case, "bf16", 32, 2, 0.125, backward=True)
+    _print("  " + p.summary())
 
 
 def test_empty_inputs():
@@ -137,55 +142,59 @@ def test_tiny_fp32_workload_full():
     check_full(case, "fp32", w.block_size, w.window_blocks, w.scale, backward=True)
 
 
-def _samples(off, B, rng, n_users=6):
-    """Sampled row ranges: first, last and random users, plus block edges."""
-    batch = len(off) - 1
-    users = sorted(set([0, batch - 1, int(np.argmax(np.diff(off)))] +
-                       list(rng.integers(0, batch, n_users))))
-    out = []
-    for u in users:
-        L = int(off[u + 1] - off[u])
-        out.append((u, 0, min(L, 2 * B)))                    # start of the user
-        out.append((u, max(0, L - B - 5), L))                # ragged tail
-        if L > 4 * B:
-            a = int(rng.integers(B, L - 2 * B))
-            out.append((u, a, a + B + 3))                    # interior, unaligned
-    return out
-
-
-@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 11])
-def test_workload_full_size_sampled(wid):
-    w = wl.WORKLOADS[wid]
-    _print(f"workload {wid} ({w.name}) full size, sampled rows")
+def full_size_every_element(w, max_tokens):
+    """The whole workload on the GPU in the launch configuration bench.py
+    times, then every element of out, lse (and dq, dk, dv) against the
+    oracle, recomputed in user ranges of at most max_tokens tokens."""
     case = wl.draw(w)
-    dev, host = to_device(case, w.dtype)
+    dev, host = to_device_lazy(case, w.dtype)
     del case
-    out, lse = run_fwd(dev, w.block_size, w.window_blocks, w.scale)
-    grads = run_bwd(dev, out, lse, w.block_size, w.window_blocks, w.scale) if w.backward else None
+    B, W, sc = w.block_size, w.window_blocks, w.scale
+    out, lse = run_fwd(dev, B, W, sc)
+    gpu = {"out": out.cpu(), "lse": lse.cpu()}
+    if w.backward:
+        dq, dk, dv = run_bwd(dev, out, lse, B, W, sc)
+        gpu.update(dq=dq.cpu(), dk=dk.cpu(), dv=dv.cpu())
+        del dq, dk, dv
     torch.cuda.synchronize()
-    rng = np.random.default_rng(wid)
-    samples = _samples(host["offsets"], w.block_size, rng)
-    check_sampled(dev, host, out, lse, grads, w.block_size, w.window_blocks, w.scale,
-                  w.dtype, samples)
-    # every row written: no NaN/garbage anywhere in the outputs
-    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
-    if grads is not None:
-        for g in grads:
-            assert torch.isfinite(g).all().item()
+    del dev, out, lse
+
+    def reference(sub):
+        o, l = oracle.fwd(sub["q"], sub["k"], sub["v"], sub["offsets"], B, W, sc)
+        r = {"out": o, "lse": l}
+        if w.backward:
+            r["dq"], r["dk"], r["dv"] = oracle.bwd(sub["q"], sub["k"], sub["v"], sub["dout"],
+                                                   sub["offsets"], B, W, sc)
+        return r
+
+    p = compare_by_users(host, gpu, host["offsets"], reference, w.dtype, max_tokens, log=_print)
+    _print("  " + p.summary())
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid", [2, 3, 5, 6])
+def test_workload_full_size_every_element(wid):
+    w = wl.WORKLOADS[wid]
+    _print(f"workload {wid} ({w.name}) full size, every element")
+    full_size_every_element(w, max_tokens=1 << 30)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid", [4, 11])
+def test_long_context_full_size_every_element(wid):
+    """32 users of 16384 tokens (1 GiB per tensor): the oracle recomputes
+    four users at a time."""
+    w = wl.WORKLOADS[wid]
+    _print(f"workload {wid} ({w.name}) full size, every element in 4-user ranges")
+    full_size_every_element(w, max_tokens=4 * w.fixed_length)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("L", [2048, 4096, 8192])
-def test_long_context_sweep_sampled(L):
+def test_long_context_sweep_every_element(L):
     w = wl.long_context(L)
-    _print(f"long-context sweep L={L}, sampled rows")
-    w = dataclasses.replace(w, users=4)
-    case = wl.draw(w)
-    dev, host = to_device(case, w.dtype)
-    out, lse = run_fwd(dev, w.block_size, w.window_blocks, w.scale)
-    torch.cuda.synchronize()
-    samples = [(u, a, a + 300) for u in range(4) for a in (0, L // 2 - 7, L - 300)]
-    check_sampled(dev, host, out, lse, None, w.block_size, w.window_blocks, w.scale,
-                  w.dtype, samples)
+    _print(f"long-context sweep L={L}, all 32 users, every element")
+    full_size_every_element(w, max_tokens=max(8 * L, 65536))
 
 
 def test_lse_pin_zero_queries():
