@@ -636,3 +636,102 @@ def test_mx_workload_draws():
     v = np.abs(oracle.mx_decode(c["q_mx"], np.full(c["q_sc"].shape, 127, np.uint8)))
     assert np.all(np.isfinite(v)) and v.min() >= 4 and v.max() <= 448
     assert set(np.unique(c["k_sc"])) <= {119, 120, 121}
+
+
+def test_gdpa_absolute_sums_against_torch():
+    """The oracle's sums of |terms| (the magnitude the GPU parity bounds of
+    GDPA scale with) against the same dense torch reference with every term
+    made non-negative: |act(s)| |v| forward; |scale act'(s) dP| |k|,
+    |scale act'(s) dP| |q| and |act(s)| |dO| backward, with dP = dO . v."""
+    lengths = [0, 1, 9, 23]
+    c = case(640, lengths, H=2, D=6)
+    off = c["offsets"]
+    for act in (1, 2):
+        for B, W, sc in ((4, 2, 0.55), (1, 5, -0.8)):
+            out = oracle.gdpa_fwd(c["q"], c["k"], c["v"], off, B, W, sc, act, absolute=True)
+            g = oracle.gdpa_bwd(c["q"], c["k"], c["v"], c["dout"], off, B, W, sc, act,
+                                absolute=True)
+            for u, L in enumerate(lengths):
+                a, b = off[u], off[u + 1]
+                if L == 0:
+                    continue
+                q, k, v, do = (torch.from_numpy(c[n][a:b].copy()) for n in ("q", "k", "v", "dout"))
+                s = torch.einsum("ihd,jhd->hij", q, k) * sc
+                m = torch.from_numpy(visible_mask(L, B, W))[None]
+                if act == 1:
+                    p, slope = torch.nn.functional.silu(s), torch.sigmoid(s) * (1 + s * (1 - torch.sigmoid(s)))
+                else:
+                    cdf = 0.5 * (1 + torch.erf(s / math.sqrt(2)))
+                    p = s * cdf
+                    slope = cdf + s * torch.exp(-0.5 * s * s) / math.sqrt(2 * math.pi)
+                p = torch.where(m, p, torch.zeros_like(p)).abs()
+                dp = torch.einsum("ihd,jhd->hij", do, v)
+                ds = torch.where(m, (sc * slope * dp).abs(), torch.zeros_like(s))
+                np.testing.assert_allclose(out[a:b], torch.einsum("hij,jhd->ihd", p, v.abs()).numpy(),
+                                           atol=1e-12, rtol=1e-12)
+                np.testing.assert_allclose(g[0][a:b], torch.einsum("hij,jhd->ihd", ds, k.abs()).numpy(),
+                                           atol=1e-12, rtol=1e-12)
+                np.testing.assert_allclose(g[1][a:b], torch.einsum("hij,ihd->jhd", ds, q.abs()).numpy(),
+                                           atol=1e-12, rtol=1e-12)
+                np.testing.assert_allclose(g[2][a:b], torch.einsum("hij,ihd->jhd", p, do.abs()).numpy(),
+                                           atol=1e-12, rtol=1e-12)
+
+
+def test_gdpa_absolute_sums_bound_the_sums():
+    """Triangle inequality: every plain sum is at most its sum of |terms|,
+    and the two agree where every term is non-negative (q = k with positive
+    entries and scale > 0 make every score, activation and slope positive;
+    v, dO positive)."""
+    c = case(641, [30, 17], H=2, D=5)
+    off = c["offsets"]
+    for act in (1, 2):
+        o = oracle.gdpa_fwd(c["q"], c["k"], c["v"], off, 8, 2, 0.6, act)
+        oa = oracle.gdpa_fwd(c["q"], c["k"], c["v"], off, 8, 2, 0.6, act, absolute=True)
+        assert np.all(np.abs(o) <= oa + 1e-12)
+        g = oracle.gdpa_bwd(c["q"], c["k"], c["v"], c["dout"], off, 8, 2, 0.6, act)
+        ga = oracle.gdpa_bwd(c["q"], c["k"], c["v"], c["dout"], off, 8, 2, 0.6, act, absolute=True)
+        for x, xa in zip(g, ga):
+            assert np.all(np.abs(x) <= xa + 1e-12)
+        pos = {n: np.abs(c[n]) + 0.1 for n in ("q", "v", "dout")}
+        o = oracle.gdpa_fwd(pos["q"], pos["q"], pos["v"], off, 8, 2, 0.6, act)
+        oa = oracle.gdpa_fwd(pos["q"], pos["q"], pos["v"], off, 8, 2, 0.6, act, absolute=True)
+        np.testing.assert_allclose(o, oa, rtol=1e-13, atol=0)
+        g = oracle.gdpa_bwd(pos["q"], pos["q"], pos["v"], pos["dout"], off, 8, 2, 0.6, act)
+        ga = oracle.gdpa_bwd(pos["q"], pos["q"], pos["v"], pos["dout"], off, 8, 2, 0.6, act,
+                             absolute=True)
+        for x, xa in zip(g, ga):
+            np.testing.assert_allclose(x, xa, rtol=1e-13, atol=0)
+
+
+def test_huge_block_and_window_are_causal_attention():
+    """B and W as large as int32 allows: one block per user, every earlier
+    key visible, i.e. causal attention (torch SDPA, fp64); the oracle's
+    scratch is sized by the longest visible range, not by W * B."""
+    lengths = [40, 0, 13]
+    c = case(642, lengths, H=2, D=4)
+    big = 2 ** 31 - 1
+    out, lse = oracle.fwd(c["q"], c["k"], c["v"], c["offsets"], big, big, 0.5)
+    g = oracle.bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], big, big, 0.5)
+    ref = oracle.fwd(c["q"], c["k"], c["v"], c["offsets"], 64, 1, 0.5)
+    refg = oracle.bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], 64, 1, 0.5)
+    np.testing.assert_array_equal(out, ref[0])
+    np.testing.assert_array_equal(lse, ref[1])
+    for x, y in zip(g, refg):
+        np.testing.assert_array_equal(x, y)
+    off = c["offsets"]
+    for u in (0, 2):
+        a, b = off[u], off[u + 1]
+        t = [torch.from_numpy(np.ascontiguousarray(c[n][a:b].transpose(1, 0, 2))) for n in "qkv"]
+        sd = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True, scale=0.5)
+        np.testing.assert_allclose(out[a:b], sd.numpy().transpose(1, 0, 2), atol=1e-13, rtol=0)
+
+
+def test_mx_all_codes_draw():
+    """The full-range MX draw covers all 254 finite E4M3 codes (both zeros,
+    every subnormal), never a NaN code, and scales in the requested range."""
+    c = wl.random_mx_case(7, [400, 300], 2, 64, wide=((94, 100), (140, 146)))
+    codes = np.concatenate([c["q_mx"].ravel(), c["k_mx"].ravel()])
+    assert len(np.unique(codes)) == 254
+    assert not np.any((codes & 0x7F) == 0x7F)
+    assert c["q_sc"].min() >= 94 and c["q_sc"].max() <= 100
+    assert c["k_sc"].min() >= 140 and c["k_sc"].max() <= 146
