@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 6
+#define BLOCKATTN_ABI_VERSION 7
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -62,7 +62,8 @@ typedef enum {
     BLOCKATTN_ERR_INVALID_ARGUMENT = 1, /* batch<0, T<0, H<1, B<1, W<1, non-finite
                                            scale, null or misaligned pointer,
                                            unknown dtype                        */
-    BLOCKATTN_ERR_UNSUPPORTED = 2,      /* D not in {32,64,128}; T above 2^31-1;
+    BLOCKATTN_ERR_UNSUPPORTED = 2,      /* D not in {32,64,128}; T above
+                                           2^31-1025; 128 * H * D * 4 >= 2^32;
                                            launch too large                     */
     BLOCKATTN_ERR_WORKSPACE = 3,        /* workspace needed but null, too small
                                            or not 256-byte aligned              */
@@ -75,8 +76,10 @@ typedef enum {
  *   total_tokens   T = offsets[batch]; T = 0 or batch = 0 returns OK at once
  *   num_heads      H >= 1;  head_dim D in {32, 64, 128}
  *   block_size     B >= 1 (B = 1 with W = w is the token sliding window of
- *                  w tokens, see blockattn_swa_fwd)
- *   window_blocks  W >= 1 (W = 1: independent blocks)
+ *                  w tokens, see blockattn_swa_fwd); any B >= T gives one
+ *                  block per user, as B = T does
+ *   window_blocks  W >= 1 (W = 1: independent blocks); any W >= ceil(T/B)
+ *                  gives causal attention over each whole user
  *   scale          finite multiplier of <q, k> (typically 1/sqrt(D))
  */
 blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
@@ -90,7 +93,8 @@ blockattn_status blockattn_fwd(const void *q, const void *k, const void *v,
 /*
  * Bytes of device workspace blockattn_bwd needs for these sizes.  For bf16:
  * two fp32 row statistics per (head, token) (lse in base 2 and -delta, with
- * delta = <dO, O>), 256 bytes of counters, batch + 1 int32 tile prefix sums
+ * delta_i = sum_j P_ij <dO_i, v_j>), 256 bytes of counters, batch + 1 int32
+ * tile prefix sums
  * and a 16-byte tile-table entry per (user, head, 128-row unit, role), i.e.
  * at most 2 * (ceil(T / 128) + batch) * H entries; each region is rounded up
  * to 256 bytes.  0 for fp32 and for empty calls (T or batch 0).  Returns
@@ -234,9 +238,10 @@ blockattn_status blockattn_gdpa_bwd(const void *q, const void *k, const void *v,
  *   q_scale,   E8M0 bytes [H, T, D/32] (head-major, like lse), 4-byte
  *   k_scale    aligned; element (t, h, d) has scale [h][t][d / 32]
  *   v          bf16 [T, H, D];  out bf16 [T, H, D];  lse fp32 [H, T]
- * D must be 64 or 128, and T * H * D / 32 a multiple of 4 (the scales are
- * read in dword windows), else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments
- * and errors as for blockattn_fwd.  There is no MXFP8 backward.
+ * D must be 64 or 128, else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments and
+ * errors as for blockattn_fwd.  The block-scaled fp8 products sum with fewer
+ * bits than fp32 (measured: within 2^-12 of sum_d |scale q_d k_d| per score).
+ * There is no MXFP8 backward.
  */
 blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
                                   const void *k, const void *k_scale,
@@ -246,6 +251,31 @@ blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
                                   int32_t block_size, int32_t window_blocks,
                                   float scale, void *out, float *lse,
                                   hipStream_t stream);
+
+/*
+ * blockattn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of BLOCKATTN_NOALLOC_WORKSPACE_BYTES inside the library, one per GPU,
+ * created with the library's code object and held until the process ends;
+ * this call allocates nothing.  Calls whose blockattn_bwd_workspace_size
+ * exceeds that size return BLOCKATTN_ERR_WORKSPACE (64 MiB covers, e.g.,
+ * 524288 tokens x 8 heads: 33.6 MB).  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller; each call sets up
+ * everything it reads (no state carries over between calls).  Arguments,
+ * results and other errors as for blockattn_bwd; BLOCKATTN_ERR_HIP if the
+ * array's address cannot be obtained.
+ */
+#define BLOCKATTN_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+blockattn_status blockattn_bwd_noalloc(const void *q, const void *k, const void *v,
+                                       const void *out, const void *dout,
+                                       const float *lse, const int32_t *offsets,
+                                       int32_t batch, int64_t total_tokens,
+                                       int32_t num_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t window_blocks,
+                                       float scale, blockattn_dtype dtype, void *dq,
+                                       void *dk, void *dv, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *blockattn_status_string(blockattn_status status);

@@ -23,7 +23,9 @@ GDPA_SILU, GDPA_GELU = 1, 2  # blockattn_gdpa_act
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
            "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_rope", "blockattn_rope_bwd",
            "blockattn_gdpa_fwd", "blockattn_gdpa_bwd", "blockattn_mx_fwd",
-           "blockattn_status_string", "blockattn_abi_version")
+           "blockattn_bwd_noalloc", "blockattn_status_string", "blockattn_abi_version")
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # BLOCKATTN_NOALLOC_WORKSPACE_BYTES
 
 _lib = None
 
@@ -78,6 +80,9 @@ def load() -> ctypes.CDLL:
     lib.blockattn_mx_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32,
                                      vp, vp, vp]
     lib.blockattn_mx_fwd.restype = ctypes.c_int
+    lib.blockattn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                          i32, f32, ctypes.c_int, vp, vp, vp, vp]
+    lib.blockattn_bwd_noalloc.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_abi_version.argtypes = []
@@ -102,6 +107,14 @@ def blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_hea
     return load().blockattn_bwd(q, k, v, out, dout, lse, offsets, batch, total_tokens,
                                 num_heads, head_dim, block_size, window_blocks, scale,
                                 dtype, dq, dk, dv, workspace, workspace_bytes, stream)
+
+
+def blockattn_bwd_noalloc(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads,
+                          head_dim, block_size, window_blocks, scale, dtype, dq, dk, dv,
+                          stream) -> int:
+    return load().blockattn_bwd_noalloc(q, k, v, out, dout, lse, offsets, batch, total_tokens,
+                                        num_heads, head_dim, block_size, window_blocks, scale,
+                                        dtype, dq, dk, dv, stream)
 
 
 def blockattn_swa_fwd(q, k, v, offsets, batch, total_tokens, num_heads, head_dim,
@@ -272,6 +285,28 @@ def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
         del ws
     if rc != OK:
         raise BlockAttnError("blockattn_bwd", rc)
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
+                scale: float, grads=None, stream=None):
+    """Backward block attention through blockattn_bwd_noalloc (the library's
+    static workspace; nothing is allocated for it).  Returns (dq, dk, dv);
+    pass grads to have nothing allocated at all."""
+    _check(q, k, v, offsets)
+    T, H, D = q.shape
+    _check_like(q, out, dout)
+    _check_lse(lse, H, T)
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv = _grads(q, grads)
+        rc = blockattn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), offsets.data_ptr(),
+                                   offsets.numel() - 1, T, H, D, block_size, window_blocks,
+                                   float(scale), _dtype_code(q), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), st.cuda_stream)
+    if rc != OK:
+        raise BlockAttnError("blockattn_bwd_noalloc", rc)
     return dq, dk, dv
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "blockattn.h"
 #include "common.h"
 #include "kernels.h"
@@ -97,15 +99,38 @@ blockattn_status forward(const void *q, const void *k, const void *v, const int3
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 
+// The workspace of blockattn_bwd_noalloc: a static device array, one copy per
+// GPU, created by the runtime with this file's code object.  Host code never
+// uses its name as an address (on the host it is a stand-in, not device
+// memory): scratch_address() looks up the device address once per device.
+static __device__ __align__(256) unsigned char scratch[BLOCKATTN_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (null if it cannot be
+// obtained), looked up with that device current on its first use and kept.
+void *scratch_address() {
+    static std::atomic<void *> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 // The backward entry points: plain (rope_base 0) or through a rotary
-// embedding of q and k (rope_base > 0, q and k already rotated).
+// embedding of q and k (rope_base > 0, q and k already rotated).  noalloc:
+// the workspace is the static array above (workspace and workspace_bytes
+// are ignored), looked up only once the arguments have passed their checks.
 blockattn_status backward(const void *q, const void *k, const void *v, const void *out,
                           const void *dout, const float *lse, const int32_t *offsets,
                           int32_t batch, int64_t total_tokens, int32_t num_heads,
                           int32_t head_dim, int32_t block_size, int32_t window_blocks,
                           float scale, float rope_base, int act, blockattn_dtype dtype,
                           void *dq, void *dk, void *dv, void *workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+                          size_t workspace_bytes, hipStream_t stream, bool noalloc = false) {
     bool empty;
     blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
                                        &block_size, &window_blocks, scale, dtype, &empty);
@@ -118,6 +143,15 @@ blockattn_status backward(const void *q, const void *k, const void *v, const voi
         (stats && (!aligned16(out) || !aligned16(lse))))
         return BLOCKATTN_ERR_INVALID_ARGUMENT;
     const size_t need = blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype);
+    if (noalloc) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0 && need <= BLOCKATTN_NOALLOC_WORKSPACE_BYTES) {
+            workspace = scratch_address();
+            if (!workspace) return BLOCKATTN_ERR_HIP;
+            workspace_bytes = BLOCKATTN_NOALLOC_WORKSPACE_BYTES;
+        }
+    }
     if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
         return BLOCKATTN_ERR_WORKSPACE;
     ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, block_size,
@@ -178,6 +212,19 @@ blockattn_status blockattn_bwd(const void *q, const void *k, const void *v, cons
     return backward(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads, head_dim,
                     block_size, window_blocks, scale, 0.f, ba::kSoftmax, dtype, dq, dk, dv,
                     workspace, workspace_bytes, stream);
+}
+
+blockattn_status blockattn_bwd_noalloc(const void *q, const void *k, const void *v,
+                                       const void *out, const void *dout, const float *lse,
+                                       const int32_t *offsets, int32_t batch,
+                                       int64_t total_tokens, int32_t num_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t window_blocks, float scale,
+                                       blockattn_dtype dtype, void *dq, void *dk, void *dv,
+                                       hipStream_t stream) {
+    return backward(q, k, v, out, dout, lse, offsets, batch, total_tokens, num_heads, head_dim,
+                    block_size, window_blocks, scale, 0.f, ba::kSoftmax, dtype, dq, dk, dv,
+                    nullptr, 0, stream, /*noalloc=*/true);
 }
 
 blockattn_status blockattn_rope(const void *q, const void *k, const int32_t *offsets,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 6
+    assert lsb.blockattn_abi_version() == 7
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -100,6 +100,25 @@ def bwd_status(**kw):
 ])
 def test_bwd_argument_checks(kw, code):
     assert bwd_status(**kw) == code
+
+
+def test_noalloc_argument_checks():
+    """blockattn_bwd_noalloc checks like blockattn_bwd, and a call whose
+    workspace would exceed the static array returns the workspace error
+    before any HIP call."""
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, offsets=FAKE,
+             batch=2, total_tokens=100, num_heads=2, head_dim=48, block_size=64,
+             window_blocks=2, scale=0.125, dtype=lsb.BF16, dq=FAKE, dk=FAKE, dv=FAKE,
+             stream=None)
+    assert lsb.blockattn_bwd_noalloc(*a.values()) == binding.ERR_UNSUPPORTED
+    a.update(head_dim=64, dout=None)
+    assert lsb.blockattn_bwd_noalloc(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    T = 4 << 20  # 2 * 4 B * 8 heads * T = 268 MB of row statistics > 64 MiB
+    a.update(dout=FAKE, total_tokens=T, num_heads=8)
+    assert lsb.blockattn_bwd_workspace_size(T, 2, 8, lsb.BF16) > lsb.NOALLOC_WORKSPACE_BYTES
+    assert lsb.blockattn_bwd_noalloc(*a.values()) == binding.ERR_WORKSPACE
+    a.update(total_tokens=0)
+    assert lsb.blockattn_bwd_noalloc(*a.values()) == binding.OK
 
 
 def test_sliding_window_argument_checks():
