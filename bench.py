@@ -99,11 +99,12 @@ def measured_counters(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(w, users: int, flops_per_pair_head: float):
-    """The fp64 oracle, as it stands, on users [0, users) of the workload."""
+def _oracle_inputs(w, users):
+    """Users [0, users) of the workload as the oracle sees them: fp64 values
+    of the bf16-rounded inputs (or decoded MXFP8)."""
     import oracle
-    from long_sequence_block_amd import workloads as wl
     import torch
+    from long_sequence_block_amd import workloads as wl
     c = wl.draw(w, users=slice(0, users))
     host = {}
     for key, val in c.items():
@@ -117,29 +118,77 @@ def cpu_baseline(w, users: int, flops_per_pair_head: float):
     if w.mx:  # the oracle attends on the decoded MXFP8 values
         host["q"] = oracle.mx_decode(host.pop("q_mx"), host.pop("q_sc"))
         host["k"] = oracle.mx_decode(host.pop("k_mx"), host.pop("k_sc"))
+    return host
+
+
+def _oracle_run(w, host):
+    """The oracle's whole path for the workload: forward (and backward)."""
+    import oracle
     off = host["offsets"]
-    t0 = time.perf_counter()
     q, k, v = host["q"], host["k"], host["v"]
     B, W, sc = w.block_size, w.window_blocks, w.scale
     if w.act:  # activation scores
         oracle.gdpa_fwd(q, k, v, off, B, W, sc, w.act)
         if w.backward:
             oracle.gdpa_bwd(q, k, v, host["dout"], off, B, W, sc, w.act)
-    else:
-        if w.rope_base:
-            q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
-        oracle.fwd(q, k, v, off, B, W, sc)
-        if w.backward and w.rope_base:
-            oracle.rope_bwd(q, k, v, host["dout"], off, B, W, sc, w.rope_base)
-        elif w.backward:
-            oracle.bwd(q, k, v, host["dout"], off, B, W, sc)
+        return
+    if w.rope_base:
+        q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
+    oracle.fwd(q, k, v, off, B, W, sc)
+    if w.backward and w.rope_base:
+        oracle.rope_bwd(q, k, v, host["dout"], off, B, W, sc, w.rope_base)
+    elif w.backward:
+        oracle.bwd(q, k, v, host["dout"], off, B, W, sc)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, users: int, flops_per_pair_head: float):
+    """The fp64 oracle, as it stands, on users [0, users) of the workload, on
+    all host threads; plus single-thread times of the forward on bounded
+    samples of the tiny, fixed-length and jagged workloads."""
+    import oracle
+    from long_sequence_block_amd import workloads as wl
+    host = _oracle_inputs(w, users)
+    off = host["offsets"]
+    t0 = time.perf_counter()
+    _oracle_run(w, host)
     dt = time.perf_counter() - t0
     flops = flops_per_pair_head * pairs_per_head(off, w.block_size, w.window_blocks) * w.heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    single = []
+    oracle.set_num_threads(1)
+    try:
+        for wid, nu in ((1, 2), (2, 8), (3, 32)):
+            ws = dataclasses.replace(wl.WORKLOADS[wid], backward=False)
+            hs = _oracle_inputs(ws, nu)
+            t1 = time.perf_counter()
+            _oracle_run(ws, hs)
+            d1 = time.perf_counter() - t1
+            f1 = 4.0 * ws.head_dim * pairs_per_head(hs["offsets"], ws.block_size,
+                                                    ws.window_blocks) * ws.heads
+            single.append({"workload": ws.name, "sample": f"users 0-{nu - 1} of {ws.users}, fwd",
+                           "seconds": round(d1, 3), "GFLOP/s": round(f1 / d1 / 1e9, 3)})
+    finally:
+        oracle.set_num_threads(threads)
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"users 0-{users - 1} of {w.name} ({int(off[-1])} tokens, "
                        f"{'fwd+bwd' if w.backward else 'fwd'}, fp64), {dt:.1f} s"),
-            "seconds": dt}
+            "seconds": dt, "threads": threads, "nproc": nproc, "cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(), "single_thread": single}
 
 
 def copy_calibration(mib: int, steps: int, warmup: int):
@@ -164,6 +213,63 @@ def copy_calibration(mib: int, steps: int, warmup: int):
                       "GB_per_s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def length_sweep(steps: int, warmup: int):
+    """The long-context shape (32 users of L tokens, 8 heads, head_dim 128,
+    block 256) at every sweep length, forward, with the block window (W = 4)
+    and with a window of L/256 blocks (plain causal attention), on the same
+    kernels: one JSON line per (L, window) with the median call time, then
+    the affine fit of the block-window times against the visible-pair count
+    and the log-log slopes of both against L.  Inputs: seeded N(0,1) draws
+    made on the device (the values do not change the work)."""
+    import torch
+    import long_sequence_block_amd as lsb
+    from long_sequence_block_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    rows = []
+    for L in wl.LONG_CONTEXT_SWEEP:
+        w = wl.long_context(L)
+        T, H, D, B = w.users * L, w.heads, w.head_dim, w.block_size
+        g = torch.Generator(device=dev)
+        g.manual_seed(L)
+        q, k, v = (torch.randn(T, H, D, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        off = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+        for W, kind in ((w.window_blocks, "block window"), (L // B, "full causal")):
+            for _ in range(warmup):
+                lsb.fwd(q, k, v, off, B, W, w.scale, out=out, lse=lse)
+            times = []
+            for _ in range(steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                lsb.fwd(q, k, v, off, B, W, w.scale, out=out, lse=lse)
+                e1.record()
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1))
+            times.sort()
+            npair = pairs_per_head(off.cpu().numpy(), B, W)
+            row = {"length": L, "window": kind, "window_blocks": W, "pairs_per_head": npair,
+                   "median_ms": round(times[len(times) // 2], 4), "min_ms": round(times[0], 4),
+                   "TFLOP/s": round(4.0 * D * npair * H / (times[len(times) // 2] * 1e-3) / 1e12,
+                                    1)}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+        del q, k, v, out, lse
+    blk = [r for r in rows if r["window"] == "block window"]
+    cau = [r for r in rows if r["window"] == "full causal"]
+    x = np.array([r["pairs_per_head"] for r in blk], np.float64)
+    y = np.array([r["median_ms"] for r in blk], np.float64)
+    a, c = np.polyfit(x, y, 1)
+    r2 = 1.0 - np.sum((y - (a * x + c)) ** 2) / np.sum((y - y.mean()) ** 2)
+    lens = np.log([r["length"] for r in blk])
+    slope = lambda rs: float(np.polyfit(lens, np.log([r["median_ms"] for r in rs]), 1)[0])
+    print(json.dumps({"fit": "block-window median_ms = a * pairs_per_head + c",
+                      "a_ms_per_pair": a, "c_ms": round(c, 4), "r2": round(r2, 5),
+                      "loglog_slope_block": round(slope(blk), 3),
+                      "loglog_slope_causal": round(slope(cau), 3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,7 +282,8 @@ def main():
                          "step with the rotary embedding (rope, fwd, fused rope backward), 8 the "
                          "training step with SiLU scores (generalized dot-product attention), "
                          "9 and 10 the long-context and jagged forwards with q, k in MXFP8, "
-                         "11 the long-context shape as a training step")
+                         "11 the long-context shape as a training step, 12 the training step "
+                         "at 1024 users")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--window-blocks", type=int, default=0,
@@ -186,6 +293,9 @@ def main():
                     help="skip the cold pass (steps after an L2 / Infinity Cache flush)")
     ap.add_argument("--cpu-users", type=int, default=0,
                     help="users timed for the oracle baseline (default: all)")
+    ap.add_argument("--length-sweep", action="store_true",
+                    help="instead of the workload, time the long-context forward at each sweep "
+                         "length with the block window and with full causal attention")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, time a plain device copy of MIB MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -205,6 +315,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps, args.warmup)
+        return
+    if args.length_sweep:
+        length_sweep(args.steps, args.warmup)
         return
 
     w = wl.WORKLOADS[args.workload]
@@ -359,6 +472,9 @@ def main():
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * tflops / peak, 3),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "timing": ("value and ms_per_step: warm, the timed steps run back to back with "
+                   "inputs resident in HBM; calls.cold: per-call medians after a 512 MiB "
+                   "write that evicts L2 and the Infinity Cache"),
         "calls": calls,
         "roofline": roof,
         "cpu_baseline": None,

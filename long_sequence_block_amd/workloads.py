@@ -161,6 +161,11 @@ WORKLOADS = {
     8: Workload(3, "jagged-bf16-train-gdpa-silu", users=256, heads=8, head_dim=64,
                 block_size=128, window_blocks=2, dtype="bf16", backward=True,
                 dout_wid=5, act=1),
+    # The training step at a local batch of 1024 users (the pages put local
+    # batches above 1,000 samples), same length law and shapes.
+    12: Workload(12, "jagged-bf16-1024-train", users=1024, heads=8, head_dim=64,
+                 block_size=128, window_blocks=2, dtype="bf16", backward=True,
+                 dout_wid=12),
 }
 
 # Length sweep of the long-context workload (time should grow linearly).

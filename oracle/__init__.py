@@ -68,6 +68,8 @@ def _load():
     lib.oracle_pair_count.restype = ctypes.c_int64
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -91,6 +93,11 @@ def _ip(a: np.ndarray):
 def num_threads() -> int:
     """OpenMP threads the oracle runs with (OMP_NUM_THREADS or all cores)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def pair_count(offsets, block_size: int, window_blocks: int) -> int:

@@ -97,6 +97,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Sets the OpenMP thread count of later calls (n >= 1); results do not
+ * depend on it.  Used to time the oracle on one thread. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Sum over all users of the number of visible keys per query (one head). */
 int64_t oracle_pair_count(const int32_t *offsets, int batch, int B, int W)
 {

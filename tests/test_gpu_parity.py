@@ -172,7 +172,7 @@ def full_size_every_element(w, max_tokens):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("wid", [2, 3, 5, 6])
+@pytest.mark.parametrize("wid", [2, 3, 5, 6, 12])
 def test_workload_full_size_every_element(wid):
     w = wl.WORKLOADS[wid]
     _print(f"workload {wid} ({w.name}) full size, every element")
