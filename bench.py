@@ -76,8 +76,8 @@ def measured_traffic(kernel: str, workload: str):
 
 def measured_counters(kernel: str, workload: str):
     """Shader clock and MFMA busy share of the dominant kernel from the
-    committed rocprofv3 counter summary (fwd_mfma for the forward, the main
-    kernel bwd_mfma for the backward), or None if there is none for the
+    committed rocprofv3 counter summary (fwd_mfma for the forward; for the
+    backward, each of its bwd_mfma passes), or None if there is none for the
     current kernel sources."""
     files = ([f"fwd_{workload}_counters.md", f"fwd-bwd_{workload}_counters.md"]
              if kernel == "fwd" else [f"fwd-bwd_{workload}_counters.md"])
@@ -90,12 +90,15 @@ def measured_counters(kernel: str, workload: str):
         m_src = re.search(r"kernel_source_hash\s*([0-9a-f]{16})", text)
         if not m_src or m_src.group(1) != kernel_source_hash():
             return None
+        rows = []
         for line in text.splitlines():
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
             if cells and cells[0].startswith(row_key) and len(cells) > 4:
-                return {"kernel": cells[0], "clock_ghz": float(cells[3]),
-                        "mfma_busy_pct": float(cells[4]),
-                        "source": os.path.join("profiles", f)}
+                rows.append({"kernel": cells[0], "clock_ghz": float(cells[3]),
+                             "mfma_busy_pct": float(cells[4]),
+                             "source": os.path.join("profiles", f)})
+        if rows:
+            return rows[0] if kernel == "fwd" else rows
     return None
 
 
