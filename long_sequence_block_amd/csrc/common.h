@@ -134,32 +134,58 @@ __device__ __forceinline__ int logical_tile() {
 // per unit), so consecutive tiles are consecutive row units of one (user,
 // head).  Tiles exist only for rows that exist: a jagged batch costs no
 // padding.  Returns false for a workgroup beyond the last tile (the grid is
-// an upper bound, since the host never reads the offsets).  `sh` must hold
-// NT/64 + 4 ints in LDS.  All results are wave-uniform.
-template <int NT>
+// an upper bound, since the host never reads the offsets).  Each pass of the
+// scan covers NT * UPT users.  `sh` must hold NT/64 + 4 ints in LDS.  All
+// results are wave-uniform.
+template <int NT, int UPT = 1>
 __device__ bool decode_tile(const Shape &s, int R, int tpb, Tile &t, int *sh) {
     const int tid = threadIdx.x;
     const int lt = logical_tile();
     const int T = (int)s.T;
     int base = 0;
-    for (int c0 = 0; c0 < s.batch; c0 += NT) {
-        const int u = c0 + tid;
-        int n = 0, a = 0, L = 0;
-        if (u < s.batch) {
-            a = clamp_off(s.offsets[u], T);
-            const int b = clamp_off(s.offsets[u + 1], T);
-            L = b > a ? b - a : 0;
-            n = (int)(((int64_t)L + R - 1) / R * tpb * s.H);
+    for (int c0 = 0; c0 < s.batch; c0 += NT * UPT) {
+        // UPT consecutive users per thread: UPT + 1 offsets, read once
+        const int u0 = c0 + tid * UPT;
+        int n[UPT], a[UPT], L[UPT];
+        int sum = 0;
+        if constexpr (UPT == 1) {
+            n[0] = a[0] = L[0] = 0;
+            if (u0 < s.batch) {  // both offsets in one branch
+                a[0] = clamp_off(s.offsets[u0], T);
+                const int e = clamp_off(s.offsets[u0 + 1], T);
+                L[0] = e > a[0] ? e - a[0] : 0;
+                n[0] = (int)(((int64_t)L[0] + R - 1) / R * tpb * s.H);
+            }
+            sum = n[0];
+        } else {
+            int prev = u0 < s.batch ? clamp_off(s.offsets[u0], T) : 0;
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                n[i] = a[i] = L[i] = 0;
+                if (u0 + i < s.batch) {
+                    const int e = clamp_off(s.offsets[u0 + i + 1], T);
+                    a[i] = prev;
+                    L[i] = e > prev ? e - prev : 0;
+                    n[i] = (int)(((int64_t)L[i] + R - 1) / R * tpb * s.H);
+                    prev = e;
+                }
+                sum += n[i];
+            }
         }
         int chunk;
-        const int incl = wg_inclusive_scan<NT>(n, sh, chunk);
+        const int incl = wg_inclusive_scan<NT>(sum, sh, chunk);
         // the thread of the owning user passes on its rows (no second read
         // of the offsets)
-        if (n > 0 && lt >= base + incl - n && lt < base + incl) {
-            sh[NT / 64] = u;
-            sh[NT / 64 + 1] = lt - (base + incl - n);
-            sh[NT / 64 + 2] = a;
-            sh[NT / 64 + 3] = L;
+        int first = base + incl - sum;
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            if (n[i] > 0 && lt >= first && lt < first + n[i]) {
+                sh[NT / 64] = u0 + i;
+                sh[NT / 64 + 1] = lt - first;
+                sh[NT / 64 + 2] = a[i];
+                sh[NT / 64 + 3] = L[i];
+            }
+            first += n[i];
         }
         base += chunk;
         if (lt < base) break;  // uniform: base and lt are the same in every thread

@@ -66,7 +66,10 @@ struct FwdChunk {
 // two blocks, and the scale of (row m, block j) comes from lane m + 32j.
 // Those 16-byte reads are exactly the granule reads of a bf16 tile of D/2
 // columns, so the fp8 K tile uses that geometry and its DMA offsets as is.
-template <int D, int ACT, bool MX>
+//
+// UPT: users per thread in each pass of the tile decode (4 for batches above
+// 1024 users, chosen by the host, which knows the batch size).
+template <int D, int ACT, bool MX, int UPT>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     bf16 *__restrict__ out, float *__restrict__ lse, const uint8_t *__restrict__ qsc,
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     __shared__ int sh[8];
     __shared__ __align__(1024) FwdChunk<D> sm[NB];
     Tile t;
-    if (!decode_tile<kThreads>(s, kTileRows, 1, t, sh)) return;
+    if (!decode_tile<kThreads, UPT>(s, kTileRows, 1, t, sh)) return;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -377,9 +380,16 @@ hipError_t launch_act(const Shape &s, const void *q, const void *k, const void *
                       float *lse, hipStream_t st, const uint8_t *qsc = nullptr,
                       const uint8_t *ksc = nullptr) {
     const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 1, s.H);
-    hipLaunchKernelGGL((fwd_mfma<D, ACT, MX>), dim3((unsigned)grid), dim3(kThreads), 0, st, s,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse, qsc,
-                       ksc);
+    // one pass of 256 users per thread-scan is fastest up to 1024 users; four
+    // users per thread and pass beyond that
+    if (s.batch > 4 * kThreads)
+        hipLaunchKernelGGL((fwd_mfma<D, ACT, MX, 4>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse,
+                           qsc, ksc);
+    else
+        hipLaunchKernelGGL((fwd_mfma<D, ACT, MX, 1>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse,
+                           qsc, ksc);
     return hipGetLastError();
 }
 

@@ -88,13 +88,15 @@ MX = [
     # ends inside a dword (read byte by byte)
     ([301, 0, 78], 1, 64, 64, 2, 1),
     ([129, 254], 3, 64, 16, 4, -1),
+    # 1101 users: the tile decode's four-users-per-thread form
+    ([int(x) for x in np.random.default_rng(31).integers(0, 30, 1101)], 1, 64, 16, 2, 1),
 ]
 
 
 @pytest.mark.parametrize("idx", range(len(MX)))
 def test_mx_fwd_every_element(idx):
     lengths, H, D, B, W, sign = MX[idx]
-    _print(f"mx {idx}: lengths={lengths} H={H} D={D} B={B} W={W}")
+    _print(f"mx {idx}: {len(lengths)} users, lengths={lengths[:8]} H={H} D={D} B={B} W={W}")
     c = wl.random_mx_case(idx, lengths, H, D)
     mx_parity(c, B, W, sign / math.sqrt(D), 1 << 30)
 

@@ -123,6 +123,26 @@ def test_many_users_every_element():
     _print("  " + p.summary())
 
 
+LARGE_BATCH = [
+    # (users, max tokens, H, D, B, W, seed): above 1024 users the forward's
+    # tile decode reads four users per thread and pass; user counts that are
+    # not multiples of four leave a ragged last group
+    (4097, 70, 2, 64, 32, 2, 611),
+    (5003, 24, 2, 128, 16, 3, 612),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(LARGE_BATCH)))
+def test_large_batch_every_element(idx):
+    n, top, H, D, B, W, seed = LARGE_BATCH[idx]
+    lengths = [int(x) for x in np.random.default_rng(seed).integers(0, top + 1, n)]
+    _print(f"large batch {idx}: {n} users of 0-{top} tokens, T={sum(lengths)} H={H} D={D} "
+           f"B={B} W={W}")
+    case = wl.random_case(seed, lengths, H, D)
+    p = check_full(case, "bf16", B, W, 1.0 / math.sqrt(D), backward=True)
+    _print("  " + p.summary())
+
+
 def test_empty_inputs():
     for lengths in ([], [0], [0, 0, 0]):
         case = wl.random_case(7, lengths, 2, 64)
