@@ -49,6 +49,11 @@ SMALL = [
     ([300, 77, 0, 5], 2, 64, 2**31 - 1, 2**31 - 1, "bf16"),
     ([100, 37], 1, 32, 2**31 - 1, 2**31 - 1, "fp32"),
     ([260, 1000], 1, 128, 64, 2**31 - 1, "bf16"),
+    # windows of more than 1024 rows (W B after clamping): a key tile's
+    # queries span up to 11 query tiles
+    ([2000, 700], 1, 64, 256, 5, "bf16"),
+    ([1500, 300, 40], 2, 128, 128, 10, "bf16"),
+    ([1300, 9], 1, 32, 1200, 1, "bf16"),
 ]
 
 
