@@ -441,3 +441,218 @@ int oracle_gdpa_bwd_abs(const double *q, const double *k, const double *v,
     return gdpa_bwd_sum(q, k, v, dout, offsets, batch, T, H, D, B, W, scale, act, 1, dq,
                         dk, dv);
 }
+
+/* ------------------------------------------------------------------------
+ * MXFP8 attention with the weights quantized too.  "GEM (Meta)" (aiwiki.ai),
+ * section "Custom kernels", says production attention runs in MXFP8, and
+ * section "Ultra-low-precision training" that the matmuls are block-scaled
+ * MXFP8 end to end.  For P.V that means the softmax weights are themselves
+ * quantized to E4M3 with one shared power-of-two scale per 32 elements
+ * along the product's contraction axis (the keys).  The pages say no more;
+ * the readings taken here:
+ *
+ *   - q, k, v arrive decoded (exact fp64 values of their MXFP8 codes);
+ *     scores s_ij, visibility and lse are those of oracle_fwd;
+ *   - with t_ij = s_ij log2(e), a weight is 2^t_ij up to a factor common to
+ *     the row, which cancels;
+ *   - the keys of a query fall into blocks of 32 consecutive positions of
+ *     the packed token axis (block index = global token / 32; a block may
+ *     hold keys the query does not see, which weigh 0);
+ *   - in block b, with F_b = floor(max of t_ij over its visible keys), each
+ *     visible weight is stored as 2^(F_b - 7) * R(2^(t_ij - F_b + 7)), R the
+ *     nearest E4M3 value, ties to the even code.  The argument stays below
+ *     2^8 (the E4M3 maximum is 448), so nothing saturates;
+ *   - O_i = sum_j Pq_ij v_j / sum_j 2^t_ij: the normaliser and lse come
+ *     from the unquantized weights.
+ * Shifting every t_ij of a row by an integer shifts every F_b by the same
+ * integer and leaves the codes, hence O_i, unchanged.
+ */
+
+static const double kLog2e = 1.4426950408889634; /* log2(e) */
+
+/* Nearest E4M3 value to x >= 0 (x < 2^8 + 2^4), ties to the even code:
+ * subnormals are multiples of 2^-9 below 2^-6, normals have 3 fraction
+ * bits. */
+double oracle_e4m3_round(double x)
+{
+    if (!(x > 0.0))
+        return 0.0;
+    int e;
+    (void)frexp(x, &e); /* x = f 2^e, f in [0.5, 1): floor(log2 x) = e - 1 */
+    const int q = e - 1 < -6 ? -9 : e - 1 - 3; /* exponent of the quantum */
+    return ldexp(rint(ldexp(x, -q)), q);      /* rint: nearest, ties even */
+}
+
+/* The block maxima F_b of row i: t[0..n) are the row's t_ij for keys
+ * j0 .. j0 + n - 1, g0 their first global token index; fb[] gets F of each
+ * key's block. */
+static void block_floor(const double *t, int64_t n, int64_t g0, double *fb)
+{
+    int64_t a = 0;
+    while (a < n) {
+        const int64_t blk = (g0 + a) / 32;
+        int64_t e = a;
+        double mx = -INFINITY;
+        while (e < n && (g0 + e) / 32 == blk) {
+            if (t[e] > mx)
+                mx = t[e];
+            ++e;
+        }
+        const double f = floor(mx);
+        for (int64_t x = a; x < e; ++x)
+            fb[x] = f;
+        a = e;
+    }
+}
+
+/* Forward with quantized weights: out [T,H,D], lse [H,T]. */
+int oracle_mxpv_fwd(const double *q, const double *k, const double *v,
+                    const int32_t *offsets, int batch, int64_t T, int H, int D,
+                    int B, int W, double scale, double *out, double *lse)
+{
+    if (check_args(offsets, batch, T, H, D, B, W))
+        return -1;
+    int status = 0;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D;
+    const size_t nvis = visible_max(offsets, batch, B, W);
+#pragma omp parallel
+    {
+        double *t = (double *)malloc(sizeof(double) * nvis * 2);
+        if (!t) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < npairs; ++p) {
+            if (!t)
+                continue;
+            double *fb = t + nvis;
+            const int u = (int)(p / H), h = (int)(p % H);
+            const int64_t t0 = offsets[u];
+            const int64_t L = (int64_t)offsets[u + 1] - t0;
+            for (int64_t i = 0; i < L; ++i) {
+                const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+                const int64_t j0 = first_visible(i, B, W);
+                const int64_t n = i - j0 + 1;
+                double m = -INFINITY;
+                for (int64_t x = 0; x < n; ++x) {
+                    const double *kj = k + (t0 + j0 + x) * rs + (int64_t)h * D;
+                    t[x] = scale * dot(qi, kj, D) * kLog2e;
+                    if (t[x] > m)
+                        m = t[x];
+                }
+                /* weights relative to 2^M, M = floor of the row maximum
+                 * (an integer shift, which changes no code) */
+                const double M = floor(m);
+                block_floor(t, n, t0 + j0, fb);
+                double l = 0.0;
+                for (int64_t x = 0; x < n; ++x)
+                    l += exp2(t[x] - M);
+                double *oi = out + (t0 + i) * rs + (int64_t)h * D;
+                for (int d = 0; d < D; ++d)
+                    oi[d] = 0.0;
+                for (int64_t x = 0; x < n; ++x) {
+                    const double pq =
+                        ldexp(oracle_e4m3_round(exp2(t[x] - fb[x] + 7.0)), (int)(fb[x] - 7.0 - M));
+                    const double *vj = v + (t0 + j0 + x) * rs + (int64_t)h * D;
+                    for (int d = 0; d < D; ++d)
+                        oi[d] += pq * vj[d];
+                }
+                for (int d = 0; d < D; ++d)
+                    oi[d] /= l;
+                lse[(int64_t)h * T + t0 + i] = (M + log2(l)) / kLog2e;
+            }
+        }
+        free(t);
+    }
+    return status;
+}
+
+/* Parity allowance for oracle_mxpv_fwd (test support, not part of the
+ * definition).  A computation whose t_ij are off by at most eps2[h*T + i]
+ * (log2 units) may round a weight to the neighbouring E4M3 value when its
+ * scaled argument lies that close to a midpoint, and may pick F_b one
+ * apart when the block maximum lies that close to an integer (which moves
+ * only the weights below 2^(F_b - 13), the E4M3 subnormal range).  For each
+ * output element, slack = sum_j a_ij |v_jd| / l_i, with a_ij the largest
+ * change of Pq_ij those flips allow (0 for a weight no flip can reach). */
+int oracle_mxpv_slack(const double *q, const double *k, const double *v,
+                      const int32_t *offsets, int batch, int64_t T, int H, int D,
+                      int B, int W, double scale, const double *eps2, double *slack)
+{
+    if (check_args(offsets, batch, T, H, D, B, W))
+        return -1;
+    int status = 0;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D;
+    const size_t nvis = visible_max(offsets, batch, B, W);
+#pragma omp parallel
+    {
+        double *t = (double *)malloc(sizeof(double) * nvis * 2);
+        if (!t) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < npairs; ++p) {
+            if (!t)
+                continue;
+            double *fb = t + nvis;
+            const int u = (int)(p / H), h = (int)(p % H);
+            const int64_t t0 = offsets[u];
+            const int64_t L = (int64_t)offsets[u + 1] - t0;
+            for (int64_t i = 0; i < L; ++i) {
+                const double *qi = q + (t0 + i) * rs + (int64_t)h * D;
+                const int64_t j0 = first_visible(i, B, W);
+                const int64_t n = i - j0 + 1;
+                const double e = eps2[(int64_t)h * T + t0 + i];
+                double m = -INFINITY;
+                for (int64_t x = 0; x < n; ++x) {
+                    const double *kj = k + (t0 + j0 + x) * rs + (int64_t)h * D;
+                    t[x] = scale * dot(qi, kj, D) * kLog2e;
+                    if (t[x] > m)
+                        m = t[x];
+                }
+                const double M = floor(m);
+                block_floor(t, n, t0 + j0, fb);
+                /* the unquantized normaliser, at its smallest */
+                double l = 0.0;
+                for (int64_t x = 0; x < n; ++x)
+                    l += exp2(t[x] - M - e);
+                double *si = slack + (t0 + i) * rs + (int64_t)h * D;
+                for (int d = 0; d < D; ++d)
+                    si[d] = 0.0;
+                for (int64_t x = 0; x < n; ++x) {
+                    /* is the block's maximum within e of an integer? */
+                    int64_t a = x;
+                    while (a > 0 && (t0 + j0 + a - 1) / 32 == (t0 + j0 + x) / 32)
+                        --a;
+                    double bm = -INFINITY;
+                    for (int64_t y = a; y < n && (t0 + j0 + y) / 32 == (t0 + j0 + x) / 32; ++y)
+                        if (t[y] > bm)
+                            bm = t[y];
+                    const double fr = bm - floor(bm);
+                    const int f_flip = fr <= e || 1.0 - fr <= e;
+                    /* the scaled argument and its reach */
+                    const double xs = exp2(t[x] - fb[x] + 7.0);
+                    const double lo = xs * exp2(-e), hi = xs * exp2(e);
+                    const int code_flip = oracle_e4m3_round(lo) != oracle_e4m3_round(hi);
+                    double a_ij = 0.0;
+                    if (code_flip) /* one E4M3 step at the larger end */
+                        a_ij = oracle_e4m3_round(hi) - oracle_e4m3_round(lo);
+                    if (f_flip) /* the subnormal quantum of the grid one F below */
+                        a_ij += 2.0 * ldexp(1.0, -9);
+                    a_ij = ldexp(a_ij, (int)(fb[x] - 7.0 - M));
+                    if (a_ij == 0.0)
+                        continue;
+                    const double *vj = v + (t0 + j0 + x) * rs + (int64_t)h * D;
+                    for (int d = 0; d < D; ++d)
+                        si[d] += a_ij * fabs(vj[d]) / l;
+                }
+            }
+        }
+        free(t);
+    }
+    return status;
+}

@@ -735,3 +735,172 @@ def test_mx_all_codes_draw():
     assert not np.any((codes & 0x7F) == 0x7F)
     assert c["q_sc"].min() >= 94 and c["q_sc"].max() <= 100
     assert c["k_sc"].min() >= 140 and c["k_sc"].max() <= 146
+
+
+# ------------------------------------------- MXFP8 weights for the P.V product
+
+
+def test_e4m3_round_matches_torch():
+    """oracle's E4M3 rounding (nearest, ties to the even code) against
+    torch's float8_e4m3fn conversion: every code value, every midpoint
+    between neighbouring codes (the ties), their fp32 neighbours, and
+    log-uniform values from below the smallest subnormal to 2^8.  All
+    inputs are fp32 values: torch converts through fp32, so an fp64 input
+    one ulp from a midpoint would be rounded twice there."""
+    vals = np.array(sorted({oracle.e4m3_value(c) for c in range(127)}), np.float32)  # 0 .. 448
+    vals = vals[vals <= 256.0]
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(5)
+    x = np.concatenate([vals, mids, np.nextafter(mids, np.float32(0)),
+                        np.nextafter(mids, np.float32(np.inf)),
+                        np.exp2(rng.uniform(-12, 8, 20000)).astype(np.float32)])
+    x = x[x < 2 ** 8 + 2 ** 3]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    x = x.astype(np.float64)
+    np.testing.assert_array_equal(oracle.e4m3_round(x), ref)
+
+
+def _mx_rows(seed, lengths, D, lo=-1, hi=2):
+    rng = np.random.default_rng(seed)
+    T = sum(lengths)
+    q = rng.integers(lo, hi, (T, 1, D)).astype(np.float64)
+    k = rng.integers(lo, hi, (T, 1, D)).astype(np.float64)
+    v = rng.standard_normal((T, 1, D))
+    return q, k, v, wl.offsets_from_lengths(lengths)
+
+
+def test_mxpv_integer_scores_are_exact():
+    """With scale = ln 2 and integer q, k every t_ij = s_ij log2(e) is an
+    integer, so every weight is a power of two (within 2^16 of its block's
+    largest here) and exactly representable: the quantized forward equals
+    the plain softmax forward."""
+    q, k, v, off = _mx_rows(11, [70, 33, 1, 40], 4)
+    out, lse = oracle.mxpv_fwd(q, k, v, off, 16, 3, math.log(2))
+    ref, lref = oracle.fwd(q, k, v, off, 16, 3, math.log(2))
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lref, rtol=1e-14, atol=1e-14)
+
+
+def test_mxpv_integer_row_shift_changes_nothing():
+    """A bias column adds the same amount to every t_ij of a row.  An
+    integer amount moves every block's F by that integer and leaves every
+    code, hence out, unchanged; half an integer moves the codes."""
+    lengths = [90, 37, 64]
+    c = case(12, lengths, H=2, D=16)
+    scale = 0.3
+
+    def with_bias(n):
+        q = np.concatenate([c["q"], np.ones(c["q"].shape[:2] + (1,))], axis=2)
+        b = n / (scale * math.log2(math.e))
+        k = np.concatenate([c["k"], np.full(c["k"].shape[:2] + (1,), b)], axis=2)
+        v = np.concatenate([c["v"], np.zeros(c["v"].shape[:2] + (1,))], axis=2)
+        return oracle.mxpv_fwd(q, k, v, c["offsets"], 32, 2, scale)[0]
+
+    base = with_bias(0)
+    for n in (3, -5, 17):
+        np.testing.assert_allclose(with_bias(n), base, rtol=1e-12, atol=1e-13)
+    assert np.abs(with_bias(0.5) - base).max() > 1e-4
+
+
+def test_mxpv_normal_weights_round_to_four_significant_bits():
+    """Where no weight falls below 2^-13 of its block's largest (the E4M3
+    subnormal range), each quantized weight is the weight rounded to four
+    significant bits (ties to even): out = sum_j sig4(w_ij) v_j / sum_j w_ij,
+    written here from frexp and numpy's half-even rounding, with no block
+    exponent and no E4M3 table (the weights in a power-of-two unit, since
+    four-bit rounding commutes only with power-of-two scaling)."""
+    lengths = [100, 45]
+    c = case(13, lengths, H=2, D=8)
+    scale = 0.15   # t spans well under 13 within any block
+    B, W = 32, 2
+    out, _ = oracle.mxpv_fwd(c["q"], c["k"], c["v"], c["offsets"], B, W, scale)
+    off = c["offsets"]
+    ref = np.zeros_like(out)
+    for u in range(len(lengths)):
+        t0 = off[u]
+        for h in range(2):
+            for i in range(off[u + 1] - t0):
+                j0 = max(0, (i // B - W + 1) * B)
+                kk = c["k"][t0 + j0:t0 + i + 1, h]
+                s = scale * kk @ c["q"][t0 + i, h]
+                t = s * math.log2(math.e)
+                w = np.exp2(t - np.floor(t.max()))   # a power-of-two unit
+                assert w.min() > 2.0 ** -12
+                m, e = np.frexp(w)
+                sig4 = np.ldexp(np.round(m * 16) / 16, e)
+                ref[t0 + i, h] = sig4 @ c["v"][t0 + j0:t0 + i + 1, h] / w.sum()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_mxpv_small_weights_use_their_blocks_exponent():
+    """Hand case, scale = ln 2 so t_ij = <q_i, k_j>: query 32 of a user at
+    token 0 sees keys 0..32; key 0 has t = 0, keys 1..31 t = -100 and key
+    32 t = -14.3.  Key 32 is alone in block 1 (tokens 32..63), so F = -15 and
+    2^(t - F + 7) = 2^7.7 = 207.9 rounds to 208: weight 208 * 2^-22.  Moved
+    to token 1, inside block 0 (F = 0), the same t gives 2^-7.3 = 0.00635,
+    in the subnormal range: 3 * 2^-9, weight 3 * 2^-16.  With key 0 at
+    t = -0.5 the block's F is floor(-0.5) = -1, and key 1 at t = -14.8 gives
+    2^-6.8 = 0.00897, i.e. 5 * 2^-9 (4.59 quanta), weight 5 * 2^-17 (F = 0
+    would give 2 quanta at 2^-7: 4 * 2^-17)."""
+    def run(pos, t0, tp, pre=0):
+        # (pre: tokens of an earlier user, which move the packed positions)
+        q = np.zeros((pre + 33, 1, 2))
+        k = np.zeros((pre + 33, 1, 2))
+        v = np.zeros((pre + 33, 1, 2))
+        q[:, 0, 0] = 1.0
+        k[pre + 1:, 0, 0] = -100.0
+        k[pre, 0, 0] = t0
+        k[pre + pos, 0, 0] = tp
+        v[pre + pos, 0, 1] = 1.0
+        off = [0, pre, pre + 33] if pre else [0, 33]
+        out, _ = oracle.mxpv_fwd(q, k, v, off, 64, 1, math.log(2))
+        l = 2.0 ** t0 + 31 * 2.0 ** -100 + 2.0 ** tp
+        return out[pre + 32, 0, 1] * l
+
+    assert run(32, 0.0, -14.3) == pytest.approx(208 * 2.0 ** -22, rel=1e-12)
+    assert run(1, 0.0, -14.3) == pytest.approx(3 * 2.0 ** -16, rel=1e-12)
+    assert run(1, -0.5, -14.8) == pytest.approx(5 * 2.0 ** -17, rel=1e-12)
+    # blocks follow the packed token axis: behind a 5-token user, local key
+    # 27 is token 32, alone in its block (local 1 .. 26 are token 6 .. 31)
+    assert run(27, 0.0, -14.3, pre=5) == pytest.approx(208 * 2.0 ** -22, rel=1e-12)
+
+
+def test_mxpv_keys_outside_the_window_do_not_matter():
+    """Keys no query of a user sees (here: another user's, and later keys)
+    may take any value: out and lse of the others are unchanged, so block
+    maxima are taken over visible keys only."""
+    lengths = [80, 50]
+    c = case(14, lengths, H=1, D=8)
+    a = oracle.mxpv_fwd(c["q"], c["k"], c["v"], c["offsets"], 16, 2, 0.4)
+    k2 = c["k"].copy()
+    k2[80:] = 50.0          # user 1's keys: user 0 never sees them
+    b = oracle.mxpv_fwd(c["q"], k2, c["v"], c["offsets"], 16, 2, 0.4)
+    np.testing.assert_array_equal(a[0][:80], b[0][:80])
+    np.testing.assert_array_equal(a[1][:, :80], b[1][:, :80])
+
+
+def test_mxpv_slack_covers_perturbed_scores():
+    """The parity allowance is zero for exact scores and covers what a
+    computation with scores off by up to eps does: perturb q so every t_ij
+    moves by at most eps (|dt| <= |scale| |dq|_1 max|k| log2 e) and check
+    |out' - out| <= slack + (2^(2 eps) - 1) max|v| (the second term: the
+    unquantized weights' own change)."""
+    lengths = [120, 64, 7]
+    c = case(15, lengths, H=2, D=16)
+    scale, B, W = 0.25, 32, 2
+    T = sum(lengths)
+    z = oracle.mxpv_slack(c["q"], c["k"], c["v"], c["offsets"], B, W, scale, np.zeros((2, T)))
+    assert not z.any()
+    out, _ = oracle.mxpv_fwd(c["q"], c["k"], c["v"], c["offsets"], B, W, scale)
+    rng = np.random.default_rng(3)
+    kmax = np.abs(c["k"]).max()
+    hits = 0
+    for rep in range(6):
+        dq = rng.uniform(-1, 1, c["q"].shape) * 1e-3
+        eps = abs(scale) * np.abs(dq).sum(axis=2).T * kmax * math.log2(math.e)  # [H, T]
+        sl = oracle.mxpv_slack(c["q"], c["k"], c["v"], c["offsets"], B, W, scale, eps)
+        o2, _ = oracle.mxpv_fwd(c["q"] + dq, c["k"], c["v"], c["offsets"], B, W, scale)
+        extra = (np.exp2(2 * eps) - 1).T[:, :, None] * np.abs(c["v"]).max()
+        assert np.all(np.abs(o2 - out) <= sl + extra + 1e-12)
+        hits += int(np.sum(np.abs(o2 - out) > extra))
+    assert hits > 0   # some codes did flip, and the slack covered them
