@@ -72,10 +72,11 @@ def _load():
     lib.oracle_set_num_threads.restype = None
     lib.oracle_e4m3_round.argtypes = [f64]
     lib.oracle_e4m3_round.restype = ctypes.c_double
-    lib.oracle_mxpv_fwd.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, dp, dp]
+    lib.oracle_mxpv_fwd.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, i64, dp,
+                                    dp]
     lib.oracle_mxpv_fwd.restype = ctypes.c_int
-    lib.oracle_mxpv_slack.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, dp,
-                                      dp]
+    lib.oracle_mxpv_slack.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, i64,
+                                      dp, dp]
     lib.oracle_mxpv_slack.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -246,19 +247,20 @@ def mx_decode(codes, scales) -> np.ndarray:
     return _E4M3[codes] * np.repeat(f, 32, axis=-1)
 
 
-def mx_decode_tokens(codes, scales, total_tokens: int) -> np.ndarray:
-    """fp64 [T, H, D] values of MXFP8 data blocked along the token axis:
-    codes uint8 [H, D, Tp] (each (head, column) row holds its T tokens,
-    Tp >= T), scales uint8 [H, ceil(T/32), D] (scale (h, b, d) covers tokens
-    32b .. 32b + 31 of column d)."""
+def mx_decode_tokens(codes, scales, first_token: int = 0) -> np.ndarray:
+    """fp64 values of MXFP8 data blocked along the packed token axis: codes
+    uint8 [n, H, D] for tokens first_token .. first_token + n - 1, scales
+    uint8 [nblocks, H, D], scale (b, h, d) covering tokens 32b .. 32b + 31
+    of column (h, d) (the blocks of the whole tensor, indexed by packed
+    token)."""
     codes, scales = np.asarray(codes, np.uint8), np.asarray(scales, np.uint8)
-    T = int(total_tokens)
-    H, D, Tp = codes.shape
-    if Tp < T or scales.shape != (H, -(-T // 32), D):
-        raise ValueError("codes [H, D, Tp >= T], scales [H, ceil(T/32), D]")
-    f = np.where(scales == 255, np.nan, np.ldexp(1.0, scales.astype(np.int64) - 127))
-    val = _E4M3[codes[:, :, :T]] * np.repeat(f.transpose(0, 2, 1), 32, axis=2)[:, :, :T]
-    return np.ascontiguousarray(val.transpose(2, 0, 1))
+    n = codes.shape[0]
+    blk = (int(first_token) + np.arange(n)) // 32
+    if n and (blk[-1] >= scales.shape[0] or codes.shape[1:] != scales.shape[1:]):
+        raise ValueError("scales [ceil(T/32), H, D] for codes [T, H, D]")
+    sc = scales[blk]
+    f = np.where(sc == 255, np.nan, np.ldexp(1.0, sc.astype(np.int64) - 127))
+    return _E4M3[codes] * f
 
 
 def e4m3_round(x) -> np.ndarray:
@@ -268,22 +270,26 @@ def e4m3_round(x) -> np.ndarray:
     return np.array([f(float(v)) for v in x.ravel()], np.float64).reshape(x.shape)
 
 
-def mxpv_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float):
+def mxpv_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
+             first_token: int = 0):
     """Forward with the weights quantized to MXFP8 for the P.V product
-    (blockattn_oracle.c: oracle_mxpv_fwd): (out [T, H, D], lse [H, T])."""
+    (blockattn_oracle.c: oracle_mxpv_fwd): (out [T, H, D], lse [H, T]).
+    first_token: packed index of these arrays' token 0 (weight blocks are
+    32 packed tokens)."""
     q, k, v, off = _f64(q), _f64(k), _f64(v), _i32(offsets)
     T, H, D = q.shape
     out = np.zeros((T, H, D), np.float64)
     lse = np.zeros((H, T), np.float64)
     rc = _load().oracle_mxpv_fwd(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
-                                 int(block_size), int(window_blocks), float(scale), _dp(out),
-                                 _dp(lse))
+                                 int(block_size), int(window_blocks), float(scale),
+                                 int(first_token), _dp(out), _dp(lse))
     if rc != 0:
         raise ValueError(f"oracle_mxpv_fwd failed with status {rc}")
     return out, lse
 
 
-def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: float, eps2):
+def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: float, eps2,
+               first_token: int = 0):
     """Per-element parity allowance [T, H, D] of mxpv_fwd's out for a
     computation whose t_ij = s_ij log2(e) are off by at most eps2 [H, T]
     (blockattn_oracle.c: oracle_mxpv_slack).  Test support."""
@@ -292,8 +298,8 @@ def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: flo
     e = _f64(np.broadcast_to(np.asarray(eps2, np.float64), (H, T)))
     sl = np.zeros((T, H, D), np.float64)
     rc = _load().oracle_mxpv_slack(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
-                                   int(block_size), int(window_blocks), float(scale), _dp(e),
-                                   _dp(sl))
+                                   int(block_size), int(window_blocks), float(scale),
+                                   int(first_token), _dp(e), _dp(sl))
     if rc != 0:
         raise ValueError(f"oracle_mxpv_slack failed with status {rc}")
     return sl

@@ -904,3 +904,33 @@ def test_mxpv_slack_covers_perturbed_scores():
         assert np.all(np.abs(o2 - out) <= sl + extra + 1e-12)
         hits += int(np.sum(np.abs(o2 - out) > extra))
     assert hits > 0   # some codes did flip, and the slack covered them
+
+
+def test_mxpv_user_range_keeps_packed_blocks():
+    """Checking a range of users on its own gives the whole run's values
+    when first_token names the range's packed start (weight blocks are 32
+    packed tokens); re-based to 0 it would put the block edges elsewhere."""
+    lengths = [45, 70, 33]
+    c = case(16, lengths, H=2, D=8)
+    full, lfull = oracle.mxpv_fwd(c["q"], c["k"], c["v"], c["offsets"], 16, 3, 0.7)
+    lo, hi = 45, 148
+    sub = wl.subset_users(c, slice(1, 3))
+    part, lpart = oracle.mxpv_fwd(sub["q"], sub["k"], sub["v"], sub["offsets"], 16, 3, 0.7,
+                                  first_token=lo)
+    np.testing.assert_array_equal(part, full[lo:hi])
+    np.testing.assert_array_equal(lpart, lfull[:, lo:hi])
+    moved, _ = oracle.mxpv_fwd(sub["q"], sub["k"], sub["v"], sub["offsets"], 16, 3, 0.7)
+    assert np.abs(moved - full[lo:hi]).max() > 1e-6
+
+
+def test_mx_decode_tokens_blocks_follow_packed_tokens():
+    """Token-blocked decode: code 0x38 (1.0) with scale byte 127 + b for
+    block b gives 2^b on tokens 32b .. 32b + 31, also for a range that
+    starts inside a block."""
+    T = 100
+    codes = np.full((T, 1, 2), 0x38, np.uint8)
+    scales = (127 + np.arange(4, dtype=np.uint8))[:, None, None].repeat(2, axis=2)
+    full = oracle.mx_decode_tokens(codes, scales)
+    np.testing.assert_array_equal(full[:, 0, 0], 2.0 ** (np.arange(T) // 32))
+    part = oracle.mx_decode_tokens(codes[40:70], scales, first_token=40)
+    np.testing.assert_array_equal(part, full[40:70])
