@@ -111,7 +111,7 @@ def _oracle_inputs(w, users):
     c = wl.draw(w, users=slice(0, users))
     host = {}
     for key, val in c.items():
-        if key == "offsets" or key.endswith("_mx") or key.endswith("_sc"):
+        if key in ("offsets", "first_token") or key.endswith("_mx") or key.endswith("_sc"):
             host[key] = val
         else:
             t = torch.from_numpy(val)
@@ -121,6 +121,9 @@ def _oracle_inputs(w, users):
     if w.mx:  # the oracle attends on the decoded MXFP8 values
         host["q"] = oracle.mx_decode(host.pop("q_mx"), host.pop("q_sc"))
         host["k"] = oracle.mx_decode(host.pop("k_mx"), host.pop("k_sc"))
+    if w.mx_v:
+        host["v"] = oracle.mx_decode_tokens(host.pop("v_mx"), host.pop("v_bsc"),
+                                            host["first_token"])
     return host
 
 
@@ -134,6 +137,9 @@ def _oracle_run(w, host):
         oracle.gdpa_fwd(q, k, v, off, B, W, sc, w.act)
         if w.backward:
             oracle.gdpa_bwd(q, k, v, host["dout"], off, B, W, sc, w.act)
+        return
+    if w.mx_v:  # the weights quantized for P.V
+        oracle.mxpv_fwd(q, k, v, off, B, W, sc, first_token=host["first_token"])
         return
     if w.rope_base:
         q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
@@ -286,7 +292,8 @@ def main():
                          "training step with SiLU scores (generalized dot-product attention), "
                          "9 and 10 the long-context and jagged forwards with q, k in MXFP8, "
                          "11 the long-context shape as a training step, 12 the training step "
-                         "at 1024 users")
+                         "at 1024 users, 13 and 14 the long-context and jagged forwards with "
+                         "q, k, v in MXFP8 and the weights quantized for a block-scaled P.V")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--window-blocks", type=int, default=0,
@@ -337,18 +344,23 @@ def main():
     T = int(off_np[-1])
     if w.mx:  # fp8 codes as is, scales head-major [H, T, D/32]
         d = {k: torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)) if k.endswith("_sc")
-                                 else v).to(dev) for k, v in c.items() if k != "v"}
-        d["v"] = torch.from_numpy(c["v"]).to(tdt).to(dev)
+                                 else v).to(dev)
+             for k, v in c.items() if k in ("offsets", "q_mx", "q_sc", "k_mx", "k_sc")}
         d["q"], d["k"] = d.pop("q_mx"), d.pop("k_mx")
+        if w.mx_v:  # v transposed [H, D, Tp] with scales [H, ceil(T/32), D]
+            vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"])
+            d["v_t"], d["v_bsc"] = torch.from_numpy(vt).to(dev), torch.from_numpy(vs).to(dev)
+        else:
+            d["v"] = torch.from_numpy(c["v"]).to(tdt).to(dev)
     else:
         d = {k: torch.from_numpy(v).to(dev) if k == "offsets" else
              torch.from_numpy(v).to(tdt).to(dev) for k, v in c.items()}
     del c
     B, W, sc = w.block_size, w.window_blocks, w.scale
     H, D = w.heads, w.head_dim
-    out = torch.empty_like(d["v"])
+    out = torch.empty((T, H, D), dtype=tdt, device=dev)
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
-    grads = tuple(torch.empty_like(d["v"]) for _ in range(3)) if w.backward else None
+    grads = tuple(torch.empty_like(out) for _ in range(3)) if w.backward else None
     ws_n = lsb.blockattn_bwd_workspace_size(T, d["offsets"].numel() - 1, H,
                                            lsb.BF16 if w.dtype == "bf16" else lsb.FP32)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
@@ -360,7 +372,10 @@ def main():
             ev[0].record()
         if rb:  # rotary embedding of q and k into qa, ka
             lsb.rope(d["q"], d["k"], d["offsets"], rb, q_rot=qa, k_rot=ka)
-        if w.mx:  # q, k in MXFP8
+        if w.mx_v:  # q, k, v in MXFP8, the weights quantized for P.V
+            lsb.mxpv_fwd(qa, d["q_sc"], ka, d["k_sc"], d["v_t"], d["v_bsc"], d["offsets"], B, W,
+                         sc, out=out, lse=lse)
+        elif w.mx:  # q, k in MXFP8
             lsb.mx_fwd(qa, d["q_sc"], ka, d["k_sc"], d["v"], d["offsets"], B, W, sc, out=out,
                        lse=lse)
         elif w.act:  # activation scores (GDPA): no lse
@@ -426,6 +441,8 @@ def main():
     fwd_bytes = T * H * (4.0 * D * e + (0 if w.act else 4)) + (4.0 * T * H * D * e if rb else 0.0)
     if w.mx:  # q, k one byte per element plus one scale byte per 32
         fwd_bytes = T * H * (2.0 * D * (1 + 1 / 32) + 2.0 * D * e + 4)
+    if w.mx_v:  # v one byte per element too
+        fwd_bytes = T * H * (3.0 * D * (1 + 1 / 32) + 2.0 * D + 4)
     # GDPA's backward reads q, k, v, dO and writes dq, dk, dv (no out, no lse)
     bwd_bytes = (T * H * ((7.0 * D * e) if w.act else (8.0 * D * e + 4))) if w.backward else 0.0
     flops = fwd_flops + bwd_flops
@@ -433,6 +450,8 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     if w.mx:  # half the products at the fp8 rate, half (P.V) at the bf16 rate
         peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    if w.mx_v:  # both products at the fp8 rate
+        peak = PEAK_FP8_TFLOPS
 
     # dominant kernel: the entry point (one launch each) with the larger time
     if w.backward and bwd_ms >= fwd_ms:
@@ -463,9 +482,10 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp8(qk)+bf16" if w.mx else w.dtype,
+        "dtype": "mxfp8" if w.mx_v else "mxfp8(qk)+bf16" if w.mx else w.dtype,
         "data": "synthetic (seeded; lognormal jagged lengths, N(0,1) values"
-                + ("; random E4M3 codes and E8M0 scales for q, k)" if w.mx else ")"),
+                + ("; random E4M3 codes and E8M0 scales for q, k, v)" if w.mx_v else
+                   "; random E4M3 codes and E8M0 scales for q, k)" if w.mx else ")"),
         "config": {"workload": w.name, "users": w.users, "tokens": T, "heads": H,
                    "head_dim": D, "block_size": B, "window_blocks": W,
                    "backward": w.backward, "pairs_per_head": npair,

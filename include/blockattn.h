@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 7
+#define BLOCKATTN_ABI_VERSION 8
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -251,6 +251,43 @@ blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
                                   int32_t block_size, int32_t window_blocks,
                                   float scale, void *out, float *lse,
                                   hipStream_t stream);
+
+/*
+ * Forward with q, k and v in MXFP8 and the P.V product block-scaled too.
+ * The pages put production attention in MXFP8 ("GEM (Meta)", section
+ * "Custom kernels") and the matmuls in block-scaled MXFP8 end to end
+ * (section "Ultra-low-precision training"), which for P.V means the softmax
+ * weights are quantized as well.  Reading: each query's weights fall into
+ * blocks of 32 packed token positions; with F the floor of the block's
+ * largest s * log2(e), a weight 2^(s log2 e) (relative to the row) is
+ * stored as 2^(F - 7) times the nearest E4M3 value of 2^(s log2 e - F + 7)
+ * (ties to even; below 2^8, so nothing saturates).  The row sum and lse use
+ * the unquantized weights.  v's scales run along the P.V contraction, the
+ * token axis, so v comes transposed:
+ *   q, k, q_scale, k_scale   as for blockattn_mx_fwd
+ *   v_t      E4M3 bytes [H, D, Tp], Tp = 32 * ceil(T / 32): row (h, d)
+ *            holds column d of head h for tokens 0 .. T-1 (the rest is
+ *            padding); 16-byte aligned
+ *   v_scale  E8M0 bytes [H, ceil(T / 32), D], 4-byte aligned: element
+ *            (t, h, d) has scale [h][t / 32][d]
+ *   out      bf16 [T, H, D];  lse fp32 [H, T]
+ * A chunk of 64 keys starts on a multiple of 32 packed tokens, so the
+ * products read v's codes and scales of whole 32-token blocks around a
+ * window, including other users' tokens and the padding: every code of v_t
+ * (padding included) must be finite and no scale may be 255 (NaN), or NaN
+ * can reach unrelated rows.  D must be 64 or 128 and D * Tp below 2^32,
+ * else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments and errors as for
+ * blockattn_fwd.  The block-scaled products sum with fewer bits than fp32
+ * (see blockattn_mx_fwd).  There is no MXFP8 backward.
+ */
+blockattn_status blockattn_mxpv_fwd(const void *q, const void *q_scale,
+                                    const void *k, const void *k_scale,
+                                    const void *v_t, const void *v_scale,
+                                    const int32_t *offsets, int32_t batch,
+                                    int64_t total_tokens, int32_t num_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t window_blocks, float scale,
+                                    void *out, float *lse, hipStream_t stream);
 
 /*
  * blockattn_bwd without a workspace argument, for callers that cannot

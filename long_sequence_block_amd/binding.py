@@ -22,7 +22,7 @@ GDPA_SILU, GDPA_GELU = 1, 2  # blockattn_gdpa_act
 # Every symbol include/blockattn.h declares.
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
            "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_rope", "blockattn_rope_bwd",
-           "blockattn_gdpa_fwd", "blockattn_gdpa_bwd", "blockattn_mx_fwd",
+           "blockattn_gdpa_fwd", "blockattn_gdpa_bwd", "blockattn_mx_fwd", "blockattn_mxpv_fwd",
            "blockattn_bwd_noalloc", "blockattn_status_string", "blockattn_abi_version")
 
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # BLOCKATTN_NOALLOC_WORKSPACE_BYTES
@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
     lib.blockattn_mx_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32,
                                      vp, vp, vp]
     lib.blockattn_mx_fwd.restype = ctypes.c_int
+    lib.blockattn_mxpv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                       f32, vp, vp, vp]
+    lib.blockattn_mxpv_fwd.restype = ctypes.c_int
     lib.blockattn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                           i32, f32, ctypes.c_int, vp, vp, vp, vp]
     lib.blockattn_bwd_noalloc.restype = ctypes.c_int
@@ -166,6 +169,14 @@ def blockattn_mx_fwd(q, q_scale, k, k_scale, v, offsets, batch, total_tokens, nu
     return load().blockattn_mx_fwd(q, q_scale, k, k_scale, v, offsets, batch, total_tokens,
                                    num_heads, head_dim, block_size, window_blocks, scale, out,
                                    lse, stream)
+
+
+def blockattn_mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, batch, total_tokens,
+                       num_heads, head_dim, block_size, window_blocks, scale, out, lse,
+                       stream) -> int:
+    return load().blockattn_mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, batch,
+                                     total_tokens, num_heads, head_dim, block_size,
+                                     window_blocks, scale, out, lse, stream)
 
 
 def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
@@ -462,4 +473,37 @@ def mx_fwd(q, q_scale, k, k_scale, v, offsets, block_size: int, window_blocks: i
                               float(scale), out.data_ptr(), lse.data_ptr(), st.cuda_stream)
     if rc != OK:
         raise BlockAttnError("blockattn_mx_fwd", rc)
+    return out, lse
+
+
+def mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, block_size: int,
+             window_blocks: int, scale: float, out=None, lse=None, stream=None):
+    """Forward with q, k and v in MXFP8 and the weights quantized for P.V
+    (blockattn_mxpv_fwd): q, k uint8 [T, H, D] and q_scale, k_scale uint8
+    [H, T, D/32] as for mx_fwd; v_t uint8 [H, D, 32 ceil(T/32)] (v
+    transposed, padded with finite codes); v_scale uint8 [H, ceil(T/32), D].
+    Returns (out bf16 [T, H, D], lse fp32 [H, T])."""
+    T, H, D = q.shape
+    nb = -(-T // 32)
+    for t in (q, k):
+        if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q and k must be contiguous uint8 [T, H, D] device tensors")
+    for t in (q_scale, k_scale):
+        if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
+            raise ValueError("q_scale and k_scale must be contiguous uint8 [H, T, D/32]")
+    if v_t.dtype != torch.uint8 or v_t.shape != (H, D, 32 * nb) or not v_t.is_contiguous():
+        raise ValueError("v_t must be a contiguous uint8 [H, D, 32 ceil(T/32)] tensor")
+    if v_scale.dtype != torch.uint8 or v_scale.shape != (H, nb, D) or not v_scale.is_contiguous():
+        raise ValueError("v_scale must be a contiguous uint8 [H, ceil(T/32), D] tensor")
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device) if out is None else out
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+        rc = blockattn_mxpv_fwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(),
+                                k_scale.data_ptr(), v_t.data_ptr(), v_scale.data_ptr(),
+                                offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
+                                window_blocks, float(scale), out.data_ptr(), lse.data_ptr(),
+                                st.cuda_stream)
+    if rc != OK:
+        raise BlockAttnError("blockattn_mxpv_fwd", rc)
     return out, lse

@@ -309,6 +309,34 @@ blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale, const void
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 
+blockattn_status blockattn_mxpv_fwd(const void *q, const void *q_scale, const void *k,
+                                    const void *k_scale, const void *v_t, const void *v_scale,
+                                    const int32_t *offsets, int32_t batch, int64_t total_tokens,
+                                    int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t window_blocks, float scale, void *out, float *lse,
+                                    hipStream_t stream) {
+    bool empty;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
+                                       &block_size, &window_blocks, scale, BLOCKATTN_BF16, &empty);
+    if (st != BLOCKATTN_OK) return st;
+    if (head_dim != 64 && head_dim != 128) return BLOCKATTN_ERR_UNSUPPORTED;
+    // v^T rows are addressed with 32-bit byte offsets
+    const int64_t tp = (total_tokens + 31) / 32 * 32;
+    if ((int64_t)head_dim * tp >= ((int64_t)1 << 32)) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (empty) return BLOCKATTN_OK;
+    if (!q || !q_scale || !k || !k_scale || !v_t || !v_scale || !out || !lse)
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v_t) || !aligned16(out) ||
+        !aligned16(lse) || ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) ||
+        ((uintptr_t)v_scale & 3u))
+        return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, block_size,
+                                   window_blocks, scale);
+    const hipError_t e =
+        ba::launch_mfma_fwd_mxpv(s, q, q_scale, k, k_scale, v_t, v_scale, out, lse, stream);
+    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+}
+
 blockattn_status blockattn_swa_fwd(const void *q, const void *k, const void *v,
                                    const int32_t *offsets, int32_t batch, int64_t total_tokens,
                                    int32_t num_heads, int32_t head_dim, int32_t window_tokens,

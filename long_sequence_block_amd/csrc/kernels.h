@@ -30,6 +30,14 @@ hipError_t launch_mfma_fwd_mx(const Shape &s, const void *q, const void *q_scale
                               const void *k_scale, const void *v, void *out, float *lse,
                               hipStream_t st);
 
+// Forward with q, k and v in MXFP8 and the softmax weights quantized for a
+// block-scaled P.V product: q, k as above; v^T E4M3 [H, D, Tp] with
+// Tp = 32 ceil(T/32), v scales E8M0 [H, ceil(T/32), D] (one per 32 packed
+// tokens of a column).  D 64 or 128; D * Tp < 2^32.
+hipError_t launch_mfma_fwd_mxpv(const Shape &s, const void *q, const void *q_scale,
+                                const void *k, const void *k_scale, const void *v_t,
+                                const void *v_scale, void *out, float *lse, hipStream_t st);
+
 // bf16 MFMA backward.  Workspace (caller-owned device memory, 256-byte
 // aligned): per-(head, token) row statistics lse * log2(e) and -delta, which
 // the query pass writes for the key pass, a

@@ -30,7 +30,13 @@ namespace ba {
 typedef __attribute__((address_space(3))) char lds_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+// SW = 1: the swizzle of tiles read only by 16-byte row reads, such as fp8
+// tiles (which have no transposed reads).  For 64-byte rows (D = 32) it
+// takes row bits 2 and 3, so the 16 lanes that one LDS clock serves (rows
+// r .. r + 15 at 256 bytes per clock) all hit distinct banks; the SW = 0
+// swizzle there also serves the transposed reads, and rows r and r + 8 of
+// a 16-row group share banks.  Wider rows are the same for both.
+template <int D, int SW = 0>
 struct TileGeom {
     static constexpr int kRowBytes = D * 2;
     static constexpr int kBytes = 64 * kRowBytes;
@@ -38,6 +44,7 @@ struct TileGeom {
 
     // Granule XOR of physical row p (bits 0..3 of p only).
     __device__ static int swz(int p) {
+        if (D == 32 && SW) return (p >> 2) & 3;
         if (D == 32) return (((p >> 1) & 1) << 1) | ((p >> 2) & 1);
         int f = ((p >> 2) & 1) | (((p ^ (p >> 3)) & 1) << 1) | (((p >> 1) & 1) << 2);
         if (D == 128) f |= (p & 1) << 3;
@@ -50,15 +57,16 @@ struct TileGeom {
 // Per-lane source offsets (bytes from the first source row) of this wave's
 // DMA instructions for one tile; rsb = source row stride in bytes.  They do
 // not depend on the chunk, so they are computed once per workgroup.
-template <int D>
+// Physical row p holds source row sigma(p), or rho(p) with RHO.
+template <int D, bool RHO = false, int SW = 0>
 __device__ __forceinline__ void dma_offsets(uint32_t (&voff)[TileGeom<D>::kDmaPerWave],
                                             int wave, int lane, uint32_t rsb) {
 #pragma unroll
     for (int j = 0; j < TileGeom<D>::kDmaPerWave; ++j) {
         const int slot = (wave * TileGeom<D>::kDmaPerWave + j) * 64 + lane;
         const int p = slot / (D / 8), pg = slot % (D / 8);
-        const int gr = pg ^ TileGeom<D>::swz(p);
-        voff[j] = (uint32_t)sigma(p) * rsb + (uint32_t)gr * 16u;
+        const int gr = pg ^ TileGeom<D, SW>::swz(p);
+        voff[j] = (uint32_t)(RHO ? rho(p) : sigma(p)) * rsb + (uint32_t)gr * 16u;
     }
 }
 
@@ -105,9 +113,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // Offset (bytes) of the 16-byte row read of MFMA operand rows: lane (qi, g)
 // reads physical row qi, granule 2ks + g.  Returns the ks = 0 offset; the
 // offset for ks is (that ^ (ks << 5)), and rows 32*sub.. add sub*32*kRowBytes.
-template <int D>
+template <int D, int SW = 0>
 __device__ __forceinline__ int row_read_offset(int qi, int g) {
-    return TileGeom<D>::at(qi, g);
+    return TileGeom<D, SW>::at(qi, g);
 }
 
 // Offset (bytes) of the transposed reads that give this lane (m = lane%32,

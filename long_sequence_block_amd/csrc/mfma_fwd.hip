@@ -46,11 +46,12 @@ constexpr int kKC = 64;        // keys per staged chunk
 
 // LDS tiles in rotation (two: a small footprint lets more workgroups share a
 // CU, which hides more latency than a deeper prefetch), and waves per SIMD the
-// register budget is sized for.
+// register budget is sized for (the quantized-weights variant holds both
+// halves' scores and the v operands of a chunk at once).
 template <int D>
 constexpr int kBufs = 2;
-template <int D>
-constexpr int kWavesPerSimd = D == 128 ? 2 : 4;
+template <int D, int MX = 0>
+constexpr int kWavesPerSimd = D == 128 ? (MX == 2 ? 3 : 2) : 4;
 
 template <int D>
 struct FwdChunk {
@@ -67,19 +68,42 @@ struct FwdChunk {
 // Those 16-byte reads are exactly the granule reads of a bf16 tile of D/2
 // columns, so the fp8 K tile uses that geometry and its DMA offsets as is.
 //
+// MX = 2 takes v in MXFP8 too and quantizes the softmax weights for a
+// block-scaled P.V product ("GEM (Meta)", sections "Custom kernels" and
+// "Ultra-low-precision training": MXFP8 block-scaled matmuls end to end).
+// v arrives transposed, E4M3 [H, D, Tp] (Tp = 32 ceil(T/32); row (h, d)
+// holds that column's tokens) with E8M0 scales [H, ceil(T/32), D], one per
+// 32 packed tokens of a column: the scales run along the P.V contraction.
+// Chunks then start on a multiple of 32 packed tokens (keys before the
+// window are masked), so each 32-key half of a chunk is one scale block of
+// v and of the weights, and one 32x32x64 product takes a whole chunk.  K
+// rows sit at LDS row rho(m) (mfma_util.h), so a lane's 16 score registers
+// of a half are keys 16g .. 16g + 15: in register order they are the
+// lane's bytes of the weights' operand.  v^T rows are plain 16-byte row
+// reads of a tile with 64-byte rows.  The running max m is kept as a whole
+// number in the log2 domain, so a rescale is an exact power of two and a
+// weight's code depends only on its own block: with F = floor(block max of
+// s c), the weight p = 2^(s c - m) is stored as 2^(F - 7 - m) times the
+// nearest E4M3 value of p 2^(m - F + 7) = 2^(s c - F + 7) < 2^8.  The row
+// sum and lse use the unquantized weights.
+//
 // UPT: users per thread in each pass of the tile decode (4 for batches above
 // 1024 users, chosen by the host, which knows the batch size).
-template <int D, int ACT, bool MX, int UPT>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
+template <int D, int ACT, int MX, int UPT>
+__global__ __launch_bounds__(kThreads, (kWavesPerSimd<D, MX>)) void fwd_mfma(
     Shape s, const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     bf16 *__restrict__ out, float *__restrict__ lse, const uint8_t *__restrict__ qsc,
-    const uint8_t *__restrict__ ksc) {
+    const uint8_t *__restrict__ ksc, const uint8_t *__restrict__ vsc) {
     using G = TileGeom<D>;
-    using G8 = TileGeom<(D >= 64 ? D / 2 : 32)>;  // an fp8 row of D bytes
+    using G8 = TileGeom<(D >= 64 ? D / 2 : 32), 1>;  // an fp8 row of D bytes
     constexpr int NB = kBufs<D>;
     constexpr int kDma = 2 * G::kDmaPerWave;  // DMA instructions per wave per chunk
     __shared__ int sh[8];
-    __shared__ __align__(1024) FwdChunk<D> sm[NB];
+    // chunk buffers: K then V tiles (MX = 2: the fp8 K tile, its scales, the
+    // fp8 v^T tile at kVOff, its scales; half the bf16 footprint)
+    constexpr int kBuf = MX == 2 ? 128 * D + 2048 : (int)sizeof(FwdChunk<D>);
+    constexpr int kVOff = MX == 2 ? 64 * D + 1024 : G::kBytes;
+    __shared__ __align__(1024) unsigned char sm[NB * kBuf];
     Tile t;
     if (!decode_tile<kThreads, UPT>(s, kTileRows, 1, t, sh)) return;
 
@@ -107,7 +131,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     const uint32_t qsign = MX ? (s.scale < 0.f ? 0x80808080u : 0u)
                               : (ACT == kSoftmax && s.scale < 0.f ? 0x80008000u : 0u);
 
-    const int kbeg = window_start(row0, s.B, s.W);
+    const int kwin = window_start(row0, s.B, s.W);
+    // (MX = 2: back to a multiple of 32 packed tokens)
+    const int kbeg = MX == 2 ? kwin - ((t.tok0 + kwin) & 31) : kwin;
     const int nch = (row_end - kbeg + kKC - 1) / kKC;
     // fp8 rows are addressed in bf16 units (half their byte offsets)
     const int64_t rs8 = rs / 2;
@@ -120,13 +146,21 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     uint32_t voff[G::kDmaPerWave];
     dma_offsets<D>(voff, wave, lane, rsb);
     uint32_t voff8[G8::kDmaPerWave];
-    if constexpr (MX) dma_offsets<G8::kRowBytes / 2>(voff8, wave, lane, (uint32_t)(rs8 * 2));
+    if constexpr (MX)
+        dma_offsets<G8::kRowBytes / 2, MX == 2, 1>(voff8, wave, lane, (uint32_t)(rs8 * 2));
+    // MX = 2: v^T rows of this head from the chunk's first key (byte
+    // offsets), and their scales
+    const int64_t Tp = (s.T + 31) / 32 * 32, nblk = Tp / 32;
+    const int64_t vb8 = (int64_t)t.h * D * Tp + t.tok0 + kbeg;
+    const int64_t vs0 = ((int64_t)t.h * nblk + (t.tok0 + kbeg) / 32) * D;
+    uint32_t voffv[1];
+    if constexpr (MX == 2) dma_offsets<32, false, 1>(voffv, wave, lane, (uint32_t)Tp);
     // Scales of chunk ci: a dword-aligned window starts `mis` bytes before
     // them and lands in LDS after the fp8 K tile.
     auto scale_mis = [&](int ci) { return (int)((ks0 + (int64_t)ci * kKC * (D / 32)) & 3); };
     auto issue = [&](int ci, int buf) {
         const int off = ci * kKC, rows = min(kKC, row_end - kbeg - off);
-        lds_t *b = lds + buf * (int)sizeof(FwdChunk<D>);
+        lds_t *b = lds + buf * kBuf;
         if constexpr (MX) {
             dma_tile<G8::kRowBytes / 2>(row_desc<G8::kRowBytes / 2>(kb + off * rs8, rows, rs8), b,
                                         voff8, wave);
@@ -148,7 +182,28 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
         } else {
             dma_tile<D>(row_desc<D>(kb + off * rs, rows, rs), b, voff, wave);
         }
-        dma_tile<D>(row_desc<D>(vb + off * rs, rows, rs), b + G::kBytes, voff, wave);
+        if constexpr (MX == 2) {
+            // v^T: D rows of 64 key bytes (64-row tiles of 64-byte rows),
+            // ranges ending at the tensor's end; and the chunk's 2 x D
+            // scales (wave 1)
+            const int64_t vtot = (int64_t)s.H * D * Tp;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) {
+                const int64_t o = vb8 + off + (int64_t)j * 64 * Tp;
+                const uint64_t a = (uint64_t)((const uint8_t *)v + o);
+                const uint32_t range = (uint32_t)min(63 * Tp + 64, vtot - o);
+                dma_tile<32>(i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)range,
+                                   0x00020000},
+                             b + kVOff + j * 4096, voffv, wave);
+            }
+            if (wave == 1) {
+                const int64_t so = vs0 + (int64_t)(off / 32) * D;
+                const uint32_t nb = (uint32_t)min((int64_t)2 * D, (int64_t)s.H * nblk * D - so);
+                dma_dwords_lds(vsc + so, nb, lds_addr_of(b + kVOff + 64 * D), lane);
+            }
+        } else {
+            dma_tile<D>(row_desc<D>(vb + off * rs, rows, rs), b + G::kBytes, voff, wave);
+        }
     };
 
     if (nch > 0) issue(0, 0);
@@ -198,11 +253,16 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     int rd[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-        rd[ks] = MX ? row_read_offset<G8::kRowBytes / 2>(qi, g) ^ (ks << 5)
+        rd[ks] = MX ? row_read_offset<G8::kRowBytes / 2, 1>(qi, g) ^ (ks << 5)
                     : row_read_offset<D>(qi, g) ^ (ks << 5);
     // MX: byte offset of the lane's key row in the chunk's scale window
-    // (physical row m of the tile holds key sigma(m))
-    const int srd = sigma32(qi) * (D / 32);
+    // (physical row m of the tile holds key sigma(m), or rho(m) for MX = 2)
+    const int srd = (MX == 2 ? rho32(qi) : sigma32(qi)) * (D / 32);
+    // MX = 2: the lane's v^T row read (physical row qi, granule g of each
+    // 32-key block) and its scale byte (head-dim column sigma(qi) of
+    // block g)
+    const int rdv = row_read_offset<32, 1>(qi, g);
+    const int vsrd = g * D + sigma32(qi);
     int trd[2][D / 32];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -212,6 +272,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+    // running max (MX = 2: in the log2 domain, a whole number) and the
+    // lane's share of the row sum
     float m = -INFINITY, l = 0.f;
 
     // One chunk held in tile `buf` (a constant, so LDS offsets fold into
@@ -224,9 +286,123 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
             wait_vm_barrier<0>();
         if (ci + NB - 1 < nch) issue(ci + NB - 1, (buf + NB - 1) % NB);
         if (!wave_live) return;
-        const lds_t *kt = lds + buf * (int)sizeof(FwdChunk<D>);
-        const lds_t *vt = kt + G::kBytes;
+        const lds_t *kt = lds + buf * kBuf;
+        const lds_t *vt = kt + kVOff;
         const int c0 = kbeg + ci * kKC;
+        if constexpr (MX == 2) {
+            // halves h = 0, 1: keys c0 + 32h .. c0 + 32h + 31
+            const bool live0 = c0 <= w_last && c0 + 31 >= wave_klo;
+            const bool live1 = c0 + 32 <= w_last && c0 + 63 >= wave_klo;
+            if (!live0 && !live1) return;
+            // Each half in turn: scores (register r of lane group g is key
+            // a + 16g + r), masked; the running max; weights, their fp32
+            // sum, and the E4M3 codes of p 2^-E with
+            // E = floor(block max s c) - 7 - m (at most 1; at least -127,
+            // the scale's range: weights below 2^-119 of the row's max).
+            // The lazy rescale moves m to ceil(max s c) once a score passes
+            // m + 8: a whole power of two, so it is exact, and the first
+            // half's codes keep their values through its block exponent.
+            i32x8 pf8;
+            int e8[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int a = c0 + h * 32;
+                f32x16 x;
+                float bm = -INFINITY;
+                if (h ? live1 : live0) {
+                    const lds_t *k8 = kt + h * 32 * G8::kRowBytes;
+                    const lds_t *sp = kt + kKC * D + scale_mis(ci) + h * 32 * (D / 32) + srd + g;
+                    i32x8 kf[D / 64];
+                    int ksc8[D / 64];
+#pragma unroll
+                    for (int i = 0; i < D / 64; ++i) {
+                        const uint4 lo = __builtin_bit_cast(uint4, lds_read16(k8 + rd[2 * i]));
+                        const uint4 hi = __builtin_bit_cast(uint4, lds_read16(k8 + rd[2 * i + 1]));
+                        kf[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        ksc8[i] = *(const __attribute__((address_space(3))) uint8_t *)(sp + 2 * i);
+                    }
+                    x = f32x16{};
+#pragma unroll
+                    for (int i = 0; i < D / 64; ++i)
+                        x = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], qf8[i], x, 0,
+                                                                           0, 0, ksc8[i], 0,
+                                                                           qs8[i]);
+                    if (a + 31 > wr0 || a < wave_klo_max) {
+                        const int x0 = a + 16 * g - my_klo;
+                        const uint32_t span = (uint32_t)(my_row - my_klo);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if ((uint32_t)(x0 + r) > span) x[r] = -INFINITY;
+                    }
+                    float mh = x[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mh = fmaxf(mh, x[r]);
+                    bm = swap_max(mh);
+                }
+                const bool grow = bm * c > m + 8.f;
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float mn = grow ? ceilf(bm * c) : m;
+                    const int shift = m == -INFINITY ? -1000 : (int)(m - mn);  // <= 0
+                    m = mn;
+                    const float alpha = ldexpf(1.f, shift);
+                    l *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+                    if (h == 1) {
+                        // the first half's block exponent moves with m (its
+                        // weights drop below the scale's range only when
+                        // they are below 2^-119 of the row's max)
+                        e8[0] += shift;
+                        if (e8[0] < 0) {
+                            e8[0] = 0;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) pf8[j] = 0;
+                        }
+                    }
+                }
+                const int E = bm == -INFINITY ? -127 : (int)fmaxf(floorf(bm * c) - 7.f - m, -127.f);
+                const float mult = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E
+                e8[h] = E + 127;
+                // (this half's weights join l before the next half can
+                // rescale it)
+                float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int w = 0;
+                    if (bm != -INFINITY) {  // (uniform per lane pair; m is finite here)
+                        float p[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            p[i] = __builtin_amdgcn_exp2f(fmaf(x[4 * j + i], c, -m));
+                            ls[i] += p[i];
+                        }
+                        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * mult, p[1] * mult, 0, false);
+                        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * mult, p[3] * mult, w, true);
+                    }
+                    pf8[4 * h + j] = w;
+                }
+                l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            }
+            const int ps8 = g ? e8[1] : e8[0];  // the scale of (query, block g)
+            // v^T operands and scales, each read just before its product
+            // (fewer registers live across the chunk)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int tb = (dt >> 1) * 4096 + (dt & 1) * 2048;
+                const uint4 lo = __builtin_bit_cast(uint4, lds_read16(vt + tb + rdv));
+                const uint4 hi = __builtin_bit_cast(uint4, lds_read16(vt + tb + (rdv ^ 32)));
+                const i32x8 va = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                const int vs8 = *(const __attribute__((address_space(3))) uint8_t *)(
+                    vt + 64 * D + vsrd + 32 * dt);
+                acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf8, acc[dt], 0, 0,
+                                                                         0, vs8, 0, ps8);
+            }
+            return;
+        }
         // Softmax and P.V of the sub-tile `sub` (first key a) whose scores
         // are in sc.  The V reads go first so that their latency hides under
         // the vector work.
@@ -372,24 +548,24 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void fwd_mfma(
         }
     }
     if (ACT == kSoftmax && g == 0)
-        lse[(int64_t)t.h * s.T + t.tok0 + my_row] = (m * c + log2f(lt)) * kLn2;
+        lse[(int64_t)t.h * s.T + t.tok0 + my_row] = ((MX == 2 ? m : m * c) + log2f(lt)) * kLn2;
 }
 
-template <int D, int ACT, bool MX = false>
+template <int D, int ACT, int MX = 0>
 hipError_t launch_act(const Shape &s, const void *q, const void *k, const void *v, void *out,
                       float *lse, hipStream_t st, const uint8_t *qsc = nullptr,
-                      const uint8_t *ksc = nullptr) {
+                      const uint8_t *ksc = nullptr, const uint8_t *vsc = nullptr) {
     const int64_t grid = grid_upper_bound(s.T, s.batch, kTileRows, 1, s.H);
     // one pass of 256 users per thread-scan is fastest up to 1024 users; four
     // users per thread and pass beyond that
     if (s.batch > 4 * kThreads)
         hipLaunchKernelGGL((fwd_mfma<D, ACT, MX, 4>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                            s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse,
-                           qsc, ksc);
+                           qsc, ksc, vsc);
     else
         hipLaunchKernelGGL((fwd_mfma<D, ACT, MX, 1>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                            s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)out, lse,
-                           qsc, ksc);
+                           qsc, ksc, vsc);
     return hipGetLastError();
 }
 
@@ -411,8 +587,20 @@ hipError_t launch_mfma_fwd_mx(const Shape &s, const void *q, const void *q_scale
                               hipStream_t st) {
     const uint8_t *qs = (const uint8_t *)q_scale, *ks = (const uint8_t *)k_scale;
     switch (s.D) {
-    case 64: return launch_act<64, kSoftmax, true>(s, q, k, v, out, lse, st, qs, ks);
-    case 128: return launch_act<128, kSoftmax, true>(s, q, k, v, out, lse, st, qs, ks);
+    case 64: return launch_act<64, kSoftmax, 1>(s, q, k, v, out, lse, st, qs, ks);
+    case 128: return launch_act<128, kSoftmax, 1>(s, q, k, v, out, lse, st, qs, ks);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma_fwd_mxpv(const Shape &s, const void *q, const void *q_scale,
+                                const void *k, const void *k_scale, const void *v_t,
+                                const void *v_scale, void *out, float *lse, hipStream_t st) {
+    const uint8_t *qs = (const uint8_t *)q_scale, *ks = (const uint8_t *)k_scale;
+    const uint8_t *vs = (const uint8_t *)v_scale;
+    switch (s.D) {
+    case 64: return launch_act<64, kSoftmax, 2>(s, q, k, v_t, out, lse, st, qs, ks, vs);
+    case 128: return launch_act<128, kSoftmax, 2>(s, q, k, v_t, out, lse, st, qs, ks, vs);
     }
     return hipErrorInvalidValue;
 }

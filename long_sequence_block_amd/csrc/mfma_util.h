@@ -15,6 +15,17 @@ __device__ __forceinline__ int sigma32(int a) {
 }
 __device__ __forceinline__ int sigma(int x) { return (x & ~31) | sigma32(x & 31); }
 
+// rho: operand row m holds logical row (m & 3) | ((m >> 3) & 3) << 2 |
+// ((m >> 2) & 1) << 4 inside each group of 32 rows, which makes register r
+// of lane group g of a 32x32 accumulator hold logical row 16g + r: 16
+// consecutive rows per lane, the operand layout of the 64-deep block-scaled
+// fp8 product (lane (n, g) holds elements 16g .. 16g + 15 of each 32-element
+// block).
+__device__ __forceinline__ int rho32(int m) {
+    return (m & 3) | (((m >> 3) & 3) << 2) | (((m >> 2) & 1) << 4);
+}
+__device__ __forceinline__ int rho(int x) { return (x & ~31) | rho32(x & 31); }
+
 // First local key visible to local query `row`: its own block plus the W-1
 // previous blocks, clipped at the user's first token.
 __device__ __forceinline__ int window_start(int row, int B, int W) {

@@ -33,6 +33,7 @@ import numpy as np
 
 STREAM_LENGTHS, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = 0, 1, 2, 3, 4
 STREAM_QMX, STREAM_QSC, STREAM_KMX, STREAM_KSC = 5, 6, 7, 8
+STREAM_VMX, STREAM_VSC = 9, 10
 
 
 def rng(workload: int, stream: int) -> np.random.Generator:
@@ -56,6 +57,7 @@ class Workload:
     rope_base: float = 0.0   # >0: rotary embedding of q and k with this base
     act: int = 0             # 0 softmax; 1 SiLU, 2 GELU (generalized dot-product attention)
     mx: bool = False         # q and k as MXFP8 codes and block scales
+    mx_v: bool = False       # v too (scales along tokens), weights quantized for P.V
 
     @property
     def scale(self) -> float:
@@ -161,6 +163,13 @@ WORKLOADS = {
     8: Workload(3, "jagged-bf16-train-gdpa-silu", users=256, heads=8, head_dim=64,
                 block_size=128, window_blocks=2, dtype="bf16", backward=True,
                 dout_wid=5, act=1),
+    # The long-context and jagged forwards with q, k and v in MXFP8 and the
+    # softmax weights quantized for a block-scaled P.V product.
+    13: Workload(4, "long-context-mxfp8", users=32, heads=8, head_dim=128,
+                 block_size=256, window_blocks=4, dtype="bf16", backward=False,
+                 fixed_length=16384, mx=True, mx_v=True),
+    14: Workload(3, "jagged-mxfp8", users=256, heads=8, head_dim=64, block_size=128,
+                 window_blocks=2, dtype="bf16", backward=False, mx=True, mx_v=True),
     # The training step at a local batch of 1024 users (the pages put local
     # batches above 1,000 samples), same length law and shapes.
     12: Workload(12, "jagged-bf16-1024-train", users=1024, heads=8, head_dim=64,
@@ -195,8 +204,11 @@ def draw(w: Workload, users=None):
                "q_mx": mx_codes(w.wid, STREAM_QMX, shape),
                "q_sc": mx_scales(w.wid, STREAM_QSC, sshape),
                "k_mx": mx_codes(w.wid, STREAM_KMX, shape),
-               "k_sc": mx_scales(w.wid, STREAM_KSC, sshape),
-               "v": normal(w.wid, STREAM_V, shape)}
+               "k_sc": mx_scales(w.wid, STREAM_KSC, sshape)}
+        if w.mx_v:
+            out.update(mx_v_draw(w.wid, T, w.heads, w.head_dim))
+        else:
+            out["v"] = normal(w.wid, STREAM_V, shape)
     else:
         out = {"offsets": off,
                "q": normal(w.wid, STREAM_Q, shape),
@@ -209,8 +221,31 @@ def draw(w: Workload, users=None):
     return out
 
 
+def mx_v_draw(wid: int, T: int, heads: int, head_dim: int, scales=(119, 121), codes=None):
+    """v as MXFP8 blocked along the packed token axis: codes ``v_mx`` uint8
+    [T, H, D] (the mx_codes draw, or ``codes`` = mx_codes_all) and block
+    scales ``v_bsc`` uint8 [ceil(T/32), H, D], scale (b, h, d) covering
+    tokens 32b .. 32b + 31 of column (h, d)."""
+    fn = mx_codes if codes is None else codes
+    return {"v_mx": fn(wid, STREAM_VMX, (T, heads, head_dim)),
+            "v_bsc": mx_scales(wid, STREAM_VSC, (-(-T // 32), heads, head_dim), *scales)}
+
+
+def mx_v_device_layout(v_mx: np.ndarray, v_bsc: np.ndarray):
+    """The C ABI's layout of token-blocked MXFP8 v: codes transposed to
+    [H, D, 32 ceil(T/32)] (padding: code 0, i.e. +0) and scales to
+    [H, ceil(T/32), D]."""
+    T, H, D = v_mx.shape
+    tp = 32 * (-(-T // 32))
+    vt = np.zeros((H, D, tp), np.uint8)
+    vt[:, :, :T] = v_mx.transpose(1, 2, 0)
+    return vt, np.ascontiguousarray(v_bsc.transpose(1, 0, 2))
+
+
 def subset_users(tensors: dict, users: slice) -> dict:
-    """Keep a contiguous range of users (rows and re-based offsets)."""
+    """Keep a contiguous range of users (rows and re-based offsets).  Token
+    block scales (keys ending in ``_bsc``) stay whole, and ``first_token``
+    records the range's packed start, which indexes them."""
     off = tensors["offsets"]
     idx = np.arange(len(off) - 1)[users]
     if len(idx) == 0:
@@ -222,8 +257,13 @@ def subset_users(tensors: dict, users: slice) -> dict:
     res = {"offsets": (off[idx[0]: idx[-1] + 2] - lo).astype(np.int32)
            if len(idx) else np.zeros(1, np.int32)}
     for key, val in tensors.items():
-        if key != "offsets":
+        if key == "first_token":
+            continue
+        if key.endswith("_bsc"):
+            res[key] = val
+        elif key != "offsets":
             res[key] = val[lo:hi]
+    res["first_token"] = int(tensors.get("first_token", 0)) + lo
     return res
 
 
@@ -265,3 +305,18 @@ def random_mx_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
             "q_mx": mx_codes(wid, STREAM_QMX, shape), "q_sc": mx_scales(wid, STREAM_QSC, sshape),
             "k_mx": mx_codes(wid, STREAM_KMX, shape), "k_sc": mx_scales(wid, STREAM_KSC, sshape),
             "v": normal(wid, STREAM_V, shape)}
+
+
+def random_mxpv_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
+    """random_mx_case with v as token-blocked MXFP8 too (mx_v_draw) in place
+    of the bf16 v; wide = ((q_lo, q_hi), (k_lo, k_hi), (v_lo, v_hi)) draws
+    every finite code with those scale ranges."""
+    c = random_mx_case(seed, lengths, heads, head_dim,
+                       wide=None if wide is None else wide[:2])
+    del c["v"]
+    T = int(c["offsets"][-1])
+    if wide is None:
+        c.update(mx_v_draw(2000 + seed, T, heads, head_dim))
+    else:
+        c.update(mx_v_draw(2000 + seed, T, heads, head_dim, scales=wide[2], codes=mx_codes_all))
+    return c

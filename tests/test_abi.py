@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 7
+    assert lsb.blockattn_abi_version() == 8
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -208,3 +208,22 @@ def test_workspace_size():
     assert lsb.blockattn_bwd_workspace_size(-1, 1, 8, lsb.BF16) == bad
     assert lsb.blockattn_bwd_workspace_size(10, -1, 8, lsb.BF16) == bad
     assert lsb.blockattn_bwd_workspace_size(10, 1, 0, lsb.BF16) == bad
+
+
+def test_mxpv_argument_checks():
+    """blockattn_mxpv_fwd: D 64 or 128, D * Tp below 2^32, v_t and v_scale
+    present and aligned; empty calls succeed before any pointer is looked at."""
+    a = dict(q=FAKE, q_scale=FAKE, k=FAKE, k_scale=FAKE, v_t=FAKE, v_scale=FAKE, offsets=FAKE,
+             batch=2, total_tokens=100, num_heads=2, head_dim=32, block_size=64,
+             window_blocks=2, scale=0.125, out=FAKE, lse=FAKE, stream=None)
+    assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.ERR_UNSUPPORTED    # D = 32
+    a.update(head_dim=128, total_tokens=(1 << 25))     # 128 * 2^25 = 2^32
+    assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.ERR_UNSUPPORTED
+    a.update(total_tokens=100, v_scale=FAKE + 2)
+    assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(v_scale=FAKE, v_t=FAKE + 8)
+    assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(v_t=None)
+    assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
+    a.update(v_t=FAKE, total_tokens=0)
+    assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.OK
