@@ -50,13 +50,24 @@ def pairs_per_head(offsets: np.ndarray, B: int, W: int) -> int:
     return total
 
 
+def source_code(text: str) -> str:
+    """C/HIP source without its comments, trailing blanks and empty lines:
+    what the compiler sees (the sources hold no string literals with comment
+    markers), so an edit to a comment leaves the hash of the kernels alone."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel and ABI sources' code (comments excluded), which
+    the committed profile summaries record."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         p = os.path.join(ROOT, "long_sequence_block_amd", "csrc", name)
         if os.path.exists(p):
             h.update(name.encode())
-            h.update(open(p, "rb").read())
+            h.update(source_code(open(p).read()).encode())
     return h.hexdigest()[:16]
 
 

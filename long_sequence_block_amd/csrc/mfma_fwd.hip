@@ -9,8 +9,8 @@
 // Work split.  A workgroup of 4 waves owns 128 consecutive rows of one user
 // and one head; each wave owns 32 of them (which 32 rotates with the tile so
 // that the causal imbalance between waves does not always land on the same
-// SIMD).  Every row carries its own window start, so any B that is a
-// multiple of 16 works.  Keys are streamed in chunks of 64 from the window
+// SIMD).  Every row carries its own window start, so any B >= 1 works.
+// Keys are streamed in chunks of 64 from the window
 // start of the tile's first row.  Each chunk's K and V rows go from HBM
 // straight into LDS tiles (lds_tile.h) through buffer loads sized to the
 // chunk's valid rows (keys past the tile's last row arrive as zeros); NB
@@ -46,8 +46,9 @@ constexpr int kKC = 64;        // keys per staged chunk
 
 // LDS tiles in rotation (two: a small footprint lets more workgroups share a
 // CU, which hides more latency than a deeper prefetch), and waves per SIMD the
-// register budget is sized for (the quantized-weights variant holds both
-// halves' scores and the v operands of a chunk at once).
+// register budget is sized for (at D = 128 the quantized-weights variant
+// fits three: it keeps one half-chunk's scores live at a time and its chunk
+// buffers are half the bf16 size).
 template <int D>
 constexpr int kBufs = 2;
 template <int D, int MX = 0>
@@ -66,7 +67,8 @@ struct FwdChunk {
 // an in-bounds probe on gfx950: lane (m, g) holds 16 bytes of each of the
 // two blocks, and the scale of (row m, block j) comes from lane m + 32j.
 // Those 16-byte reads are exactly the granule reads of a bf16 tile of D/2
-// columns, so the fp8 K tile uses that geometry and its DMA offsets as is.
+// columns, so the fp8 K tile uses that geometry, with the swizzle of tiles
+// read only by row reads (lds_tile.h, SW = 1).
 //
 // MX = 2 takes v in MXFP8 too and quantizes the softmax weights for a
 // block-scaled P.V product ("GEM (Meta)", sections "Custom kernels" and
@@ -85,7 +87,9 @@ struct FwdChunk {
 // weight's code depends only on its own block: with F = floor(block max of
 // s c), the weight p = 2^(s c - m) is stored as 2^(F - 7 - m) times the
 // nearest E4M3 value of p 2^(m - F + 7) = 2^(s c - F + 7) < 2^8.  The row
-// sum and lse use the unquantized weights.
+// sum and lse use the unquantized weights.  The two halves of a chunk are
+// worked through in turn (one half's scores live at a time); a rescale
+// between them moves the first half's block exponent, not its codes.
 //
 // UPT: users per thread in each pass of the tile decode (4 for batches above
 // 1024 users, chosen by the host, which knows the batch size).
