@@ -72,11 +72,10 @@ def _load():
     lib.oracle_set_num_threads.restype = None
     lib.oracle_e4m3_round.argtypes = [f64]
     lib.oracle_e4m3_round.restype = ctypes.c_double
-    lib.oracle_mxpv_fwd.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, i64, dp,
-                                    dp]
+    lib.oracle_mxpv_fwd.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, dp, dp]
     lib.oracle_mxpv_fwd.restype = ctypes.c_int
-    lib.oracle_mxpv_slack.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, i64,
-                                      dp, dp]
+    lib.oracle_mxpv_slack.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, dp,
+                                      dp]
     lib.oracle_mxpv_slack.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -247,17 +246,26 @@ def mx_decode(codes, scales) -> np.ndarray:
     return _E4M3[codes] * np.repeat(f, 32, axis=-1)
 
 
-def mx_decode_tokens(codes, scales, first_token: int = 0) -> np.ndarray:
-    """fp64 values of MXFP8 data blocked along the packed token axis: codes
-    uint8 [n, H, D] for tokens first_token .. first_token + n - 1, scales
-    uint8 [nblocks, H, D], scale (b, h, d) covering tokens 32b .. 32b + 31
-    of column (h, d) (the blocks of the whole tensor, indexed by packed
-    token)."""
+def user_block_base(offsets) -> np.ndarray:
+    """First 32-token block of each user in user-blocked MXFP8 data:
+    ceil(offsets[u] / 32) + u, so user u's blocks (ceil(L_u / 32) of them)
+    never meet the next user's; [batch] int64."""
+    off = np.asarray(offsets, np.int64)
+    return -(-off[:-1] // 32) + np.arange(len(off) - 1)
+
+
+def mx_decode_user_blocks(codes, scales, offsets) -> np.ndarray:
+    """fp64 values of MXFP8 data blocked along each user's tokens: codes
+    uint8 [T, H, D], scales uint8 [nblocks, H, D]; local token j of user u
+    has scale row user_block_base(offsets)[u] + j // 32."""
     codes, scales = np.asarray(codes, np.uint8), np.asarray(scales, np.uint8)
-    n = codes.shape[0]
-    blk = (int(first_token) + np.arange(n)) // 32
-    if n and (blk[-1] >= scales.shape[0] or codes.shape[1:] != scales.shape[1:]):
-        raise ValueError("scales [ceil(T/32), H, D] for codes [T, H, D]")
+    off = np.asarray(offsets, np.int64)
+    blk = np.zeros(codes.shape[0], np.int64)
+    base = user_block_base(off)
+    for u in range(len(off) - 1):
+        blk[off[u]:off[u + 1]] = base[u] + np.arange(off[u + 1] - off[u]) // 32
+    if len(blk) and (blk.max() >= scales.shape[0] or codes.shape[1:] != scales.shape[1:]):
+        raise ValueError("scales [nblocks, H, D] cover every user's blocks")
     sc = scales[blk]
     f = np.where(sc == 255, np.nan, np.ldexp(1.0, sc.astype(np.int64) - 127))
     return _E4M3[codes] * f
@@ -270,26 +278,22 @@ def e4m3_round(x) -> np.ndarray:
     return np.array([f(float(v)) for v in x.ravel()], np.float64).reshape(x.shape)
 
 
-def mxpv_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
-             first_token: int = 0):
+def mxpv_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float):
     """Forward with the weights quantized to MXFP8 for the P.V product
-    (blockattn_oracle.c: oracle_mxpv_fwd): (out [T, H, D], lse [H, T]).
-    first_token: packed index of these arrays' token 0 (weight blocks are
-    32 packed tokens)."""
+    (blockattn_oracle.c: oracle_mxpv_fwd): (out [T, H, D], lse [H, T])."""
     q, k, v, off = _f64(q), _f64(k), _f64(v), _i32(offsets)
     T, H, D = q.shape
     out = np.zeros((T, H, D), np.float64)
     lse = np.zeros((H, T), np.float64)
     rc = _load().oracle_mxpv_fwd(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
-                                 int(block_size), int(window_blocks), float(scale),
-                                 int(first_token), _dp(out), _dp(lse))
+                                 int(block_size), int(window_blocks), float(scale), _dp(out),
+                                 _dp(lse))
     if rc != 0:
         raise ValueError(f"oracle_mxpv_fwd failed with status {rc}")
     return out, lse
 
 
-def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: float, eps2,
-               first_token: int = 0):
+def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: float, eps2):
     """Per-element parity allowance [T, H, D] of mxpv_fwd's out for a
     computation whose t_ij = s_ij log2(e) are off by at most eps2 [H, T]
     (blockattn_oracle.c: oracle_mxpv_slack).  Test support."""
@@ -298,8 +302,8 @@ def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: flo
     e = _f64(np.broadcast_to(np.asarray(eps2, np.float64), (H, T)))
     sl = np.zeros((T, H, D), np.float64)
     rc = _load().oracle_mxpv_slack(_dp(q), _dp(k), _dp(v), _ip(off), len(off) - 1, T, H, D,
-                                   int(block_size), int(window_blocks), float(scale),
-                                   int(first_token), _dp(e), _dp(sl))
+                                   int(block_size), int(window_blocks), float(scale), _dp(e),
+                                   _dp(sl))
     if rc != 0:
         raise ValueError(f"oracle_mxpv_slack failed with status {rc}")
     return sl

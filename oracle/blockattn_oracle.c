@@ -455,11 +455,10 @@ int oracle_gdpa_bwd_abs(const double *q, const double *k, const double *v,
  *     scores s_ij, visibility and lse are those of oracle_fwd;
  *   - with t_ij = s_ij log2(e), a weight is 2^t_ij up to a factor common to
  *     the row, which cancels;
- *   - the keys of a query fall into blocks of 32 consecutive positions of
- *     the packed token axis (block index = packed token / 32, where the
- *     packed index of token t of these arrays is tok_base + t, so that a
- *     range of users can be checked on its own; a block may hold keys the
- *     query does not see, which weigh 0);
+ *   - the keys of a query fall into blocks of 32 consecutive positions
+ *     counted from its user's first token (block index = local key / 32),
+ *     so a user's result does not depend on the other users of the batch;
+ *     a block may hold keys the query does not see, which weigh 0;
  *   - in block b, with F_b = floor(max of t_ij over its visible keys), each
  *     visible weight is stored as 2^(F_b - 7) * R(2^(t_ij - F_b + 7)), R the
  *     nearest E4M3 value, ties to the even code.  The argument stays below
@@ -485,9 +484,8 @@ double oracle_e4m3_round(double x)
     return ldexp(rint(ldexp(x, -q)), q);      /* rint: nearest, ties even */
 }
 
-/* The block maxima F_b of row i: t[0..n) are the row's t_ij for keys
- * j0 .. j0 + n - 1, g0 their first global token index; fb[] gets F of each
- * key's block. */
+/* The block maxima F_b of row i: t[0..n) are the row's t_ij for local keys
+ * j0 .. j0 + n - 1; fb[] gets F of each key's block. */
 static void block_floor(const double *t, int64_t n, int64_t g0, double *fb)
 {
     int64_t a = 0;
@@ -510,8 +508,7 @@ static void block_floor(const double *t, int64_t n, int64_t g0, double *fb)
 /* Forward with quantized weights: out [T,H,D], lse [H,T]. */
 int oracle_mxpv_fwd(const double *q, const double *k, const double *v,
                     const int32_t *offsets, int batch, int64_t T, int H, int D,
-                    int B, int W, double scale, int64_t tok_base, double *out,
-                    double *lse)
+                    int B, int W, double scale, double *out, double *lse)
 {
     if (check_args(offsets, batch, T, H, D, B, W))
         return -1;
@@ -548,7 +545,7 @@ int oracle_mxpv_fwd(const double *q, const double *k, const double *v,
                 /* weights relative to 2^M, M = floor of the row maximum
                  * (an integer shift, which changes no code) */
                 const double M = floor(m);
-                block_floor(t, n, tok_base + t0 + j0, fb);
+                block_floor(t, n, j0, fb);
                 double l = 0.0;
                 for (int64_t x = 0; x < n; ++x)
                     l += exp2(t[x] - M);
@@ -582,8 +579,7 @@ int oracle_mxpv_fwd(const double *q, const double *k, const double *v,
  * change of Pq_ij those flips allow (0 for a weight no flip can reach). */
 int oracle_mxpv_slack(const double *q, const double *k, const double *v,
                       const int32_t *offsets, int batch, int64_t T, int H, int D,
-                      int B, int W, double scale, int64_t tok_base, const double *eps2,
-                      double *slack)
+                      int B, int W, double scale, const double *eps2, double *slack)
 {
     if (check_args(offsets, batch, T, H, D, B, W))
         return -1;
@@ -619,7 +615,7 @@ int oracle_mxpv_slack(const double *q, const double *k, const double *v,
                         m = t[x];
                 }
                 const double M = floor(m);
-                block_floor(t, n, tok_base + t0 + j0, fb);
+                block_floor(t, n, j0, fb);
                 /* the unquantized normaliser, at its smallest */
                 double l = 0.0;
                 for (int64_t x = 0; x < n; ++x)
@@ -630,7 +626,7 @@ int oracle_mxpv_slack(const double *q, const double *k, const double *v,
                 for (int64_t x = 0; x < n; ++x) {
                     /* is the block's maximum within e of an integer? */
                     int64_t a = x;
-                    const int64_t g = tok_base + t0 + j0; /* packed index of key x = 0 */
+                    const int64_t g = j0; /* local index of key x = 0 */
                     while (a > 0 && (g + a - 1) / 32 == (g + x) / 32)
                         --a;
                     double bm = -INFINITY;

@@ -841,7 +841,9 @@ def test_mxpv_small_weights_use_their_blocks_exponent():
     in the subnormal range: 3 * 2^-9, weight 3 * 2^-16.  With key 0 at
     t = -0.5 the block's F is floor(-0.5) = -1, and key 1 at t = -14.8 gives
     2^-6.8 = 0.00897, i.e. 5 * 2^-9 (4.59 quanta), weight 5 * 2^-17 (F = 0
-    would give 2 quanta at 2^-7: 4 * 2^-17)."""
+    would give 2 quanta at 2^-7: 4 * 2^-17).  Blocks count from the user's
+    first token: behind a 5-token user, local key 27 still shares block 0
+    with key 0, and local key 32 is still alone in block 1."""
     def run(pos, t0, tp, pre=0):
         # (pre: tokens of an earlier user, which move the packed positions)
         q = np.zeros((pre + 33, 1, 2))
@@ -860,9 +862,8 @@ def test_mxpv_small_weights_use_their_blocks_exponent():
     assert run(32, 0.0, -14.3) == pytest.approx(208 * 2.0 ** -22, rel=1e-12)
     assert run(1, 0.0, -14.3) == pytest.approx(3 * 2.0 ** -16, rel=1e-12)
     assert run(1, -0.5, -14.8) == pytest.approx(5 * 2.0 ** -17, rel=1e-12)
-    # blocks follow the packed token axis: behind a 5-token user, local key
-    # 27 is token 32, alone in its block (local 1 .. 26 are token 6 .. 31)
-    assert run(27, 0.0, -14.3, pre=5) == pytest.approx(208 * 2.0 ** -22, rel=1e-12)
+    assert run(27, 0.0, -14.3, pre=5) == pytest.approx(3 * 2.0 ** -16, rel=1e-12)
+    assert run(32, 0.0, -14.3, pre=5) == pytest.approx(208 * 2.0 ** -22, rel=1e-12)
 
 
 def test_mxpv_keys_outside_the_window_do_not_matter():
@@ -906,31 +907,34 @@ def test_mxpv_slack_covers_perturbed_scores():
     assert hits > 0   # some codes did flip, and the slack covered them
 
 
-def test_mxpv_user_range_keeps_packed_blocks():
-    """Checking a range of users on its own gives the whole run's values
-    when first_token names the range's packed start (weight blocks are 32
-    packed tokens); re-based to 0 it would put the block edges elsewhere."""
+def test_mxpv_users_are_independent():
+    """A user's quantized forward does not depend on the rest of the batch:
+    users 1..2 checked on their own (re-based offsets) give the whole run's
+    values, and so do the same users behind other users."""
     lengths = [45, 70, 33]
     c = case(16, lengths, H=2, D=8)
     full, lfull = oracle.mxpv_fwd(c["q"], c["k"], c["v"], c["offsets"], 16, 3, 0.7)
     lo, hi = 45, 148
     sub = wl.subset_users(c, slice(1, 3))
-    part, lpart = oracle.mxpv_fwd(sub["q"], sub["k"], sub["v"], sub["offsets"], 16, 3, 0.7,
-                                  first_token=lo)
+    part, lpart = oracle.mxpv_fwd(sub["q"], sub["k"], sub["v"], sub["offsets"], 16, 3, 0.7)
     np.testing.assert_array_equal(part, full[lo:hi])
     np.testing.assert_array_equal(lpart, lfull[:, lo:hi])
-    moved, _ = oracle.mxpv_fwd(sub["q"], sub["k"], sub["v"], sub["offsets"], 16, 3, 0.7)
-    assert np.abs(moved - full[lo:hi]).max() > 1e-6
+    pre = case(17, [3, 29], H=2, D=8)
+    cat = {n: np.concatenate([pre[n], sub[n]]) for n in ("q", "k", "v")}
+    off = wl.offsets_from_lengths([3, 29] + lengths[1:])
+    moved, _ = oracle.mxpv_fwd(cat["q"], cat["k"], cat["v"], off, 16, 3, 0.7)
+    np.testing.assert_array_equal(moved[32:], full[lo:hi])
 
 
-def test_mx_decode_tokens_blocks_follow_packed_tokens():
-    """Token-blocked decode: code 0x38 (1.0) with scale byte 127 + b for
-    block b gives 2^b on tokens 32b .. 32b + 31, also for a range that
-    starts inside a block."""
-    T = 100
-    codes = np.full((T, 1, 2), 0x38, np.uint8)
-    scales = (127 + np.arange(4, dtype=np.uint8))[:, None, None].repeat(2, axis=2)
-    full = oracle.mx_decode_tokens(codes, scales)
-    np.testing.assert_array_equal(full[:, 0, 0], 2.0 ** (np.arange(T) // 32))
-    part = oracle.mx_decode_tokens(codes[40:70], scales, first_token=40)
-    np.testing.assert_array_equal(part, full[40:70])
+def test_mx_decode_user_blocks():
+    """User-blocked decode: code 0x38 (1.0) with scale byte 127 + r on scale
+    row r gives 2^r; user u's local token j reads row
+    ceil(off[u] / 32) + u + j // 32."""
+    off = np.array([0, 40, 40, 105], np.int32)
+    base = oracle.user_block_base(off)
+    np.testing.assert_array_equal(base, [0, 3, 4])   # ceil(0/32)+0, ceil(40/32)+1, +2
+    codes = np.full((105, 1, 2), 0x38, np.uint8)
+    scales = (127 + np.arange(8, dtype=np.uint8))[:, None, None].repeat(2, axis=2)
+    v = oracle.mx_decode_user_blocks(codes, scales, off)
+    expect = np.concatenate([np.arange(40) // 32, 4 + np.arange(65) // 32])
+    np.testing.assert_array_equal(v[:, 0, 0], 2.0 ** expect)
