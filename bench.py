@@ -122,7 +122,7 @@ def _oracle_inputs(w, users):
     c = wl.draw(w, users=slice(0, users))
     host = {}
     for key, val in c.items():
-        if key in ("offsets", "first_token") or key.endswith("_mx") or key.endswith("_sc"):
+        if key == "offsets" or key.endswith("_mx") or key.endswith("_sc"):
             host[key] = val
         else:
             t = torch.from_numpy(val)
@@ -133,8 +133,8 @@ def _oracle_inputs(w, users):
         host["q"] = oracle.mx_decode(host.pop("q_mx"), host.pop("q_sc"))
         host["k"] = oracle.mx_decode(host.pop("k_mx"), host.pop("k_sc"))
     if w.mx_v:
-        host["v"] = oracle.mx_decode_tokens(host.pop("v_mx"), host.pop("v_bsc"),
-                                            host["first_token"])
+        host["v"] = oracle.mx_decode_user_blocks(host.pop("v_mx"), host.pop("v_bsc"),
+                                                 host["offsets"])
     return host
 
 
@@ -150,7 +150,7 @@ def _oracle_run(w, host):
             oracle.gdpa_bwd(q, k, v, host["dout"], off, B, W, sc, w.act)
         return
     if w.mx_v:  # the weights quantized for P.V
-        oracle.mxpv_fwd(q, k, v, off, B, W, sc, first_token=host["first_token"])
+        oracle.mxpv_fwd(q, k, v, off, B, W, sc)
         return
     if w.rope_base:
         q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
@@ -358,8 +358,8 @@ def main():
                                  else v).to(dev)
              for k, v in c.items() if k in ("offsets", "q_mx", "q_sc", "k_mx", "k_sc")}
         d["q"], d["k"] = d.pop("q_mx"), d.pop("k_mx")
-        if w.mx_v:  # v transposed [H, D, Tp] with scales [H, ceil(T/32), D]
-            vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"])
+        if w.mx_v:  # v transposed, user-blocked [H, D, 32 nb], scales [H, nb, D]
+            vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"], c["offsets"])
             d["v_t"], d["v_bsc"] = torch.from_numpy(vt).to(dev), torch.from_numpy(vs).to(dev)
         else:
             d["v"] = torch.from_numpy(c["v"]).to(tdt).to(dev)

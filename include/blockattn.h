@@ -258,24 +258,26 @@ blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
  * "Custom kernels") and the matmuls in block-scaled MXFP8 end to end
  * (section "Ultra-low-precision training"), which for P.V means the softmax
  * weights are quantized as well.  Reading: each query's weights fall into
- * blocks of 32 packed token positions; with F the floor of the block's
- * largest s * log2(e), a weight 2^(s log2 e) (relative to the row) is
- * stored as 2^(F - 7) times the nearest E4M3 value of 2^(s log2 e - F + 7)
- * (ties to even; below 2^8, so nothing saturates).  The row sum and lse use
- * the unquantized weights.  v's scales run along the P.V contraction, the
- * token axis, so v comes transposed:
+ * blocks of 32 keys counted from its user's first token; with F the floor
+ * of the block's largest s * log2(e), a weight 2^(s log2 e) (relative to
+ * the row) is stored as 2^(F - 7) times the nearest E4M3 value of
+ * 2^(s log2 e - F + 7) (ties to even; below 2^8, so nothing saturates).
+ * The row sum and lse use the unquantized weights.  v's scales run along
+ * the P.V contraction, each user's tokens, so v comes transposed and
+ * blocked by user (NB = ceil(T / 32) + batch; user u's blocks start at
+ * ub = ceil(offsets[u] / 32) + u, so users never share a block):
  *   q, k, q_scale, k_scale   as for blockattn_mx_fwd
- *   v_t      E4M3 bytes [H, D, Tp], Tp = 32 * ceil(T / 32): row (h, d)
- *            holds column d of head h for tokens 0 .. T-1 (the rest is
- *            padding); 16-byte aligned
- *   v_scale  E8M0 bytes [H, ceil(T / 32), D], 4-byte aligned: element
- *            (t, h, d) has scale [h][t / 32][d]
+ *   v_t      E4M3 bytes [H, D, 32 * NB], 16-byte aligned: local token j of
+ *            user u, column d of head h, at [h][d][32 ub + j]; the columns
+ *            no token uses are padding
+ *   v_scale  E8M0 bytes [H, NB, D], 4-byte aligned: that element's scale
+ *            is [h][ub + j / 32][d]
  *   out      bf16 [T, H, D];  lse fp32 [H, T]
- * A chunk of 64 keys starts on a multiple of 32 packed tokens, so the
- * products read v's codes and scales of whole 32-token blocks around a
- * window, including other users' tokens and the padding: every code of v_t
- * (padding included) must be finite and no scale may be 255 (NaN), or NaN
- * can reach unrelated rows.  D must be 64 or 128 and D * Tp below 2^32,
+ * A chunk of 64 keys starts on a multiple of 32 of the user's tokens, so
+ * the products also read codes and scales just past a user's last token
+ * (its padding, the next user's first block): every code of v_t (padding
+ * included) must be finite and no scale may be 255 (NaN), or NaN can reach
+ * unrelated rows.  D must be 64 or 128 and D * 32 * NB below 2^32,
  * else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments and errors as for
  * blockattn_fwd.  The block-scaled products sum with fewer bits than fp32
  * (see blockattn_mx_fwd).  There is no MXFP8 backward.

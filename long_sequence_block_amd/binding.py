@@ -480,11 +480,12 @@ def mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, block_size: int,
              window_blocks: int, scale: float, out=None, lse=None, stream=None):
     """Forward with q, k and v in MXFP8 and the weights quantized for P.V
     (blockattn_mxpv_fwd): q, k uint8 [T, H, D] and q_scale, k_scale uint8
-    [H, T, D/32] as for mx_fwd; v_t uint8 [H, D, 32 ceil(T/32)] (v
-    transposed, padded with finite codes); v_scale uint8 [H, ceil(T/32), D].
+    [H, T, D/32] as for mx_fwd; v_t uint8 [H, D, 32 nb] (v transposed and
+    blocked by user, padding with finite codes) and v_scale uint8 [H, nb, D]
+    with nb = ceil(T/32) + batch (workloads.mx_v_device_layout builds them).
     Returns (out bf16 [T, H, D], lse fp32 [H, T])."""
     T, H, D = q.shape
-    nb = -(-T // 32)
+    nb = -(-T // 32) + offsets.numel() - 1
     for t in (q, k):
         if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
             raise ValueError("q and k must be contiguous uint8 [T, H, D] device tensors")
@@ -492,9 +493,9 @@ def mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, block_size: int,
         if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
             raise ValueError("q_scale and k_scale must be contiguous uint8 [H, T, D/32]")
     if v_t.dtype != torch.uint8 or v_t.shape != (H, D, 32 * nb) or not v_t.is_contiguous():
-        raise ValueError("v_t must be a contiguous uint8 [H, D, 32 ceil(T/32)] tensor")
+        raise ValueError("v_t must be a contiguous uint8 [H, D, 32 (ceil(T/32) + batch)] tensor")
     if v_scale.dtype != torch.uint8 or v_scale.shape != (H, nb, D) or not v_scale.is_contiguous():
-        raise ValueError("v_scale must be a contiguous uint8 [H, ceil(T/32), D] tensor")
+        raise ValueError("v_scale must be a contiguous uint8 [H, ceil(T/32) + batch, D] tensor")
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
         out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device) if out is None else out

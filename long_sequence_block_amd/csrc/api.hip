@@ -321,7 +321,7 @@ blockattn_status blockattn_mxpv_fwd(const void *q, const void *q_scale, const vo
     if (st != BLOCKATTN_OK) return st;
     if (head_dim != 64 && head_dim != 128) return BLOCKATTN_ERR_UNSUPPORTED;
     // v^T rows are addressed with 32-bit byte offsets
-    const int64_t tp = (total_tokens + 31) / 32 * 32;
+    const int64_t tp = ((total_tokens + 31) / 32 + batch) * 32;
     if ((int64_t)head_dim * tp >= ((int64_t)1 << 32)) return BLOCKATTN_ERR_UNSUPPORTED;
     if (empty) return BLOCKATTN_OK;
     if (!q || !q_scale || !k || !k_scale || !v_t || !v_scale || !out || !lse)

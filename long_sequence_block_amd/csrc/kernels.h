@@ -31,9 +31,10 @@ hipError_t launch_mfma_fwd_mx(const Shape &s, const void *q, const void *q_scale
                               hipStream_t st);
 
 // Forward with q, k and v in MXFP8 and the softmax weights quantized for a
-// block-scaled P.V product: q, k as above; v^T E4M3 [H, D, Tp] with
-// Tp = 32 ceil(T/32), v scales E8M0 [H, ceil(T/32), D] (one per 32 packed
-// tokens of a column).  D 64 or 128; D * Tp < 2^32.
+// block-scaled P.V product: q, k as above; v^T E4M3 [H, D, 32 NB] with
+// NB = ceil(T/32) + batch, user u's local token j at column
+// 32 (ceil(off[u]/32) + u) + j; v scales E8M0 [H, NB, D] (one per 32 tokens
+// of a user's column).  D 64 or 128; D * 32 NB < 2^32.
 hipError_t launch_mfma_fwd_mxpv(const Shape &s, const void *q, const void *q_scale,
                                 const void *k, const void *k_scale, const void *v_t,
                                 const void *v_scale, void *out, float *lse, hipStream_t st);

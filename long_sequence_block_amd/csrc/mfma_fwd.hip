@@ -73,12 +73,14 @@ struct FwdChunk {
 // MX = 2 takes v in MXFP8 too and quantizes the softmax weights for a
 // block-scaled P.V product ("GEM (Meta)", sections "Custom kernels" and
 // "Ultra-low-precision training": MXFP8 block-scaled matmuls end to end).
-// v arrives transposed, E4M3 [H, D, Tp] (Tp = 32 ceil(T/32); row (h, d)
-// holds that column's tokens) with E8M0 scales [H, ceil(T/32), D], one per
-// 32 packed tokens of a column: the scales run along the P.V contraction.
-// Chunks then start on a multiple of 32 packed tokens (keys before the
-// window are masked), so each 32-key half of a chunk is one scale block of
-// v and of the weights, and one 32x32x64 product takes a whole chunk.  K
+// v arrives transposed and blocked by user: E4M3 [H, D, 32 NB] with
+// NB = ceil(T/32) + batch, user u's local token j at column 32 ub + j with
+// ub = ceil(off[u] / 32) + u (so users never share a 32-token block), and
+// E8M0 scales [H, NB, D], one per 32 tokens of a user's column: the scales
+// run along the P.V contraction.  Chunks then start on a multiple of 32
+// local tokens (keys before the window are masked), so each 32-key half of
+// a chunk is one scale block of v and of the weights, and one 32x32x64
+// product takes a whole chunk.  K
 // rows sit at LDS row rho(m) (mfma_util.h), so a lane's 16 score registers
 // of a half are keys 16g .. 16g + 15: in register order they are the
 // lane's bytes of the weights' operand.  v^T rows are plain 16-byte row
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(kThreads, (kWavesPerSimd<D, MX>)) void fwd_mfma(
                               : (ACT == kSoftmax && s.scale < 0.f ? 0x80008000u : 0u);
 
     const int kwin = window_start(row0, s.B, s.W);
-    // (MX = 2: back to a multiple of 32 packed tokens)
-    const int kbeg = MX == 2 ? kwin - ((t.tok0 + kwin) & 31) : kwin;
+    // (MX = 2: back to a multiple of 32 local tokens)
+    const int kbeg = MX == 2 ? kwin - (kwin & 31) : kwin;
     const int nch = (row_end - kbeg + kKC - 1) / kKC;
     // fp8 rows are addressed in bf16 units (half their byte offsets)
     const int64_t rs8 = rs / 2;
@@ -152,11 +154,12 @@ __global__ __launch_bounds__(kThreads, (kWavesPerSimd<D, MX>)) void fwd_mfma(
     uint32_t voff8[G8::kDmaPerWave];
     if constexpr (MX)
         dma_offsets<G8::kRowBytes / 2, MX == 2, 1>(voff8, wave, lane, (uint32_t)(rs8 * 2));
-    // MX = 2: v^T rows of this head from the chunk's first key (byte
-    // offsets), and their scales
-    const int64_t Tp = (s.T + 31) / 32 * 32, nblk = Tp / 32;
-    const int64_t vb8 = (int64_t)t.h * D * Tp + t.tok0 + kbeg;
-    const int64_t vs0 = ((int64_t)t.h * nblk + (t.tok0 + kbeg) / 32) * D;
+    // MX = 2: v^T rows of this head from the tile's first key (byte
+    // offsets; the user's columns start at 32 ub), and their scales
+    const int64_t nblk = (s.T + 31) / 32 + s.batch, Tp = 32 * nblk;
+    const int64_t ub = (t.tok0 + 31) / 32 + t.user;
+    const int64_t vb8 = (int64_t)t.h * D * Tp + 32 * ub + kbeg;
+    const int64_t vs0 = ((int64_t)t.h * nblk + ub + kbeg / 32) * D;
     uint32_t voffv[1];
     if constexpr (MX == 2) dma_offsets<32, false, 1>(voffv, wave, lane, (uint32_t)Tp);
     // Scales of chunk ci: a dword-aligned window starts `mis` bytes before

@@ -206,7 +206,7 @@ def draw(w: Workload, users=None):
                "k_mx": mx_codes(w.wid, STREAM_KMX, shape),
                "k_sc": mx_scales(w.wid, STREAM_KSC, sshape)}
         if w.mx_v:
-            out.update(mx_v_draw(w.wid, T, w.heads, w.head_dim))
+            out.update(mx_v_draw(w.wid, off, w.heads, w.head_dim))
         else:
             out["v"] = normal(w.wid, STREAM_V, shape)
     else:
@@ -221,31 +221,52 @@ def draw(w: Workload, users=None):
     return out
 
 
-def mx_v_draw(wid: int, T: int, heads: int, head_dim: int, scales=(119, 121), codes=None):
-    """v as MXFP8 blocked along the packed token axis: codes ``v_mx`` uint8
+def user_block_base(offsets) -> np.ndarray:
+    """First 32-token block of each user in user-blocked MXFP8 data:
+    ceil(offsets[u] / 32) + u, so user u's ceil(L_u / 32) blocks never meet
+    the next user's (index arithmetic only)."""
+    off = np.asarray(offsets, np.int64)
+    return -(-off[:-1] // 32) + np.arange(len(off) - 1)
+
+
+def mx_v_blocks(offsets) -> int:
+    """Block rows of user-blocked MXFP8 data: ceil(T / 32) + batch."""
+    off = np.asarray(offsets, np.int64)
+    return int(-(-off[-1] // 32)) + len(off) - 1
+
+
+def mx_v_draw(wid: int, offsets, heads: int, head_dim: int, scales=(119, 121), codes=None):
+    """v as MXFP8 blocked along each user's tokens: codes ``v_mx`` uint8
     [T, H, D] (the mx_codes draw, or ``codes`` = mx_codes_all) and block
-    scales ``v_bsc`` uint8 [ceil(T/32), H, D], scale (b, h, d) covering
-    tokens 32b .. 32b + 31 of column (h, d)."""
+    scales ``v_bsc`` uint8 [ceil(T/32) + batch, H, D]; local token j of user
+    u has scale row user_block_base(offsets)[u] + j // 32."""
     fn = mx_codes if codes is None else codes
+    T = int(np.asarray(offsets)[-1])
     return {"v_mx": fn(wid, STREAM_VMX, (T, heads, head_dim)),
-            "v_bsc": mx_scales(wid, STREAM_VSC, (-(-T // 32), heads, head_dim), *scales)}
+            "v_bsc": mx_scales(wid, STREAM_VSC, (mx_v_blocks(offsets), heads, head_dim),
+                               *scales)}
 
 
-def mx_v_device_layout(v_mx: np.ndarray, v_bsc: np.ndarray):
-    """The C ABI's layout of token-blocked MXFP8 v: codes transposed to
-    [H, D, 32 ceil(T/32)] (padding: code 0, i.e. +0) and scales to
-    [H, ceil(T/32), D]."""
+def mx_v_device_layout(v_mx: np.ndarray, v_bsc: np.ndarray, offsets):
+    """The C ABI's layout of user-blocked MXFP8 v: codes transposed to
+    [H, D, 32 (ceil(T/32) + batch)], user u's local token j at column
+    32 user_block_base[u] + j (the rest: code 0, i.e. +0), and scales to
+    [H, ceil(T/32) + batch, D]."""
+    off = np.asarray(offsets, np.int64)
     T, H, D = v_mx.shape
-    tp = 32 * (-(-T // 32))
-    vt = np.zeros((H, D, tp), np.uint8)
-    vt[:, :, :T] = v_mx.transpose(1, 2, 0)
+    nb = mx_v_blocks(off)
+    vt = np.zeros((H, D, 32 * nb), np.uint8)
+    base = user_block_base(off)
+    for u in range(len(off) - 1):
+        a, b = int(off[u]), int(off[u + 1])
+        vt[:, :, 32 * base[u]:32 * base[u] + b - a] = v_mx[a:b].transpose(1, 2, 0)
     return vt, np.ascontiguousarray(v_bsc.transpose(1, 0, 2))
 
 
 def subset_users(tensors: dict, users: slice) -> dict:
-    """Keep a contiguous range of users (rows and re-based offsets).  Token
-    block scales (keys ending in ``_bsc``) stay whole, and ``first_token``
-    records the range's packed start, which indexes them."""
+    """Keep a contiguous range of users (rows and re-based offsets).  User
+    block scales (keys ending in ``_bsc``) are re-indexed for the kept
+    users' new positions."""
     off = tensors["offsets"]
     idx = np.arange(len(off) - 1)[users]
     if len(idx) == 0:
@@ -257,13 +278,16 @@ def subset_users(tensors: dict, users: slice) -> dict:
     res = {"offsets": (off[idx[0]: idx[-1] + 2] - lo).astype(np.int32)
            if len(idx) else np.zeros(1, np.int32)}
     for key, val in tensors.items():
-        if key == "first_token":
-            continue
         if key.endswith("_bsc"):
-            res[key] = val
+            new_off = res["offsets"]
+            out = np.zeros((mx_v_blocks(new_off),) + val.shape[1:], val.dtype)
+            old_base, new_base = user_block_base(off), user_block_base(new_off)
+            for i, u in enumerate(idx):
+                n = -(-int(off[u + 1] - off[u]) // 32)
+                out[new_base[i]:new_base[i] + n] = val[old_base[u]:old_base[u] + n]
+            res[key] = out
         elif key != "offsets":
             res[key] = val[lo:hi]
-    res["first_token"] = int(tensors.get("first_token", 0)) + lo
     return res
 
 
@@ -308,15 +332,15 @@ def random_mx_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
 
 
 def random_mxpv_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
-    """random_mx_case with v as token-blocked MXFP8 too (mx_v_draw) in place
+    """random_mx_case with v as user-blocked MXFP8 too (mx_v_draw) in place
     of the bf16 v; wide = ((q_lo, q_hi), (k_lo, k_hi), (v_lo, v_hi)) draws
     every finite code with those scale ranges."""
     c = random_mx_case(seed, lengths, heads, head_dim,
                        wide=None if wide is None else wide[:2])
     del c["v"]
-    T = int(c["offsets"][-1])
     if wide is None:
-        c.update(mx_v_draw(2000 + seed, T, heads, head_dim))
+        c.update(mx_v_draw(2000 + seed, c["offsets"], heads, head_dim))
     else:
-        c.update(mx_v_draw(2000 + seed, T, heads, head_dim, scales=wide[2], codes=mx_codes_all))
+        c.update(mx_v_draw(2000 + seed, c["offsets"], heads, head_dim, scales=wide[2],
+                           codes=mx_codes_all))
     return c

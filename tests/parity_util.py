@@ -263,7 +263,7 @@ def _compare_by_users(host, gpu, offsets, reference, dtype, max_tokens, log=None
     output already copied to the host ([T, H, D], or [H, T] for names that
     start with "lse"); reference(sub, rows) -> name -> oracle output of the
     range, given sub = {input name: fp64 rows of the range, "offsets": the
-    re-based offsets}."""
+    re-based offsets, "range": (u0, u1, t0, t1), its users and tokens}."""
     off = np.asarray(offsets, np.int64)
     p = Parity(dtype)
     for u0, u1 in user_ranges(off, max_tokens):
@@ -272,6 +272,7 @@ def _compare_by_users(host, gpu, offsets, reference, dtype, max_tokens, log=None
             continue
         sub = {k: host_rows(v, t0, t1) for k, v in host.items() if k != "offsets"}
         sub["offsets"] = (off[u0:u1 + 1] - t0).astype(np.int32)
+        sub["range"] = (u0, u1, t0, t1)
         ref = reference(sub)
         for name, g in gpu.items():
             is_lse = name.startswith("lse")

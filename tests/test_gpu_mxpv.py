@@ -22,7 +22,8 @@ Bounds, on top of the block-attention bounds (parity_util):
     rho sum_j |Pq_ij v_j| / l_i <= rho (1 + 2^-4) sum_j P_ij |v_j| (the
     exact softmax on |v|, plus a little).
 Every element is compared, in the small cases and in both workloads at
-full size (user range by user range, each with its packed first token).
+full size (user range by user range: a user's result does not depend on
+the others).
 """
 import math
 
@@ -46,10 +47,9 @@ def _print(msg):
 
 def mxpv_parity(c, B, W, scale, max_tokens):
     """Run blockattn_mxpv_fwd on case c (q_mx, q_sc, k_mx, k_sc as for the
-    MX forward; v_mx [T, H, D] with token-block scales v_bsc) and compare
+    MX forward; v_mx [T, H, D] with user-block scales v_bsc) and compare
     every element with the oracle."""
-    T = int(c["offsets"][-1])
-    vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"])
+    vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"], c["offsets"])
     dev = {"offsets": torch.from_numpy(c["offsets"]).cuda()}
     for n in ("q", "k"):
         dev[n] = torch.from_numpy(c[n + "_mx"]).cuda()
@@ -60,22 +60,23 @@ def mxpv_parity(c, B, W, scale, max_tokens):
     torch.cuda.synchronize()
     gpu = {"out": out.cpu(), "lse": lse.cpu()}
     del dev, out, lse
-    v_bsc = c["v_bsc"]
+    vfull = {"offsets": c["offsets"], "v_mx": c["v_mx"], "v_bsc": c["v_bsc"]}
     host = {"offsets": c["offsets"], "q_mx": c["q_mx"], "q_sc": c["q_sc"], "k_mx": c["k_mx"],
-            "k_sc": c["k_sc"], "v_mx": c["v_mx"], "tok": np.arange(T, dtype=np.int64)}
+            "k_sc": c["k_sc"]}
     log2e = math.log2(math.e)
 
     def reference(sub):
-        t0 = int(sub["tok"][0])
+        u0, u1 = sub["range"][:2]
         off = sub["offsets"]
         q = oracle.mx_decode(sub["q_mx"], sub["q_sc"])
         k = oracle.mx_decode(sub["k_mx"], sub["k_sc"])
-        v = oracle.mx_decode_tokens(sub["v_mx"], v_bsc, t0)
-        o, l = oracle.mxpv_fwd(q, k, v, off, B, W, scale, first_token=t0)
+        vs_ = wl.subset_users(vfull, slice(u0, u1))   # v's codes and re-indexed block scales
+        v = oracle.mx_decode_user_blocks(vs_["v_mx"], vs_["v_bsc"], off)
+        o, l = oracle.mxpv_fwd(q, k, v, off, B, W, scale)
         _, labs = oracle.fwd(np.abs(q), np.abs(k), v, off, B, W, abs(scale))
         eps = RHO * labs                                          # [H, T], natural log
         eps2 = (eps + 2.0 ** -20 * (labs + 1.0)) * log2e          # log2 domain, fp32 slack
-        slack = oracle.mxpv_slack(q, k, v, off, B, W, scale, eps2, first_token=t0)
+        slack = oracle.mxpv_slack(q, k, v, off, B, W, scale, eps2)
         pabs, _ = oracle.fwd(q, k, np.abs(v), off, B, W, scale)   # sum_j P_ij |v_j|
         vmax = np.abs(v).max() if v.size else 0.0
         extra = (slack + (np.expm1(2.0 * eps) * 1.07 * vmax).T[:, :, None]
@@ -95,7 +96,8 @@ MXPV = [
     ([1000, 16, 17], 1, 128, 256, 4, -1),
     ([301, 0, 78], 1, 64, 64, 2, 1),
     ([129, 254], 3, 64, 16, 4, -1),
-    # users that start off the 32-token grid, a block size not a multiple of 16
+    # users that start off the packed 32-token grid, block sizes that are not
+    # multiples of 32 (windows that start inside a 32-key block)
     ([45, 33, 70, 31, 64], 2, 64, 7, 5, 1),
     ([17, 600, 5], 2, 128, 100, 3, 1),
     # 1101 users: the tile decode's four-users-per-thread form
@@ -139,3 +141,46 @@ def test_mxpv_workload_full_size_every_element(wid):
     c = wl.draw(w)
     p = mxpv_parity(c, w.block_size, w.window_blocks, w.scale, 4 * 16384)
     _print("  " + p.summary())
+
+
+def _concat_users(a, b):
+    """Case a's users followed by case b's, each user's v block scales moved
+    to its new blocks."""
+    off = np.concatenate([a["offsets"], a["offsets"][-1] + b["offsets"][1:]]).astype(np.int32)
+    c = {"offsets": off}
+    for n in ("q_mx", "q_sc", "k_mx", "k_sc", "v_mx"):
+        c[n] = np.concatenate([a[n], b[n]])
+    bsc = np.zeros((wl.mx_v_blocks(off),) + a["v_bsc"].shape[1:], np.uint8)
+    nbase = wl.user_block_base(off)
+    i = 0
+    for part in (a, b):
+        base = wl.user_block_base(part["offsets"])
+        for u in range(len(part["offsets"]) - 1):
+            n = -(-int(part["offsets"][u + 1] - part["offsets"][u]) // 32)
+            bsc[nbase[i]:nbase[i] + n] = part["v_bsc"][base[u]:base[u] + n]
+            i += 1
+    c["v_bsc"] = bsc
+    return c
+
+
+def _run(c, B, W, scale):
+    vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"], c["offsets"])
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out, lse = lsb.mxpv_fwd(d(c["q_mx"]), d(c["q_sc"].transpose(1, 0, 2)), d(c["k_mx"]),
+                            d(c["k_sc"].transpose(1, 0, 2)), d(vt), d(vs), d(c["offsets"]),
+                            B, W, scale)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def test_mxpv_users_are_independent():
+    """A user's output and lse are bitwise the same with other users in
+    front of it (a different packed position, other block bases)."""
+    users = wl.random_mxpv_case(510, [45, 70, 0, 33], 2, 64)
+    pre = wl.random_mxpv_case(511, [3, 29, 1], 2, 64)
+    B, W, scale = 16, 3, 0.125
+    o1, l1 = _run(users, B, W, scale)
+    o2, l2 = _run(_concat_users(pre, users), B, W, scale)
+    n = int(pre["offsets"][-1])
+    assert torch.equal(o1.view(torch.int16), o2[n:].view(torch.int16))
+    assert torch.equal(l1, l2[:, n:])
