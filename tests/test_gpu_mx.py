@@ -88,6 +88,8 @@ MX = [
     # ends inside a dword (read byte by byte)
     ([301, 0, 78], 1, 64, 64, 2, 1),
     ([129, 254], 3, 64, 16, 4, -1),
+    # the largest block and window the ABI takes (clamped: every earlier key)
+    ([300, 77, 0, 5, 130], 2, 128, 2**31 - 1, 2**31 - 1, -1),
     # 1101 users: the tile decode's four-users-per-thread form
     ([int(x) for x in np.random.default_rng(31).integers(0, 30, 1101)], 1, 64, 16, 2, 1),
 ]

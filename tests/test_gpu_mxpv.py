@@ -102,6 +102,8 @@ MXPV = [
     ([17, 600, 5], 2, 128, 100, 3, 1),
     # 1101 users: the tile decode's four-users-per-thread form
     ([int(x) for x in np.random.default_rng(32).integers(0, 30, 1101)], 1, 64, 16, 2, 1),
+    # the largest block and window the ABI takes (clamped: every earlier key)
+    ([300, 77, 0, 5, 130], 2, 64, 2**31 - 1, 2**31 - 1, 1),
 ]
 
 
