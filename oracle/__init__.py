@@ -77,6 +77,14 @@ def _load():
     lib.oracle_mxpv_slack.argtypes = [dp, dp, dp, ip, i32, i64, i32, i32, i32, i32, f64, dp,
                                       dp]
     lib.oracle_mxpv_slack.restype = ctypes.c_int
+    lib.oracle_mx_bwd.argtypes = [dp] * 9 + [ip, i32, i64, i32, i32, i32, i32, f64, i32,
+                                             dp, dp, dp]
+    lib.oracle_mx_bwd.restype = ctypes.c_int
+    lib.oracle_mx_bwd_bounds.argtypes = [dp] * 9 + [ip, i32, i64, i32, i32, i32, i32, f64,
+                                                    f64] + [dp] * 9
+    lib.oracle_mx_bwd_bounds.restype = ctypes.c_int
+    lib.oracle_mx_quantize_block.argtypes = [dp, i64]
+    lib.oracle_mx_quantize_block.restype = None
     _lib = lib
     return lib
 
@@ -307,6 +315,60 @@ def mxpv_slack(q, k, v, offsets, block_size: int, window_blocks: int, scale: flo
     if rc != 0:
         raise ValueError(f"oracle_mxpv_slack failed with status {rc}")
     return sl
+
+
+def _mx_bwd_inputs(q, k, v, dout, out, lse, q_t, k_t, dout_t):
+    q, k, v, do, o = _f64(q), _f64(k), _f64(v), _f64(dout), _f64(out)
+    qt, kt, dt = _f64(q_t), _f64(k_t), _f64(dout_t)
+    T, H, D = q.shape
+    for a in (k, v, do, o, qt, kt, dt):
+        if a.shape != q.shape:
+            raise ValueError("every tensor must share one [T, H, D] shape")
+    ls = _f64(lse)
+    if ls.shape != (H, T):
+        raise ValueError("lse must be [H, T]")
+    return (q, k, v, do, o, ls, qt, kt, dt), (T, H, D)
+
+
+def mx_bwd(q, k, v, dout, out, lse, q_t, k_t, dout_t, offsets, block_size: int,
+           window_blocks: int, scale: float, quantize: bool = True):
+    """MXFP8 backward (blockattn_oracle.c: oracle_mx_bwd).  q, k, v, dout:
+    decoded head-dim-blocked values; q_t, k_t, dout_t: decoded token-blocked
+    values; out, lse: the forward's.  Returns (dq, dk, dv) [T, H, D] fp64.
+    quantize=False skips the quantization of P and dS."""
+    ins, (T, H, D) = _mx_bwd_inputs(q, k, v, dout, out, lse, q_t, k_t, dout_t)
+    off = _i32(offsets)
+    res = [np.zeros((T, H, D), np.float64) for _ in range(3)]
+    rc = _load().oracle_mx_bwd(*[_dp(a) for a in ins], _ip(off), len(off) - 1, T, H, D,
+                               int(block_size), int(window_blocks), float(scale),
+                               int(bool(quantize)), *[_dp(a) for a in res])
+    if rc != 0:
+        raise ValueError(f"oracle_mx_bwd failed with status {rc}")
+    return tuple(res)
+
+
+def mx_quantize_block(x) -> np.ndarray:
+    """The backward's block rule (blockattn_oracle.c: mx_block) on one block
+    of values: returns the quantized copy."""
+    y = _f64(x).copy()
+    _load().oracle_mx_quantize_block(_dp(y), y.size)
+    return y
+
+
+def mx_bwd_bounds(q, k, v, dout, out, lse, q_t, k_t, dout_t, offsets, block_size: int,
+                  window_blocks: int, scale: float, rho: float):
+    """mx_bwd's (dq, dk, dv) with their parity allowances (test support;
+    blockattn_oracle.c: oracle_mx_bwd_bounds): returns (ref, slack, absum),
+    each a tuple (dq, dk, dv) of [T, H, D] fp64."""
+    ins, (T, H, D) = _mx_bwd_inputs(q, k, v, dout, out, lse, q_t, k_t, dout_t)
+    off = _i32(offsets)
+    res = [np.zeros((T, H, D), np.float64) for _ in range(9)]
+    rc = _load().oracle_mx_bwd_bounds(*[_dp(a) for a in ins], _ip(off), len(off) - 1, T, H,
+                                      D, int(block_size), int(window_blocks), float(scale),
+                                      float(rho), *[_dp(a) for a in res])
+    if rc != 0:
+        raise ValueError(f"oracle_mx_bwd_bounds failed with status {rc}")
+    return tuple(res[0:3]), tuple(res[3:6]), tuple(res[6:9])
 
 
 # ------------------------------------------------- rotary position embedding

@@ -657,3 +657,334 @@ int oracle_mxpv_slack(const double *q, const double *k, const double *v,
     }
     return status;
 }
+
+/*
+ * MXFP8 backward.  "GEM (Meta)", section "Ultra-low-precision training":
+ * the attention kernel runs its matrix products as block-scaled MXFP8 in the
+ * backward pass as well as in the forward.  Nothing more is given; the
+ * readings taken here:
+ *   - every product takes MXFP8 operands whose scale blocks run along that
+ *     product's contraction: S = scale Q K^T and dP = dO V^T along head
+ *     dims (q, k, v, dout: head-dim blocks, as in the forward); dV = P^T dO
+ *     and dK = scale dS^T Q along queries, dQ = scale dS K along keys.  Q, K
+ *     and dO therefore enter the last three products through a second
+ *     quantization along tokens (qt, kt, dot: blocks of 32 tokens counted
+ *     from the user's first token), which the caller supplies.  All arrays
+ *     here hold decoded values;
+ *   - P_ij = exp(s_ij - lse_i) with the forward's lse, and
+ *     delta_i = <dO_i, O_i> with the forward's O (both given), the row
+ *     statistic of the FlashAttention backward; dS_ij = P_ij (dP_ij - delta_i);
+ *   - the operands formed inside the backward are quantized along their
+ *     product's contraction: P over each key's queries (for dV), dS over
+ *     each key's queries (for dK) and over each query's keys (for dQ), in
+ *     blocks of 32 positions counted from the user's first token, where a
+ *     position that is not visible holds 0.  In a block whose largest
+ *     magnitude is a > 0, each x is stored as 2^E R(x 2^-E) with
+ *     E = max(floor(log2 a) - 7, -127) (the E8M0 range) and R the nearest
+ *     E4M3 value, ties to the even code, sign kept.  |x 2^-E| < 2^8, so
+ *     nothing saturates: the rule of the forward's weights (oracle_mxpv_fwd);
+ *   - dQ_i = scale sum_j dSq_ij kt_j, dK_j = scale sum_i dSq_ij qt_i (the
+ *     query-blocked dSq), dV_j = sum_i Pq_ij dot_i.
+ * With quant = 0 the quantization is skipped: with the exact O and lse and
+ * qt = q, kt = k, dot = dout this is oracle_bwd.
+ * Layouts: every tensor fp64 [T, H, D]; lse fp64 [H, T].
+ */
+
+/* Quantizes n values x[0], x[st], ... as one block, in place. */
+static void mx_block(double *x, int64_t n, int64_t st)
+{
+    double a = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        if (fabs(x[i * st]) > a)
+            a = fabs(x[i * st]);
+    if (!(a > 0.0))
+        return; /* all zero */
+    int e;
+    (void)frexp(a, &e);
+    const int E = e - 8 < -127 ? -127 : e - 8; /* floor(log2 a) - 7 */
+    for (int64_t i = 0; i < n; ++i) {
+        const double y = x[i * st];
+        x[i * st] = copysign(ldexp(oracle_e4m3_round(ldexp(fabs(y), -E)), E), y);
+    }
+}
+
+/* The block rule with a given exponent E, |y| clipped below 2^(E + 8). */
+static double mx_at(double y, int E)
+{
+    const double lim = ldexp(1.0, E + 8) * (1.0 - 0x1p-40);
+    const double m = fabs(y) < lim ? fabs(y) : lim;
+    return copysign(ldexp(oracle_e4m3_round(ldexp(m, -E)), E), y);
+}
+
+static int mx_exp(double a)
+{
+    int e;
+    (void)frexp(a, &e);
+    return e - 8 < -127 ? -127 : e - 8;
+}
+
+/* Parity allowance of one block (test support): x[] the exact values, err[]
+ * bounds on how far a computation's values may be from them (0 for exact
+ * zeros), q[] the quantized x.  A computation may take its block exponent
+ * from any maximum within the errors and round any value within its error:
+ * a[] gets the largest change of each quantized value those allow. */
+static void mx_block_reach(const double *x, const double *err, const double *q,
+                           int64_t n, int64_t st, double *a)
+{
+    double lo = 0.0, hi = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double m = fabs(x[i * st]);
+        if (m - err[i * st] > lo)
+            lo = m - err[i * st];
+        if (m + err[i * st] > hi)
+            hi = m + err[i * st];
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        const double y = x[i * st], e = err[i * st];
+        double r = 0.0;
+        if (!(hi > 0.0)) {
+            r = 0.0;
+        } else if (!(lo > 0.0)) { /* the maximum may be near 0: any code */
+            r = fabs(q[i * st]) + 2.0 * (fabs(y) + e);
+        } else {
+            for (int E = mx_exp(lo); E <= mx_exp(hi); ++E) {
+                const double d0 = fabs(mx_at(y - e, E) - q[i * st]);
+                const double d1 = fabs(mx_at(y + e, E) - q[i * st]);
+                r = fmax(r, fmax(d0, d1));
+            }
+        }
+        a[i * st] = r;
+    }
+}
+
+static int mx_bwd_core(const double *q, const double *k, const double *v,
+                       const double *dout, const double *out, const double *lse,
+                       const double *qt, const double *kt, const double *dot_t,
+                       const int32_t *offsets, int batch, int64_t T, int H,
+                       int D, int B, int W, double scale, int quant, double rho,
+                       double *dq, double *dk, double *dv, double *sl_dq,
+                       double *sl_dk, double *sl_dv, double *ab_dq, double *ab_dk,
+                       double *ab_dv)
+{
+    if (check_args(offsets, batch, T, H, D, B, W))
+        return -1;
+    const int bounds = sl_dq != NULL;
+    int status = 0;
+    const int64_t npairs = (int64_t)batch * H;
+    const int64_t rs = (int64_t)H * D;
+    /* keys seen by one block of 32 queries */
+    const int64_t nk = (int64_t)visible_max(offsets, batch, B, W) + 32;
+    const double sa = fabs(scale);
+#pragma omp parallel
+    {
+        /* per 32-query block: P, dS (exact), their quantized copies along
+         * queries and along keys, error bounds and flip allowances */
+        const int nbuf = bounds ? 10 : 5;
+        double *buf = (double *)calloc((size_t)(32 * nk * nbuf), sizeof(double));
+        if (!buf) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(dynamic)
+        for (int64_t p = 0; p < npairs; ++p) {
+            if (!buf)
+                continue;
+            double *P = buf, *S = P + 32 * nk;               /* P, dS [32][nk] */
+            double *PqT = S + 32 * nk, *SqT = PqT + 32 * nk; /* along queries */
+            double *Sq = SqT + 32 * nk;                      /* along keys */
+            /* (bounds only) error bounds of P and dS, and the allowances of
+             * PqT, SqT and Sq */
+            double *eP = Sq + 32 * nk, *eS = eP + 32 * nk;
+            double *aP = eS + 32 * nk, *aST = aP + 32 * nk, *aS = aST + 32 * nk;
+            const int u = (int)(p / H), h = (int)(p % H);
+            const int64_t t0 = offsets[u];
+            const int64_t L = (int64_t)offsets[u + 1] - t0;
+            const int64_t ho = (int64_t)h * D;
+            for (int64_t i = 0; i < L; ++i)
+                for (int d = 0; d < D; ++d) {
+                    const int64_t o = (t0 + i) * rs + ho + d;
+                    dk[o] = dv[o] = dq[o] = 0.0;
+                    if (bounds)
+                        sl_dq[o] = sl_dk[o] = sl_dv[o] = ab_dq[o] = ab_dk[o] = ab_dv[o] = 0.0;
+                }
+            for (int64_t i0 = 0; i0 < L; i0 += 32) {
+                const int64_t ni = L - i0 < 32 ? L - i0 : 32;
+                const int64_t k0 = first_visible(i0, B, W); /* keys k0 .. */
+                const int64_t kn = i0 + ni - k0;            /* .. k0 + kn - 1 */
+                for (int64_t x = 0; x < 32 * nk; ++x)
+                    P[x] = S[x] = 0.0;
+                if (bounds)
+                    for (int64_t x = 0; x < 32 * nk; ++x)
+                        eP[x] = eS[x] = 0.0;
+                /* P and dS of the block's queries (row r, column c = key k0 + c) */
+                for (int64_t r = 0; r < ni; ++r) {
+                    const int64_t i = i0 + r;
+                    const double *qi = q + (t0 + i) * rs + ho;
+                    const double *doi = dout + (t0 + i) * rs + ho;
+                    const double *oi = out + (t0 + i) * rs + ho;
+                    const double li = lse[(int64_t)h * T + t0 + i];
+                    const double delta = dot(doi, oi, D);
+                    double dabs = 0.0;
+                    if (bounds)
+                        for (int d = 0; d < D; ++d)
+                            dabs += fabs(doi[d] * oi[d]);
+                    for (int64_t j = first_visible(i, B, W); j <= i; ++j) {
+                        const double *kj = k + (t0 + j) * rs + ho;
+                        const double *vj = v + (t0 + j) * rs + ho;
+                        const double s = scale * dot(qi, kj, D);
+                        const double pij = exp(s - li);
+                        const double dp = dot(doi, vj, D);
+                        const int64_t x = r * nk + (j - k0);
+                        P[x] = pij;
+                        S[x] = pij * (dp - delta);
+                        if (bounds) {
+                            /* score and dP products within rho of their
+                             * magnitude sums; fp32 exponent arguments and
+                             * delta's fp32 sum */
+                            double qk = 0.0, dv_ = 0.0;
+                            for (int d = 0; d < D; ++d) {
+                                qk += fabs(qi[d] * kj[d]);
+                                dv_ += fabs(doi[d] * vj[d]);
+                            }
+                            const double et = rho * sa * qk * kLog2e +
+                                              0x1p-20 * (4.0 + fabs(s * kLog2e) + fabs(li * kLog2e));
+                            eP[x] = pij * (exp2(et) - 1.0);
+                            const double edp = rho * (dv_ + fabs(delta)) + 0x1p-16 * dabs;
+                            eS[x] = eP[x] * fabs(dp - delta) + (pij + eP[x]) * edp +
+                                    0x1p-22 * fabs(S[x]);
+                        }
+                    }
+                }
+                /* along queries: one block per key (the 32 queries are one
+                 * block: i0 is a multiple of 32) */
+                memcpy(PqT, P, sizeof(double) * 32 * nk);
+                memcpy(SqT, S, sizeof(double) * 32 * nk);
+                if (quant)
+                    for (int64_t c = 0; c < kn; ++c) {
+                        mx_block(PqT + c, ni, nk);
+                        mx_block(SqT + c, ni, nk);
+                    }
+                /* along keys: blocks of 32 local keys in each query's row */
+                memcpy(Sq, S, sizeof(double) * 32 * nk);
+                if (quant)
+                    for (int64_t r = 0; r < ni; ++r)
+                        for (int64_t c = 0; c < kn;) {
+                            const int64_t j = k0 + c;
+                            const int64_t e = (j / 32 + 1) * 32 - k0; /* block end */
+                            const int64_t n = (e < kn ? e : kn) - c;
+                            mx_block(Sq + r * nk + c, n, 1);
+                            c += n;
+                        }
+                if (bounds) {
+                    if (quant) {
+                        for (int64_t c = 0; c < kn; ++c) {
+                            mx_block_reach(P + c, eP + c, PqT + c, ni, nk, aP + c);
+                            mx_block_reach(S + c, eS + c, SqT + c, ni, nk, aST + c);
+                        }
+                        for (int64_t r = 0; r < ni; ++r)
+                            for (int64_t c = 0; c < kn;) {
+                                const int64_t j = k0 + c;
+                                const int64_t e = (j / 32 + 1) * 32 - k0;
+                                const int64_t n = (e < kn ? e : kn) - c;
+                                mx_block_reach(S + r * nk + c, eS + r * nk + c, Sq + r * nk + c,
+                                               n, 1, aS + r * nk + c);
+                                c += n;
+                            }
+                    } else {
+                        for (int64_t x = 0; x < 32 * nk; ++x) {
+                            aP[x] = eP[x];
+                            aST[x] = aS[x] = eS[x];
+                        }
+                    }
+                }
+                /* the three products */
+                for (int64_t r = 0; r < ni; ++r) {
+                    const int64_t i = i0 + r;
+                    double *dqi = dq + (t0 + i) * rs + ho;
+                    for (int64_t c = 0; c < kn; ++c) {
+                        const int64_t x = r * nk + c;
+                        const double *ktj = kt + (t0 + k0 + c) * rs + ho;
+                        if (Sq[x] != 0.0)
+                            for (int d = 0; d < D; ++d)
+                                dqi[d] += scale * Sq[x] * ktj[d];
+                        if (bounds && (Sq[x] != 0.0 || aS[x] != 0.0))
+                            for (int d = 0; d < D; ++d) {
+                                const int64_t o = (t0 + i) * rs + ho + d;
+                                sl_dq[o] += sa * aS[x] * fabs(ktj[d]);
+                                ab_dq[o] += sa * fabs(Sq[x] * ktj[d]);
+                            }
+                    }
+                }
+                for (int64_t c = 0; c < kn; ++c) {
+                    const int64_t j = k0 + c;
+                    double *dkj = dk + (t0 + j) * rs + ho;
+                    double *dvj = dv + (t0 + j) * rs + ho;
+                    for (int64_t r = 0; r < ni; ++r) {
+                        const int64_t x = r * nk + c;
+                        const double *qti = qt + (t0 + i0 + r) * rs + ho;
+                        const double *dti = dot_t + (t0 + i0 + r) * rs + ho;
+                        for (int d = 0; d < D; ++d) {
+                            dkj[d] += scale * SqT[x] * qti[d];
+                            dvj[d] += PqT[x] * dti[d];
+                        }
+                        if (bounds)
+                            for (int d = 0; d < D; ++d) {
+                                const int64_t o = (t0 + j) * rs + ho + d;
+                                sl_dk[o] += sa * aST[x] * fabs(qti[d]);
+                                ab_dk[o] += sa * fabs(SqT[x] * qti[d]);
+                                sl_dv[o] += aP[x] * fabs(dti[d]);
+                                ab_dv[o] += fabs(PqT[x] * dti[d]);
+                            }
+                    }
+                }
+            }
+        }
+        free(buf);
+    }
+    return status;
+}
+
+/* MXFP8 backward (definition above): dq, dk, dv [T,H,D]. */
+int oracle_mx_bwd(const double *q, const double *k, const double *v,
+                  const double *dout, const double *out, const double *lse,
+                  const double *qt, const double *kt, const double *dot_t,
+                  const int32_t *offsets, int batch, int64_t T, int H, int D,
+                  int B, int W, double scale, int quant, double *dq, double *dk,
+                  double *dv)
+{
+    return mx_bwd_core(q, k, v, dout, out, lse, qt, kt, dot_t, offsets, batch, T, H, D,
+                       B, W, scale, quant, 0.0, dq, dk, dv, NULL, NULL, NULL, NULL,
+                       NULL, NULL);
+}
+
+/* Parity allowance for oracle_mx_bwd (test support, not part of the
+ * definition), with the same dq, dk, dv.  A computation whose score and dP
+ * products are within rho of sum_d |scale q_d k_d| and
+ * sum_d |dO_d v_d| + |delta|, whose exponent arguments, delta and dS carry
+ * fp32 rounding, and which follows the quantization rule on its own values,
+ * may take another block exponent where a block's maximum lies that close
+ * to a power of two and round to a neighbouring code where a value lies
+ * that close to a midpoint.  sl_* = sum over the contraction of the largest
+ * change those flips allow to each quantized operand times |the other
+ * operand|; ab_* = the same sum of |quantized operand| |other operand|
+ * (what the products' own rounding is relative to). */
+int oracle_mx_bwd_bounds(const double *q, const double *k, const double *v,
+                         const double *dout, const double *out, const double *lse,
+                         const double *qt, const double *kt, const double *dot_t,
+                         const int32_t *offsets, int batch, int64_t T, int H, int D,
+                         int B, int W, double scale, double rho, double *dq,
+                         double *dk, double *dv, double *sl_dq, double *sl_dk,
+                         double *sl_dv, double *ab_dq, double *ab_dk, double *ab_dv)
+{
+    return mx_bwd_core(q, k, v, dout, out, lse, qt, kt, dot_t, offsets, batch, T, H, D,
+                       B, W, scale, 1, rho, dq, dk, dv, sl_dq, sl_dk, sl_dv, ab_dq, ab_dk,
+                       ab_dv);
+}
+
+/* The block rule of oracle_mx_bwd applied to x[0..n) in place (exported so
+ * that the rule itself can be pinned). */
+void oracle_mx_quantize_block(double *x, int64_t n)
+{
+    if (x && n > 0)
+        mx_block(x, n, 1);
+}

@@ -938,3 +938,216 @@ def test_mx_decode_user_blocks():
     v = oracle.mx_decode_user_blocks(codes, scales, off)
     expect = np.concatenate([np.arange(40) // 32, 4 + np.arange(65) // 32])
     np.testing.assert_array_equal(v[:, 0, 0], 2.0 ** expect)
+
+
+# ------------------------------------------------------------ MXFP8 backward
+
+
+def _mxb_case(seed, lengths, H=2, D=32, B=16, W=2, scale=0.3):
+    """Random inputs of the MXFP8 backward oracle with the exact forward's
+    O and lse, and token-blocked copies equal to the head-dim-blocked ones
+    (the oracle takes decoded values; which quantization produced them does
+    not matter to it)."""
+    rng = np.random.default_rng(seed)
+    off = wl.offsets_from_lengths(lengths)
+    T = int(off[-1])
+    q, k, v, do = (rng.standard_normal((T, H, D)) for _ in range(4))
+    o, lse = oracle.fwd(q, k, v, off, B, W, scale)
+    return dict(q=q, k=k, v=v, dout=do, out=o, lse=lse, q_t=q.copy(), k_t=k.copy(),
+                dout_t=do.copy(), offsets=off, block_size=B, window_blocks=W, scale=scale)
+
+
+def _mxb(c, **kw):
+    args = dict(c)
+    args.update(kw)
+    return oracle.mx_bwd(**args)
+
+
+@pytest.mark.parametrize("B,W", [(16, 2), (5, 3), (1, 1), (64, 1)])
+def test_mx_bwd_unquantized_is_the_exact_backward(B, W):
+    """Without the quantization step, given the exact forward's O and lse
+    and the same values for both quantizations of q, k and dO, the MXFP8
+    backward's steps (P from lse, delta from <dO, O>, dS, the three
+    products) give the exact backward, itself pinned to finite differences
+    and the sum identities."""
+    c = _mxb_case(1, [40, 7, 73, 1], B=B, W=W)
+    got = _mxb(c, quantize=False)
+    ref = oracle.bwd(c["q"], c["k"], c["v"], c["dout"], c["offsets"], B, W, c["scale"])
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-12 * np.abs(r).max())
+
+
+@pytest.mark.parametrize("quantize", [False, True])
+def test_mx_bwd_token_blocked_operands_feed_their_own_products(quantize):
+    """dQ takes k_t, dK takes q_t and dV takes dout_t, linearly, and nothing
+    else does: scaling one of them by 4 scales exactly its gradient, bit for
+    bit.  (The quantized operands P and dS do not depend on them.)"""
+    c = _mxb_case(2, [45, 20])
+    dq, dk, dv = _mxb(c, quantize=quantize)
+    for name, idx in (("k_t", 0), ("q_t", 1), ("dout_t", 2)):
+        got = _mxb(c, quantize=quantize, **{name: 4.0 * c[name]})
+        for j, (g, r) in enumerate(zip(got, (dq, dk, dv))):
+            if j == idx:
+                np.testing.assert_array_equal(g, 4.0 * r)
+            else:
+                np.testing.assert_array_equal(g, r)
+
+
+def test_mx_block_rule_matches_torch_fp8():
+    """The block rule: with E = floor(log2 max|x|) - 7, each value becomes
+    2^E times torch's float8_e4m3fn conversion of x 2^-E (nearest, ties to
+    even, sign kept), for blocks of mixed signs, zeros, magnitudes from 2^-40
+    to 2^40 and spreads up to 2^30 inside a block, fp32 inputs (torch
+    converts through fp32); blocks whose maximum is tiny clamp E at -127;
+    an all-zero block stays zero."""
+    rng = np.random.default_rng(7)
+    for _ in range(400):
+        n = int(rng.integers(1, 33))
+        mag = rng.uniform(-40, 40)
+        x = (np.exp2(mag - rng.uniform(0, 30, n)) * rng.choice([-1, 1], n)).astype(np.float32)
+        x[rng.random(n) < 0.1] = 0
+        x = x.astype(np.float64)
+        got = oracle.mx_quantize_block(x)
+        a = np.abs(x).max()
+        if a == 0:
+            np.testing.assert_array_equal(got, 0 * x)
+            continue
+        E = max(math.frexp(a)[1] - 8, -127)
+        y = torch.from_numpy(np.ldexp(x, -E).astype(np.float32))
+        ref = np.ldexp(y.to(torch.float8_e4m3fn).double().numpy(), E)
+        np.testing.assert_array_equal(got, ref)
+    x = np.array([2.0 ** -130, -(2.0 ** -131), 2.0 ** -140])
+    E = -127
+    y = torch.from_numpy(np.ldexp(x, -E).astype(np.float32))
+    np.testing.assert_array_equal(oracle.mx_quantize_block(x),
+                                  np.ldexp(y.to(torch.float8_e4m3fn).double().numpy(), E))
+    np.testing.assert_array_equal(oracle.mx_quantize_block(np.zeros(5)), np.zeros(5))
+
+
+def test_mx_bwd_dq_blocks_run_along_the_row():
+    """dS is quantized along each query's keys for dQ: scaling query i's dO
+    (hence its dP, delta and whole dS row) by 2^5 scales dQ_i by exactly 2^5
+    and leaves every other query's dQ bit-for-bit unchanged.  Blocks along
+    queries would mix row i into other rows' codes."""
+    c = _mxb_case(3, [70, 50], B=8, W=3)
+    dq, _, _ = _mxb(c)
+    for row in (0, 33, 69, 70 + 41):
+        d2 = c["dout"].copy()
+        d2[row] *= 32.0
+        got, _, _ = _mxb(c, dout=d2)
+        np.testing.assert_array_equal(got[row], 32.0 * dq[row])
+        other = np.ones(len(dq), bool)
+        other[row] = False
+        np.testing.assert_array_equal(got[other], dq[other])
+
+
+def _only_rows(x, rows):
+    y = np.zeros_like(x)
+    y[rows] = x[rows]
+    return y
+
+
+@pytest.mark.parametrize("user,blk", [(1, 1), (1, 0), (2, 2)])
+def test_mx_bwd_dk_dv_blocks_run_along_each_keys_queries(user, blk):
+    """P and dS are quantized along each key's queries in blocks of 32
+    counted from the user's first token (users here start at 37 and 100,
+    off the packed axis's multiples of 32).  Scaling the dO of the queries
+    of one such block by 2^3 scales their dS entries exactly, so
+    dK = dK + 7 dK_b, with dK_b the block's own share (q_t zeroed outside
+    it); shifting their lse by 2 ln 2 scales their P and dS by 2^-2, so
+    dV = dV - (3/4) dV_b and dK = dK - (3/4) dK_b.  Blocks cut anywhere else
+    would change other queries' codes."""
+    c = _mxb_case(4, [37, 63, 101], B=16, W=3)
+    off = c["offsets"]
+    rows = np.arange(off[user] + 32 * blk, min(off[user] + 32 * blk + 32, off[user + 1]))
+    dq, dk, dv = _mxb(c)
+    _, dk_b, _ = _mxb(c, q_t=_only_rows(c["q_t"], rows))
+    _, _, dv_b = _mxb(c, dout_t=_only_rows(c["dout_t"], rows))
+    d2 = c["dout"].copy()
+    d2[rows] *= 8.0
+    _, got_dk, got_dv = _mxb(c, dout=d2)
+    np.testing.assert_allclose(got_dk, dk + 7.0 * dk_b, rtol=0, atol=1e-12 * np.abs(dk).max())
+    np.testing.assert_array_equal(got_dv, dv)
+    l2 = c["lse"].copy()
+    l2[:, rows] += 2.0 * math.log(2.0)
+    _, got_dk, got_dv = _mxb(c, lse=l2)
+    np.testing.assert_allclose(got_dv, dv - 0.75 * dv_b, rtol=0, atol=1e-12 * np.abs(dv).max())
+    np.testing.assert_allclose(got_dk, dk - 0.75 * dk_b, rtol=0, atol=1e-12 * np.abs(dk).max())
+
+
+def test_mx_bwd_single_token_window_closed_form():
+    """B = W = 1: each query sees only itself, P_ii = 1 (stored exactly),
+    O_i = v_i, so dS_ii = <dO_i, v_i> - <dO_i, O_i> = 0: dQ = dK = 0 and
+    dV = dout_t exactly."""
+    c = _mxb_case(5, [9, 1, 30], B=1, W=1)
+    np.testing.assert_array_equal(c["out"], c["v"])
+    dq, dk, dv = _mxb(c)
+    np.testing.assert_array_equal(dq, 0 * dq)
+    np.testing.assert_array_equal(dk, 0 * dk)
+    np.testing.assert_array_equal(dv, c["dout_t"])
+
+
+def test_mx_bwd_users_are_independent():
+    """A user's gradients are the same alone and inside a batch (blocks
+    start at each user's first token)."""
+    lengths = [37, 70, 5]
+    c = _mxb_case(6, lengths, B=8, W=4)
+    full = _mxb(c)
+    off = c["offsets"]
+    for u in range(len(lengths)):
+        sl = slice(off[u], off[u + 1])
+        cu = {n: (x[sl] if isinstance(x, np.ndarray) and x.shape[:1] == (off[-1],) else x)
+              for n, x in c.items()}
+        cu["lse"] = c["lse"][:, sl]
+        cu["offsets"] = np.array([0, off[u + 1] - off[u]], np.int32)
+        for g, r in zip(oracle.mx_bwd(**cu), full):
+            np.testing.assert_array_equal(g, r[sl])
+
+
+def test_mx_bwd_bounds_cover_perturbed_products():
+    """The allowance of mx_bwd_bounds covers real flips: scores and dP taken
+    from q and v perturbed elementwise by up to rho relative (so each moves
+    by at most rho times its magnitude sum, the allowed error) change the
+    quantized gradients by no more than the slack.  Also the absolute sums
+    bound the gradients."""
+    rho = 2.0 ** -11
+    c = _mxb_case(8, [80, 45], B=16, W=3)
+    (dq, dk, dv), sl, ab = oracle.mx_bwd_bounds(**c, rho=rho)
+    for g, a in zip((dq, dk, dv), ab):
+        assert np.all(np.abs(g) <= a * (1 + 1e-12))
+    rng = np.random.default_rng(9)
+    flipped = 0
+    for t in range(4):
+        qp = c["q"] * (1 + rho * rng.uniform(-1, 1, c["q"].shape))
+        vp = c["v"] * (1 + rho * rng.uniform(-1, 1, c["v"].shape))
+        got = _mxb(c, q=qp, v=vp)
+        for g, r, s in zip(got, (dq, dk, dv), sl):
+            d = np.abs(g - r)
+            flipped += int(np.count_nonzero(d > 1e-12 * np.abs(r).max()))
+            assert np.all(d <= s + 1e-12 * np.abs(r).max())
+    assert flipped > 0  # the perturbations did move codes
+
+
+def test_mx_bwd_p_and_ds_blocks_hold_one_keys_queries():
+    """Scaling one key's column of P by 4 (q has a constant unit feature,
+    and that key's k moves by 2 ln 2 / scale along it, so every s_ij of the
+    key grows by 2 ln 2) scales the key's P and dS entries and hence its dV
+    and dK by 4, and leaves every other key's dV and dK bit-for-bit
+    unchanged: each key's queries form its own blocks.  Blocks along a
+    query's keys would move other keys' codes."""
+    c = _mxb_case(10, [70, 45], B=16, W=3)
+    for name in ("q", "q_t"):
+        c[name][:, :, 0] = 1.0
+    c["out"], c["lse"] = oracle.fwd(c["q"], c["k"], c["v"], c["offsets"], 16, 3, c["scale"])
+    _, dk, dv = _mxb(c)
+    for key in (3, 40, 70 + 17):
+        k2 = c["k"].copy()
+        k2[key, :, 0] += 2.0 * math.log(2.0) / c["scale"]
+        _, got_dk, got_dv = _mxb(c, k=k2)
+        other = np.ones(len(dk), bool)
+        other[key] = False
+        np.testing.assert_array_equal(got_dv[other], dv[other])
+        np.testing.assert_array_equal(got_dk[other], dk[other])
+        np.testing.assert_allclose(got_dv[key], 4.0 * dv[key], rtol=1e-12)
+        np.testing.assert_allclose(got_dk[key], 4.0 * dk[key], rtol=1e-9,
+                                   atol=1e-12 * np.abs(dk).max())
