@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 8
+#define BLOCKATTN_ABI_VERSION 9
 
 typedef enum {
     BLOCKATTN_BF16 = 0, /* bf16 storage, fp32 accumulation, MFMA path      */
@@ -241,7 +241,7 @@ blockattn_status blockattn_gdpa_bwd(const void *q, const void *k, const void *v,
  * D must be 64 or 128, else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments and
  * errors as for blockattn_fwd.  The block-scaled fp8 products sum with fewer
  * bits than fp32 (measured: within 2^-12 of sum_d |scale q_d k_d| per score).
- * There is no MXFP8 backward.
+ * The MXFP8 backward is blockattn_mx_bwd.
  */
 blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
                                   const void *k, const void *k_scale,
@@ -280,7 +280,7 @@ blockattn_status blockattn_mx_fwd(const void *q, const void *q_scale,
  * unrelated rows.  D must be 64 or 128 and D * 32 * NB below 2^32,
  * else BLOCKATTN_ERR_UNSUPPORTED.  Other arguments and errors as for
  * blockattn_fwd.  The block-scaled products sum with fewer bits than fp32
- * (see blockattn_mx_fwd).  There is no MXFP8 backward.
+ * (see blockattn_mx_fwd).  The MXFP8 backward is blockattn_mx_bwd.
  */
 blockattn_status blockattn_mxpv_fwd(const void *q, const void *q_scale,
                                     const void *k, const void *k_scale,
@@ -290,6 +290,58 @@ blockattn_status blockattn_mxpv_fwd(const void *q, const void *q_scale,
                                     int32_t head_dim, int32_t block_size,
                                     int32_t window_blocks, float scale,
                                     void *out, float *lse, hipStream_t stream);
+
+/*
+ * Backward in MXFP8 ("GEM (Meta)", section "Ultra-low-precision training":
+ * the attention kernel's block-scaled MXFP8 products run in the backward as
+ * well as the forward).  Every product takes operands whose 32-element scale
+ * blocks run along its own contraction.  The score and dP products contract
+ * head dims: q, k, v and dout come head-dim-blocked.  dV = P^T dO and
+ * dK = scale dS^T Q contract queries and dQ = scale dS K contracts keys:
+ * q, k and dout come a second time, quantized along each user's tokens and
+ * transposed (the caller's producer emits both).  P_ij = exp(scale q_i.k_j -
+ * lse_i) with the forward's lse, delta_i = <dO_i, O_i> with the forward's
+ * out, dS_ij = P_ij (dP_ij - delta_i).  P and dS are quantized inside the
+ * backward along each key's queries (for dV, dK), and dS along each query's
+ * keys (for dQ), in blocks of 32 positions counted from the user's first
+ * token: with a the block's largest magnitude, each value becomes 2^E times
+ * its nearest E4M3 value (ties to even) of x 2^-E,
+ * E = max(floor(log2 a) - 7, -127), so nothing saturates.  Softmax only.
+ *   q, k, v, dout             E4M3 bytes [T, H, D], 16-byte aligned
+ *   q_scale, k_scale,         E8M0 bytes [H, T, D/32], 4-byte aligned, as
+ *   v_scale, dout_scale       for blockattn_mx_fwd
+ *   q_t, k_t, dout_t          E4M3 bytes [H, D, 32 * NB], 16-byte aligned,
+ *                             laid out like blockattn_mxpv_fwd's v_t (user
+ *                             u's local token j, column d of head h, at
+ *                             [h][d][32 ub + j], ub = ceil(offsets[u] / 32)
+ *                             + u, NB = ceil(T / 32) + batch)
+ *   q_t_scale, k_t_scale,     E8M0 bytes [H, NB, D], 4-byte aligned, as
+ *   dout_t_scale              v_scale of blockattn_mxpv_fwd
+ *   out                       bf16 [T, H, D], the forward's output
+ *   lse                       fp32 [H, T], the forward's lse
+ *   dq, dk, dv                bf16 [T, H, D], written whole
+ *   workspace                 as for blockattn_bwd (same size function)
+ * The products read codes and scales of the token-blocked tensors just past
+ * a user's last token: every code (padding included) must be finite and no
+ * scale 255, as for blockattn_mxpv_fwd.  D must be 64 or 128 and D * 32 * NB
+ * below 2^32, else BLOCKATTN_ERR_UNSUPPORTED; a null or misaligned pointer
+ * is BLOCKATTN_ERR_INVALID_ARGUMENT; other arguments and errors as for
+ * blockattn_bwd.  Results are deterministic (no atomics).
+ */
+blockattn_status blockattn_mx_bwd(const void *q, const void *q_scale,
+                                  const void *k, const void *k_scale,
+                                  const void *v, const void *v_scale,
+                                  const void *dout, const void *dout_scale,
+                                  const void *q_t, const void *q_t_scale,
+                                  const void *k_t, const void *k_t_scale,
+                                  const void *dout_t, const void *dout_t_scale,
+                                  const void *out, const float *lse,
+                                  const int32_t *offsets, int32_t batch,
+                                  int64_t total_tokens, int32_t num_heads,
+                                  int32_t head_dim, int32_t block_size,
+                                  int32_t window_blocks, float scale, void *dq,
+                                  void *dk, void *dv, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
  * blockattn_bwd without a workspace argument, for callers that cannot

@@ -23,7 +23,7 @@ GDPA_SILU, GDPA_GELU = 1, 2  # blockattn_gdpa_act
 EXPORTS = ("blockattn_fwd", "blockattn_bwd", "blockattn_bwd_workspace_size",
            "blockattn_swa_fwd", "blockattn_swa_bwd", "blockattn_rope", "blockattn_rope_bwd",
            "blockattn_gdpa_fwd", "blockattn_gdpa_bwd", "blockattn_mx_fwd", "blockattn_mxpv_fwd",
-           "blockattn_bwd_noalloc", "blockattn_status_string", "blockattn_abi_version")
+           "blockattn_mx_bwd", "blockattn_bwd_noalloc", "blockattn_status_string", "blockattn_abi_version")
 
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # BLOCKATTN_NOALLOC_WORKSPACE_BYTES
 
@@ -83,6 +83,9 @@ def load() -> ctypes.CDLL:
     lib.blockattn_mxpv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                        f32, vp, vp, vp]
     lib.blockattn_mxpv_fwd.restype = ctypes.c_int
+    lib.blockattn_mx_bwd.argtypes = [vp] * 17 + [i32, i64, i32, i32, i32, i32, f32, vp, vp, vp,
+                                                 vp, ctypes.c_size_t, vp]
+    lib.blockattn_mx_bwd.restype = ctypes.c_int
     lib.blockattn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                           i32, f32, ctypes.c_int, vp, vp, vp, vp]
     lib.blockattn_bwd_noalloc.restype = ctypes.c_int
@@ -177,6 +180,17 @@ def blockattn_mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, batch, tot
     return load().blockattn_mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, batch,
                                      total_tokens, num_heads, head_dim, block_size,
                                      window_blocks, scale, out, lse, stream)
+
+
+def blockattn_mx_bwd(q, q_scale, k, k_scale, v, v_scale, dout, dout_scale, q_t, q_t_scale,
+                     k_t, k_t_scale, dout_t, dout_t_scale, out, lse, offsets, batch,
+                     total_tokens, num_heads, head_dim, block_size, window_blocks, scale, dq,
+                     dk, dv, workspace, workspace_bytes, stream) -> int:
+    return load().blockattn_mx_bwd(q, q_scale, k, k_scale, v, v_scale, dout, dout_scale, q_t,
+                                   q_t_scale, k_t, k_t_scale, dout_t, dout_t_scale, out, lse,
+                                   offsets, batch, total_tokens, num_heads, head_dim,
+                                   block_size, window_blocks, scale, dq, dk, dv, workspace,
+                                   workspace_bytes, stream)
 
 
 def blockattn_bwd_workspace_size(total_tokens, batch, num_heads, dtype) -> int:
@@ -508,3 +522,50 @@ def mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, block_size: int,
     if rc != OK:
         raise BlockAttnError("blockattn_mxpv_fwd", rc)
     return out, lse
+
+
+def mx_bwd(q, q_scale, k, k_scale, v, v_scale, dout, dout_scale, q_t, q_t_scale, k_t,
+           k_t_scale, dout_t, dout_t_scale, out, lse, offsets, block_size: int,
+           window_blocks: int, scale: float, grads=None, workspace=None, stream=None):
+    """MXFP8 backward (blockattn_mx_bwd).  q, k, v, dout uint8 [T, H, D] with
+    scales uint8 [H, T, D/32] (head-dim blocks); q_t, k_t, dout_t uint8
+    [H, D, 32 nb] with scales uint8 [H, nb, D] (token blocks, transposed,
+    user-blocked: workloads.mx_v_device_layout builds them), nb =
+    ceil(T/32) + batch; out bf16 [T, H, D] and lse fp32 [H, T] from the
+    forward.  Returns (dq, dk, dv), bf16 [T, H, D]."""
+    T, H, D = q.shape
+    nb = -(-T // 32) + offsets.numel() - 1
+    for t in (q, k, v, dout):
+        if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v, dout must be contiguous uint8 [T, H, D] device tensors")
+    for t in (q_scale, k_scale, v_scale, dout_scale):
+        if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
+            raise ValueError("head-dim scales must be contiguous uint8 [H, T, D/32]")
+    for t in (q_t, k_t, dout_t):
+        if t.dtype != torch.uint8 or t.shape != (H, D, 32 * nb) or not t.is_contiguous():
+            raise ValueError("q_t, k_t, dout_t must be contiguous uint8 "
+                             "[H, D, 32 (ceil(T/32) + batch)]")
+    for t in (q_t_scale, k_t_scale, dout_t_scale):
+        if t.dtype != torch.uint8 or t.shape != (H, nb, D) or not t.is_contiguous():
+            raise ValueError("token scales must be contiguous uint8 [H, ceil(T/32) + batch, D]")
+    if out.dtype != torch.bfloat16 or out.shape != (T, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [T, H, D] tensor")
+    _check_lse(lse, H, T)
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv = (tuple(torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device)
+                            for _ in range(3)) if grads is None else grads)
+        ws = _workspace(q, offsets, BF16, workspace)
+        ws_ptr, ws_len = _ws_args(ws)
+        rc = blockattn_mx_bwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
+                              v.data_ptr(), v_scale.data_ptr(), dout.data_ptr(),
+                              dout_scale.data_ptr(), q_t.data_ptr(), q_t_scale.data_ptr(),
+                              k_t.data_ptr(), k_t_scale.data_ptr(), dout_t.data_ptr(),
+                              dout_t_scale.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
+                              window_blocks, float(scale), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), ws_ptr, ws_len, st.cuda_stream)
+        del ws
+    if rc != OK:
+        raise BlockAttnError("blockattn_mx_bwd", rc)
+    return dq, dk, dv

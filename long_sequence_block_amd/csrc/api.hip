@@ -337,6 +337,49 @@ blockattn_status blockattn_mxpv_fwd(const void *q, const void *q_scale, const vo
     return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
 }
 
+blockattn_status blockattn_mx_bwd(const void *q, const void *q_scale, const void *k,
+                                  const void *k_scale, const void *v, const void *v_scale,
+                                  const void *dout, const void *dout_scale, const void *q_t,
+                                  const void *q_t_scale, const void *k_t, const void *k_t_scale,
+                                  const void *dout_t, const void *dout_t_scale, const void *out,
+                                  const float *lse, const int32_t *offsets, int32_t batch,
+                                  int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t window_blocks, float scale,
+                                  void *dq, void *dk, void *dv, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    bool empty;
+    blockattn_status st = check_common(offsets, batch, total_tokens, num_heads, head_dim,
+                                       &block_size, &window_blocks, scale, BLOCKATTN_BF16, &empty);
+    if (st != BLOCKATTN_OK) return st;
+    if (head_dim != 64 && head_dim != 128) return BLOCKATTN_ERR_UNSUPPORTED;
+    // token-blocked rows are addressed with 32-bit byte offsets
+    const int64_t tp = ((total_tokens + 31) / 32 + batch) * 32;
+    if ((int64_t)head_dim * tp >= ((int64_t)1 << 32)) return BLOCKATTN_ERR_UNSUPPORTED;
+    if (empty) return BLOCKATTN_OK;
+    const void *ptrs[] = {q, q_scale, k, k_scale, v, v_scale, dout, dout_scale, q_t,
+                          q_t_scale, k_t, k_t_scale, dout_t, dout_t_scale, out, lse, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (!p) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const void *rows16[] = {q, k, v, dout, q_t, k_t, dout_t, out, lse, dq, dk, dv};
+    for (const void *p : rows16)
+        if (!aligned16(p)) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const void *scales4[] = {q_scale, k_scale, v_scale, dout_scale, q_t_scale, k_t_scale,
+                             dout_t_scale};
+    for (const void *p : scales4)
+        if ((uintptr_t)p & 3u) return BLOCKATTN_ERR_INVALID_ARGUMENT;
+    const size_t need = blockattn_bwd_workspace_size(total_tokens, batch, num_heads,
+                                                     BLOCKATTN_BF16);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+        return BLOCKATTN_ERR_WORKSPACE;
+    const ba::Shape s = make_shape(offsets, batch, total_tokens, num_heads, head_dim, block_size,
+                                   window_blocks, scale);
+    const ba::MxBwdPtrs p{q, q_scale, k, k_scale, v, v_scale, dout, dout_scale,
+                          q_t, q_t_scale, k_t, k_t_scale, dout_t, dout_t_scale,
+                          out, lse, dq, dk, dv};
+    const hipError_t e = ba::launch_mfma_bwd_mx(s, p, workspace, stream);
+    return e == hipSuccess ? BLOCKATTN_OK : BLOCKATTN_ERR_HIP;
+}
+
 blockattn_status blockattn_swa_fwd(const void *q, const void *k, const void *v,
                                    const int32_t *offsets, int32_t batch, int64_t total_tokens,
                                    int32_t num_heads, int32_t head_dim, int32_t window_tokens,

@@ -82,4 +82,18 @@ hipError_t launch_mfma_bwd(const Shape &s, const void *q, const void *k, const v
                            const void *out, const void *dout, const float *lse, void *dq,
                            void *dk, void *dv, void *ws, hipStream_t st);
 
+// MXFP8 backward (softmax): q, k, v, dout head-dim-blocked as for
+// launch_mfma_fwd_mx; q_t, k_t, dout_t token-blocked and transposed as v_t
+// for launch_mfma_fwd_mxpv; out bf16 and lse fp32 from the forward; dq, dk,
+// dv bf16 [T, H, D].  Workspace as for launch_mfma_bwd (only its two row
+// statistic regions are used).  D 64 or 128.
+struct MxBwdPtrs {
+    const void *q, *q_scale, *k, *k_scale, *v, *v_scale, *dout, *dout_scale;
+    const void *q_t, *q_t_scale, *k_t, *k_t_scale, *dout_t, *dout_t_scale;
+    const void *out;
+    const float *lse;
+    void *dq, *dk, *dv;
+};
+hipError_t launch_mfma_bwd_mx(const Shape &s, const MxBwdPtrs &p, void *ws, hipStream_t st);
+
 }  // namespace ba

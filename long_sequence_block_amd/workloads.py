@@ -34,6 +34,9 @@ import numpy as np
 STREAM_LENGTHS, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = 0, 1, 2, 3, 4
 STREAM_QMX, STREAM_QSC, STREAM_KMX, STREAM_KSC = 5, 6, 7, 8
 STREAM_VMX, STREAM_VSC = 9, 10
+# the MXFP8 backward's head-dim-blocked v and dO, and token-blocked q, k, dO
+STREAM_VHMX, STREAM_VHSC, STREAM_DOMX, STREAM_DOSC = 11, 12, 13, 14
+STREAM_QTMX, STREAM_QTSC, STREAM_KTMX, STREAM_KTSC, STREAM_DOTMX, STREAM_DOTSC = range(15, 21)
 
 
 def rng(workload: int, stream: int) -> np.random.Generator:
@@ -170,6 +173,15 @@ WORKLOADS = {
                  fixed_length=16384, mx=True, mx_v=True),
     14: Workload(3, "jagged-mxfp8", users=256, heads=8, head_dim=64, block_size=128,
                  window_blocks=2, dtype="bf16", backward=False, mx=True, mx_v=True),
+    # The same two shapes as MXFP8 training steps: that forward, then the
+    # backward with every product block-scaled (q, k, v and dO head-dim-
+    # blocked, q, k and dO also token-blocked; mx_bwd_draw).
+    15: Workload(3, "jagged-mxfp8-train", users=256, heads=8, head_dim=64, block_size=128,
+                 window_blocks=2, dtype="bf16", backward=True, dout_wid=5, mx=True,
+                 mx_v=True),
+    16: Workload(4, "long-context-mxfp8-train", users=32, heads=8, head_dim=128,
+                 block_size=256, window_blocks=4, dtype="bf16", backward=True,
+                 fixed_length=16384, dout_wid=11, mx=True, mx_v=True),
     # The training step at a local batch of 1024 users (the pages put local
     # batches above 1,000 samples), same length law and shapes.
     12: Workload(12, "jagged-bf16-1024-train", users=1024, heads=8, head_dim=64,
@@ -214,7 +226,9 @@ def draw(w: Workload, users=None):
                "q": normal(w.wid, STREAM_Q, shape),
                "k": normal(w.wid, STREAM_K, shape),
                "v": normal(w.wid, STREAM_V, shape)}
-    if w.backward:
+    if w.backward and w.mx:
+        out.update(mx_bwd_draw(w.wid, w.dout_wid, off, w.heads, w.head_dim))
+    elif w.backward:
         out["dout"] = normal(w.dout_wid, STREAM_DO, shape)
     if users is not None:
         out = subset_users(out, users)
@@ -235,16 +249,52 @@ def mx_v_blocks(offsets) -> int:
     return int(-(-off[-1] // 32)) + len(off) - 1
 
 
-def mx_v_draw(wid: int, offsets, heads: int, head_dim: int, scales=(119, 121), codes=None):
-    """v as MXFP8 blocked along each user's tokens: codes ``v_mx`` uint8
-    [T, H, D] (the mx_codes draw, or ``codes`` = mx_codes_all) and block
-    scales ``v_bsc`` uint8 [ceil(T/32) + batch, H, D]; local token j of user
-    u has scale row user_block_base(offsets)[u] + j // 32."""
+def mx_tok_draw(name: str, wid: int, streams, offsets, heads: int, head_dim: int,
+                scales=(119, 121), codes=None):
+    """A tensor as MXFP8 blocked along each user's tokens: codes
+    ``<name>_mx`` uint8 [T, H, D] (the mx_codes draw, or ``codes`` =
+    mx_codes_all) and block scales ``<name>_bsc`` uint8
+    [ceil(T/32) + batch, H, D]; local token j of user u has scale row
+    user_block_base(offsets)[u] + j // 32.  streams = (codes, scales)."""
     fn = mx_codes if codes is None else codes
     T = int(np.asarray(offsets)[-1])
-    return {"v_mx": fn(wid, STREAM_VMX, (T, heads, head_dim)),
-            "v_bsc": mx_scales(wid, STREAM_VSC, (mx_v_blocks(offsets), heads, head_dim),
-                               *scales)}
+    return {name + "_mx": fn(wid, streams[0], (T, heads, head_dim)),
+            name + "_bsc": mx_scales(wid, streams[1], (mx_v_blocks(offsets), heads, head_dim),
+                                     *scales)}
+
+
+def mx_v_draw(wid: int, offsets, heads: int, head_dim: int, scales=(119, 121), codes=None):
+    """v as MXFP8 blocked along each user's tokens (mx_tok_draw): ``v_mx``
+    and ``v_bsc``."""
+    return mx_tok_draw("v", wid, (STREAM_VMX, STREAM_VSC), offsets, heads, head_dim, scales,
+                       codes)
+
+
+def mx_bwd_draw(wid: int, dout_wid: int, offsets, heads: int, head_dim: int, wide=None):
+    """The MXFP8 backward's further inputs, each an independent seeded draw
+    (a producer would quantize one tensor twice; the draws stand in for both
+    copies with the same code and scale ranges): head-dim-blocked v
+    (``vh_mx``, ``vh_sc``) and dO (``do_mx``, ``do_sc``), codes [T, H, D] and
+    scales [T, H, D/32]; token-blocked q, k and dO (``qt_``, ``kt_``,
+    ``dot_`` + ``mx`` / ``bsc``, as mx_tok_draw).  dO's draws use dout_wid.
+    wide: five scale ranges (vh, do, qt, kt, dot) with codes over every
+    finite E4M3 code."""
+    T = int(np.asarray(offsets)[-1])
+    shape, sshape = (T, heads, head_dim), (T, heads, head_dim // 32)
+    fn = mx_codes if wide is None else mx_codes_all
+    rg = [(119, 121)] * 5 if wide is None else list(wide)
+    out = {"vh_mx": fn(wid, STREAM_VHMX, shape),
+           "vh_sc": mx_scales(wid, STREAM_VHSC, sshape, *rg[0]),
+           "do_mx": fn(dout_wid, STREAM_DOMX, shape),
+           "do_sc": mx_scales(dout_wid, STREAM_DOSC, sshape, *rg[1])}
+    cf = None if wide is None else mx_codes_all
+    out.update(mx_tok_draw("qt", wid, (STREAM_QTMX, STREAM_QTSC), offsets, heads, head_dim,
+                           rg[2], cf))
+    out.update(mx_tok_draw("kt", wid, (STREAM_KTMX, STREAM_KTSC), offsets, heads, head_dim,
+                           rg[3], cf))
+    out.update(mx_tok_draw("dot", dout_wid, (STREAM_DOTMX, STREAM_DOTSC), offsets, heads,
+                           head_dim, rg[4], cf))
+    return out
 
 
 def mx_v_device_layout(v_mx: np.ndarray, v_bsc: np.ndarray, offsets):
@@ -343,4 +393,15 @@ def random_mxpv_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
     else:
         c.update(mx_v_draw(2000 + seed, c["offsets"], heads, head_dim, scales=wide[2],
                            codes=mx_codes_all))
+    return c
+
+
+def random_mxbwd_case(seed: int, lengths, heads: int, head_dim: int, wide=None):
+    """random_mxpv_case plus the MXFP8 backward's inputs (mx_bwd_draw);
+    wide = eight scale ranges (q, k, v, vh, do, qt, kt, dot), codes over
+    every finite E4M3 code."""
+    c = random_mxpv_case(seed, lengths, heads, head_dim,
+                         wide=None if wide is None else tuple(wide[:3]))
+    c.update(mx_bwd_draw(2000 + seed, 3000 + seed, c["offsets"], heads, head_dim,
+                         wide=None if wide is None else tuple(wide[3:])))
     return c

@@ -209,6 +209,59 @@ class GdpaParity:
                          for n, a in self.acc.items())
 
 
+# MXFP8 backward (oracle.mx_bwd): per element, the oracle's slack for code
+# flips (oracle.mx_bwd_bounds) plus the block-scaled products' own rounding,
+# 2^-10 of A = the sum of |quantized operand| |other operand| (rho = 2^-11 of
+# the fp8 instruction's sums, with a margin), plus the bf16 rounding of the
+# result, plus 10^-6 of the piece's largest A.  The mean error over a tensor
+# is held to a quarter of the bound's mean, so that a systematic error
+# cannot hide inside the per-element slack.
+MXB_RHO, MXB_ATOL, MXB_MEAN_FRAC = 2.0 ** -10, 1e-6, 0.25
+
+
+class MxBwdParity:
+    """Accumulates the MXFP8 backward's comparison (bounds above)."""
+
+    def __init__(self):
+        self.acc = {}
+
+    def add(self, name, got, ref, slack, absum, tag=""):
+        got, ref, slack, absum = (np.asarray(x, np.float64) for x in (got, ref, slack, absum))
+        assert got.shape == ref.shape == slack.shape == absum.shape, (name, tag)
+        a = self.acc.setdefault(name, {"n": 0, "sum": 0.0, "bsum": 0.0, "max": 0.0,
+                                       "ratio": 0.0, "flip": 0})
+        if got.size == 0:
+            return
+        assert np.all(np.isfinite(got)), f"{name} {tag}: non-finite values"
+        err = np.abs(got - ref)
+        bound = slack + MXB_RHO * absum + BF16_ROUND * np.abs(ref) + MXB_ATOL * absum.max()
+        a["n"] += err.size
+        a["sum"] += float(err.sum())
+        a["bsum"] += float(bound.sum())
+        a["max"] = max(a["max"], float(err.max()))
+        a["ratio"] = max(a["ratio"], float((err / np.maximum(bound, 1e-300)).max()))
+        a["flip"] += int(np.count_nonzero(slack > 0))
+        worst = int(np.argmax(err - bound))
+        assert err.flat[worst] <= bound.flat[worst], (
+            f"{name} {tag}: err {err.flat[worst]:.3e} > bound {bound.flat[worst]:.3e} "
+            f"(ref {ref.flat[worst]:.3e}, slack {slack.flat[worst]:.3e}, "
+            f"|terms| {absum.flat[worst]:.3e}) at flat index {worst}")
+
+    def finish(self):
+        for name, a in self.acc.items():
+            if a["n"] == 0:
+                continue
+            assert a["sum"] <= MXB_MEAN_FRAC * a["bsum"], (
+                f"{name}: mean err {a['sum'] / a['n']:.3e} > {MXB_MEAN_FRAC} x mean bound "
+                f"{a['bsum'] / a['n']:.3e}")
+
+    def summary(self) -> str:
+        return ", ".join(f"{n} max {a['max']:.2e} max err/bound {a['ratio']:.2f} "
+                         f"mean err/bound {a['sum'] / max(a['bsum'], 1e-300):.3f} "
+                         f"(elements with flip slack {a['flip'] / max(a['n'], 1):.1%})"
+                         for n, a in self.acc.items())
+
+
 def assert_close(name, got, ref, dtype, is_lse=False):
     """The stated bounds on one whole tensor."""
     p = Parity(dtype)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lsb.blockattn_abi_version() == 8
+    assert lsb.blockattn_abi_version() == 9
     names = [lsb.blockattn_status_string(s) for s in range(5)]
     assert len(set(names)) == 5 and names[0] == "ok"
     assert lsb.blockattn_status_string(99) == "unknown status"
@@ -227,3 +227,33 @@ def test_mxpv_argument_checks():
     assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.ERR_INVALID_ARGUMENT
     a.update(v_t=FAKE, total_tokens=0)
     assert lsb.blockattn_mxpv_fwd(*a.values()) == binding.OK
+
+
+def test_mx_bwd_argument_checks():
+    """blockattn_mx_bwd: D 64 or 128, D * Tp below 2^32, every pointer present
+    and aligned (16 bytes for codes, out, lse and gradients, 4 for scales),
+    the workspace present, large enough and 256-byte aligned; empty calls
+    succeed before any pointer is looked at."""
+    a = dict(q=FAKE, q_scale=FAKE, k=FAKE, k_scale=FAKE, v=FAKE, v_scale=FAKE, dout=FAKE,
+             dout_scale=FAKE, q_t=FAKE, q_t_scale=FAKE, k_t=FAKE, k_t_scale=FAKE, dout_t=FAKE,
+             dout_t_scale=FAKE, out=FAKE, lse=FAKE, offsets=FAKE, batch=2, total_tokens=100,
+             num_heads=2, head_dim=32, block_size=64, window_blocks=2, scale=0.125, dq=FAKE,
+             dk=FAKE, dv=FAKE, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
+    call = lambda: lsb.blockattn_mx_bwd(*a.values())
+    assert call() == binding.ERR_UNSUPPORTED                  # D = 32
+    a.update(head_dim=128, total_tokens=(1 << 25))            # 128 * 2^25 = 2^32
+    assert call() == binding.ERR_UNSUPPORTED
+    a.update(total_tokens=100)
+    for name, bad in (("dout_t_scale", FAKE + 2), ("k_t", FAKE + 8), ("q_t", None),
+                      ("dv", FAKE + 4), ("lse", None), ("v_scale", FAKE + 1)):
+        a[name] = bad
+        assert call() == binding.ERR_INVALID_ARGUMENT, name
+        a[name] = FAKE
+    a.update(workspace=None)
+    assert call() == binding.ERR_WORKSPACE
+    a.update(workspace=FAKE, workspace_bytes=16)
+    assert call() == binding.ERR_WORKSPACE
+    a.update(workspace=FAKE + 16, workspace_bytes=1 << 30)
+    assert call() == binding.ERR_WORKSPACE
+    a.update(workspace=None, q=None, total_tokens=0)
+    assert call() == binding.OK

@@ -1,0 +1,219 @@
+"""GPU parity of the MXFP8 backward (blockattn_mx_bwd), through the C ABI,
+against the fp64 oracle (oracle.mx_bwd) on the decoded values.  The reading
+is the oracle's ("GEM (Meta)", section "Ultra-low-precision training": the
+backward's products are block-scaled MXFP8 too): every product's operands
+are blocked along its contraction, and P and dS are quantized inside the
+backward, P and dS along each key's queries, dS along each query's keys.
+
+O and lse, the forward's outputs that the backward takes, come from the
+oracle's forward (rounded to bf16 and fp32 as stored) for every user that is
+compared; users that are not compared (only in the long-context workload,
+which is checked on a sample of whole users) take the device forward's.
+
+Bounds (parity_util.MxBwdParity): per element, oracle.mx_bwd_bounds's slack
+(the largest change of a quantized operand that the kernel's own score, dP,
+delta and fp32 errors allow: a block's exponent or a code may flip), plus
+2^-10 of the sum of |quantized operand| |other operand| (the block-scaled
+products' rounding), plus bf16 rounding of the result; the mean error over a
+tensor stays below a quarter of the mean bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_sequence_block_amd as lsb
+import oracle
+from long_sequence_block_amd import workloads as wl
+from parity_util import MxBwdParity, user_ranges
+
+pytestmark = pytest.mark.gpu
+
+RHO = 2.0 ** -11   # relative error of a block-scaled fp8 product sum (test_gpu_mx)
+
+
+def _print(msg):
+    print(msg, flush=True)
+
+
+def device_inputs(c):
+    """The C ABI's layouts of case c on the device: head-dim-blocked codes
+    [T, H, D] with scales [H, T, D/32], token-blocked codes [H, D, 32 nb] with
+    scales [H, nb, D]."""
+    dev = {"offsets": torch.from_numpy(c["offsets"]).cuda()}
+    for n, key in (("q", "q"), ("k", "k"), ("v", "vh"), ("dout", "do")):
+        dev[n] = torch.from_numpy(c[key + "_mx"]).cuda()
+        dev[n + "_sc"] = torch.from_numpy(
+            np.ascontiguousarray(c[key + "_sc"].transpose(1, 0, 2))).cuda()
+    for n, key in (("q_t", "qt"), ("k_t", "kt"), ("dout_t", "dot"), ("v_t", "v")):
+        xt, xs = wl.mx_v_device_layout(c[key + "_mx"], c[key + "_bsc"], c["offsets"])
+        dev[n] = torch.from_numpy(xt).cuda()
+        dev[n + "_sc"] = torch.from_numpy(xs).cuda()
+    return dev
+
+
+def decoded(c, u0, u1):
+    """fp64 values of users [u0, u1) of case c, re-based to their first token."""
+    sub = wl.subset_users(c, slice(u0, u1))
+    off = sub["offsets"]
+    x = {n: oracle.mx_decode(sub[key + "_mx"], sub[key + "_sc"])
+         for n, key in (("q", "q"), ("k", "k"), ("v", "vh"), ("dout", "do"))}
+    for n, key in (("q_t", "qt"), ("k_t", "kt"), ("dout_t", "dot")):
+        x[n] = oracle.mx_decode_user_blocks(sub[key + "_mx"], sub[key + "_bsc"], off)
+    x["offsets"] = off
+    return x
+
+
+def run_mx_bwd(dev, out, lse, B, W, scale):
+    return lsb.mx_bwd(dev["q"], dev["q_sc"], dev["k"], dev["k_sc"], dev["v"], dev["v_sc"],
+                      dev["dout"], dev["dout_sc"], dev["q_t"], dev["q_t_sc"], dev["k_t"],
+                      dev["k_t_sc"], dev["dout_t"], dev["dout_t_sc"], out, lse, dev["offsets"],
+                      B, W, scale)
+
+
+def mx_bwd_parity(c, B, W, scale, users=None, max_tokens=60000):
+    """Run blockattn_mx_bwd on the whole case and compare every element of
+    dq, dk and dv of the users in `users` (a range; all by default)."""
+    off = np.asarray(c["offsets"], np.int64)
+    batch = len(off) - 1
+    T, H, D = c["q_mx"].shape
+    users = range(batch) if users is None else users
+    dev = device_inputs(c)
+    if len(users) == batch:
+        out = torch.zeros((T, H, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.zeros((H, T), dtype=torch.float32, device="cuda")
+    else:
+        out, lse = lsb.mxpv_fwd(dev["q"], dev["q_sc"], dev["k"], dev["k_sc"], dev["v_t"],
+                                dev["v_t_sc"], dev["offsets"], B, W, scale)
+    # the compared users' O and lse: the oracle's forward, as stored
+    sub_off = off[users.start:users.stop + 1] - off[users.start]
+    ranges = [(users.start + a, users.start + b) for a, b in user_ranges(sub_off, max_tokens)]
+    for u0, u1 in ranges:
+        t0, t1 = int(off[u0]), int(off[u1])
+        if t1 == t0:
+            continue
+        x = decoded(c, u0, u1)
+        o, l = oracle.fwd(x["q"], x["k"], x["v"], x["offsets"], B, W, scale)
+        out[t0:t1] = torch.from_numpy(o).to(torch.bfloat16).cuda()
+        lse[:, t0:t1] = torch.from_numpy(l).to(torch.float32).cuda()
+    torch.cuda.synchronize()
+    dq, dk, dv = run_mx_bwd(dev, out, lse, B, W, scale)
+    torch.cuda.synchronize()
+    got = {"dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    o_h, l_h = out.cpu(), lse.cpu()
+    del dev, dq, dk, dv, out, lse
+    p = MxBwdParity()
+    for u0, u1 in ranges:
+        t0, t1 = int(off[u0]), int(off[u1])
+        if t1 == t0:
+            continue
+        x = decoded(c, u0, u1)
+        ref, sl, ab = oracle.mx_bwd_bounds(
+            x["q"], x["k"], x["v"], x["dout"], o_h[t0:t1].double().numpy(),
+            l_h[:, t0:t1].double().numpy(), x["q_t"], x["k_t"], x["dout_t"], x["offsets"], B, W,
+            scale, RHO)
+        for i, name in enumerate(("dq", "dk", "dv")):
+            p.add(name, got[name][t0:t1].double().numpy(), ref[i], sl[i], ab[i],
+                  tag=f"users [{u0},{u1})")
+    p.finish()
+    return p
+
+
+MXB = [
+    # (lengths, H, D, B, W, scale sign)
+    ([300, 77, 0, 5, 130], 2, 64, 64, 2, 1),
+    ([257, 33, 1, 190], 2, 128, 100, 3, 1),
+    # users that start off the packed 32-token grid, a block size that is not
+    # a multiple of 32 (windows start inside a 32-position block)
+    ([45, 33, 70, 31, 64], 2, 64, 7, 5, -1),
+    ([700, 64, 3], 1, 128, 256, 3, -1),
+    ([90, 300], 2, 64, 1, 37, 1),      # sliding window of 37 tokens
+    ([129, 254], 3, 64, 16, 4, 1),
+    # the largest block and window the ABI takes (every earlier key)
+    ([300, 77, 0, 5, 130], 2, 64, 2**31 - 1, 2**31 - 1, 1),
+    # 1101 users: the tile decode's four-users-per-thread form
+    ([int(x) for x in np.random.default_rng(33).integers(0, 30, 1101)], 1, 64, 16, 2, 1),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MXB)))
+def test_mx_bwd_every_element(idx):
+    lengths, H, D, B, W, sign = MXB[idx]
+    _print(f"mxbwd {idx}: {len(lengths)} users, lengths={lengths[:8]} H={H} D={D} B={B} W={W}")
+    c = wl.random_mxbwd_case(500 + idx, lengths, H, D)
+    p = mx_bwd_parity(c, B, W, sign / math.sqrt(D))
+    _print("  " + p.summary())
+
+
+# Codes over the whole finite E4M3 range with block scales far from 2^0:
+# q, q_t 2^-33 .. 2^-27 and k, k_t 2^13 .. 2^19 (O(1) scores), v (forward
+# only) 2^-8 .. 2^-6, v head-dim-blocked 2^-17 .. 2^-7, dO 2^-2 .. 2^3.
+MXB_WIDE = [
+    ([300, 1, 0, 129], 2, 64, 64, 2, 1),
+    ([700, 64, 3], 1, 128, 256, 3, -1),
+]
+WIDE_SCALES = ((94, 100), (140, 146), (119, 121), (110, 120), (125, 130), (94, 100),
+               (140, 146), (125, 130))
+
+
+@pytest.mark.parametrize("idx", range(len(MXB_WIDE)))
+def test_mx_bwd_full_code_range_every_element(idx):
+    lengths, H, D, B, W, sign = MXB_WIDE[idx]
+    _print(f"mxbwd wide {idx}: lengths={lengths} H={H} D={D} B={B} W={W}")
+    c = wl.random_mxbwd_case(600 + idx, lengths, H, D, wide=WIDE_SCALES)
+    assert (c["do_mx"] & 0x7F == 0).any() and ((c["kt_mx"] & 0x78) == 0).any()
+    p = mx_bwd_parity(c, B, W, sign / math.sqrt(D))
+    _print("  " + p.summary())
+
+
+@pytest.mark.timeout(900)
+def test_mx_bwd_jagged_workload_full_size_every_element():
+    """The jagged MXFP8 training step's backward (workload 15) whole, in the
+    launch configuration the benchmark times."""
+    w = wl.WORKLOADS[15]
+    c = wl.draw(w)
+    _print(f"{w.name}: T={int(c['offsets'][-1])} users={w.users}")
+    p = mx_bwd_parity(c, w.block_size, w.window_blocks, w.scale)
+    _print("  " + p.summary())
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("users", [range(0, 1), range(31, 32)])
+def test_mx_bwd_long_context_full_size_sampled_users(users):
+    """The long-context MXFP8 training step's backward (workload 16) run
+    whole; the oracle checks every element of one whole user (users are
+    independent; the others take the device forward's O and lse)."""
+    w = wl.WORKLOADS[16]
+    c = wl.draw(w)
+    _print(f"{w.name}: T={int(c['offsets'][-1])}, comparing users {users}")
+    p = mx_bwd_parity(c, w.block_size, w.window_blocks, w.scale, users=users)
+    _print("  " + p.summary())
+
+
+def test_mx_bwd_deterministic_and_users_independent():
+    """Two calls give bitwise the same gradients, and each user's gradients
+    are bitwise the same alone as inside the batch."""
+    lengths, H, D, B, W = [45, 130, 0, 77], 2, 64, 16, 3
+    c = wl.random_mxbwd_case(700, lengths, H, D)
+    off = c["offsets"]
+    T = int(off[-1])
+    rng = np.random.default_rng(1)
+    out_h = torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32)).to(torch.bfloat16)
+    lse_h = torch.from_numpy(rng.uniform(2.0, 4.0, (H, T)).astype(np.float32))
+    dev = device_inputs(c)
+    g1 = run_mx_bwd(dev, out_h.cuda(), lse_h.cuda(), B, W, 0.125)
+    g2 = run_mx_bwd(dev, out_h.cuda(), lse_h.cuda(), B, W, 0.125)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    for u in range(len(lengths)):
+        t0, t1 = int(off[u]), int(off[u + 1])
+        if t1 == t0:
+            continue
+        cu = wl.subset_users(c, slice(u, u + 1))
+        du = device_inputs(cu)
+        gu = run_mx_bwd(du, out_h[t0:t1].cuda(), lse_h[:, t0:t1].contiguous().cuda(), B, W, 0.125)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, gu):
+            assert torch.equal(a[t0:t1], b), f"user {u}"
