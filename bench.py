@@ -122,7 +122,7 @@ def _oracle_inputs(w, users):
     c = wl.draw(w, users=slice(0, users))
     host = {}
     for key, val in c.items():
-        if key == "offsets" or key.endswith("_mx") or key.endswith("_sc"):
+        if key == "offsets" or key.endswith(("_mx", "_sc", "_bsc")):
             host[key] = val
         else:
             t = torch.from_numpy(val)
@@ -135,6 +135,12 @@ def _oracle_inputs(w, users):
     if w.mx_v:
         host["v"] = oracle.mx_decode_user_blocks(host.pop("v_mx"), host.pop("v_bsc"),
                                                  host["offsets"])
+    if w.mx and w.backward:  # the MXFP8 backward's head-dim- and token-blocked copies
+        host["v_h"] = oracle.mx_decode(host.pop("vh_mx"), host.pop("vh_sc"))
+        host["dout"] = oracle.mx_decode(host.pop("do_mx"), host.pop("do_sc"))
+        for n in ("qt", "kt", "dot"):
+            host[n] = oracle.mx_decode_user_blocks(host.pop(n + "_mx"), host.pop(n + "_bsc"),
+                                                   host["offsets"])
     return host
 
 
@@ -150,7 +156,10 @@ def _oracle_run(w, host):
             oracle.gdpa_bwd(q, k, v, host["dout"], off, B, W, sc, w.act)
         return
     if w.mx_v:  # the weights quantized for P.V
-        oracle.mxpv_fwd(q, k, v, off, B, W, sc)
+        o, l = oracle.mxpv_fwd(q, k, v, off, B, W, sc)
+        if w.backward:  # every product block-scaled
+            oracle.mx_bwd(q, k, host["v_h"], host["dout"], o, l, host["qt"], host["kt"],
+                          host["dot"], off, B, W, sc)
         return
     if w.rope_base:
         q, k = oracle.rope(q, off, w.rope_base), oracle.rope(k, off, w.rope_base)
@@ -304,7 +313,9 @@ def main():
                          "9 and 10 the long-context and jagged forwards with q, k in MXFP8, "
                          "11 the long-context shape as a training step, 12 the training step "
                          "at 1024 users, 13 and 14 the long-context and jagged forwards with "
-                         "q, k, v in MXFP8 and the weights quantized for a block-scaled P.V")
+                         "q, k, v in MXFP8 and the weights quantized for a block-scaled P.V, "
+                         "15 and 16 the jagged and long-context MXFP8 training steps (that "
+                         "forward, then the backward with every product block-scaled)")
     ap.add_argument("--length", type=int, default=0,
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--window-blocks", type=int, default=0,
@@ -361,6 +372,15 @@ def main():
         if w.mx_v:  # v transposed, user-blocked [H, D, 32 nb], scales [H, nb, D]
             vt, vs = wl.mx_v_device_layout(c["v_mx"], c["v_bsc"], c["offsets"])
             d["v_t"], d["v_bsc"] = torch.from_numpy(vt).to(dev), torch.from_numpy(vs).to(dev)
+            if w.backward:  # the MXFP8 backward's v, dO and token-blocked q, k, dO
+                for n in ("vh", "do"):
+                    d[n] = torch.from_numpy(c[n + "_mx"]).to(dev)
+                    d[n + "_sc"] = torch.from_numpy(
+                        np.ascontiguousarray(c[n + "_sc"].transpose(1, 0, 2))).to(dev)
+                for n in ("qt", "kt", "dot"):
+                    xt, xs = wl.mx_v_device_layout(c[n + "_mx"], c[n + "_bsc"], c["offsets"])
+                    d[n], d[n + "_bsc"] = (torch.from_numpy(xt).to(dev),
+                                           torch.from_numpy(xs).to(dev))
         else:
             d["v"] = torch.from_numpy(c["v"]).to(tdt).to(dev)
     else:
@@ -401,6 +421,10 @@ def main():
         elif w.backward and rb:  # gradients through attention and the rotation
             lsb.rope_bwd(qa, ka, d["v"], out, d["dout"], lse, d["offsets"], B, W, sc, rb,
                          grads=grads, workspace=ws)
+        elif w.backward and w.mx:  # every product block-scaled
+            lsb.mx_bwd(qa, d["q_sc"], ka, d["k_sc"], d["vh"], d["vh_sc"], d["do"], d["do_sc"],
+                       d["qt"], d["qt_bsc"], d["kt"], d["kt_bsc"], d["dot"], d["dot_bsc"], out,
+                       lse, d["offsets"], B, W, sc, grads=grads, workspace=ws)
         elif w.backward:
             lsb.bwd(qa, ka, d["v"], out, d["dout"], lse, d["offsets"], B, W, sc,
                     grads=grads, workspace=ws)
@@ -456,6 +480,8 @@ def main():
         fwd_bytes = T * H * (3.0 * D * (1 + 1 / 32) + 2.0 * D + 4)
     # GDPA's backward reads q, k, v, dO and writes dq, dk, dv (no out, no lse)
     bwd_bytes = (T * H * ((7.0 * D * e) if w.act else (8.0 * D * e + 4))) if w.backward else 0.0
+    if w.mx and w.backward:  # seven MXFP8 inputs (one byte + a scale per 32), O, lse in;
+        bwd_bytes = T * H * (7.0 * D * (1 + 1 / 32) + 2.0 * D + 4 + 6.0 * D)  # dq, dk, dv out
     flops = fwd_flops + bwd_flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -495,7 +521,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp8" if w.mx_v else "mxfp8(qk)+bf16" if w.mx else w.dtype,
         "data": "synthetic (seeded; lognormal jagged lengths, N(0,1) values"
-                + ("; random E4M3 codes and E8M0 scales for q, k, v)" if w.mx_v else
+                + ("; random E4M3 codes and E8M0 scales for q, k, v, dO and the backward's "
+                   "second copies)" if w.mx_v and w.backward else
+                   "; random E4M3 codes and E8M0 scales for q, k, v)" if w.mx_v else
                    "; random E4M3 codes and E8M0 scales for q, k)" if w.mx else ")"),
         "config": {"workload": w.name, "users": w.users, "tokens": T, "heads": H,
                    "head_dim": D, "block_size": B, "window_blocks": W,

@@ -165,7 +165,12 @@ __device__ __forceinline__ void dma_trows(const uint8_t *x, const uint8_t *xsc, 
 }
 
 // Block-scaled E4M3 codes of the 16 values x[] of this lane; the lane pair
-// (n, n + 32) holds one block of 32.  Returns the scale byte E + 127.
+// (n, n + 32) holds one block of 32.  Returns the scale byte E + 127.  The
+// scaled conversion divides by 2 to the power of its scale operand's
+// exponent field, so the fp32 bit pattern (E + 127) << 23 gives x 2^-E for
+// every E in [-127, 127] (checked on gfx950 against the plain conversion of
+// x 2^-E, including E = -127, whose pattern is +0.0).
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int quant_block(const float (&x)[16], int *w) {
     float a = 0.f;
 #pragma unroll
@@ -173,12 +178,13 @@ __device__ __forceinline__ int quant_block(const float (&x)[16], int *w) {
     a = swap_max(a);
     // frexp exponent e (a = f 2^e, f in [0.5, 1)): floor(log2 a) = e - 1
     const int E = a > 0.f ? max(__builtin_amdgcn_frexp_expf(a) - 8, -127) : -127;
-    const float mult = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E
+    const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        int c = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * j] * mult, x[4 * j + 1] * mult, 0, false);
-        c = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * j + 2] * mult, x[4 * j + 3] * mult, c, true);
-        w[j] = c;
+        i16x2 c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, x[4 * j], x[4 * j + 1],
+                                                          sc, false);
+        c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, x[4 * j + 2], x[4 * j + 3], sc, true);
+        w[j] = __builtin_bit_cast(int, c);
     }
     return E + 127;
 }
@@ -416,10 +422,11 @@ __global__ __launch_bounds__(kThreads, (kWaves<D, ROLE>)) void bwd_mx(Shape s, M
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int a = c0 + 32 * h;
+            // (a half that no lane of the wave sees always counts as masked
+            // below, and every position of it fails the visibility test, so
+            // it comes out as zeros without a path of its own)
             float p[16], ds[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = ds[r] = 0.f;
-            if (h ? live1 : live0) {
+            {
                 i32x8 f1[D / 64], f2[D / 64];
                 int s1[D / 64], s2[D / 64];
                 read_half8<D>(b, b + 64 * D + scale_mis<D>(s, t.h, t.tok0 + c0) + srd, h, rd, f1,
@@ -456,13 +463,23 @@ __global__ __launch_bounds__(kThreads, (kWaves<D, ROLE>)) void bwd_mx(Shape s, M
                 const f32x16 dp = hd_product<D>(f2, s2, fb, sb, nd);
                 const bool masked = ROLE == 0 ? (a + 31 > wr0 || a < full_lo)
                                               : (a < w_last || a + 31 >= full_hi);
-                const int x0 = a + 16 * g - my_lo;
+                // (two loops on the wave-uniform flag: the unmasked halves,
+                // most of them, carry no visibility test)
+                if (masked) {
+                    const int x0 = a + 16 * g - my_lo;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const bool vis = !masked || (ROLE == 0 ? (uint32_t)(x0 + r) <= span
-                                                           : (uint32_t)(x0 + r) < span);
-                    p[r] = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2[r])) : 0.f;
-                    ds[r] = p[r] * dp[r];
+                    for (int r = 0; r < 16; ++r) {
+                        const bool vis = ROLE == 0 ? (uint32_t)(x0 + r) <= span
+                                                   : (uint32_t)(x0 + r) < span;
+                        p[r] = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2[r])) : 0.f;
+                        ds[r] = p[r] * dp[r];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2[r]));
+                        ds[r] = p[r] * dp[r];
+                    }
                 }
             }
             if constexpr (ROLE == 0) {
