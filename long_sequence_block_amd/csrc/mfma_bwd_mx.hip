@@ -170,7 +170,6 @@ __device__ __forceinline__ void dma_trows(const uint8_t *x, const uint8_t *xsc, 
 // exponent field, so the fp32 bit pattern (E + 127) << 23 gives x 2^-E for
 // every E in [-127, 127] (checked on gfx950 against the plain conversion of
 // x 2^-E, including E = -127, whose pattern is +0.0).
-typedef short i16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int quant_block(const float (&x)[16], int *w) {
     float a = 0.f;
 #pragma unroll

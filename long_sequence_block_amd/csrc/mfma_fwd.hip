@@ -371,7 +371,9 @@ __global__ __launch_bounds__(kThreads, (kWavesPerSimd<D, MX>)) void fwd_mfma(
                     }
                 }
                 const int E = bm == -INFINITY ? -127 : (int)fmaxf(floorf(bm * c) - 7.f - m, -127.f);
-                const float mult = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E
+                // the scaled conversion divides by 2 to the power of its scale
+                // operand's exponent field: 2^E as a bit pattern
+                const float esc = __uint_as_float((uint32_t)(E + 127) << 23);
                 e8[h] = E + 127;
                 // (this half's weights join l before the next half can
                 // rescale it)
@@ -386,8 +388,10 @@ __global__ __launch_bounds__(kThreads, (kWavesPerSimd<D, MX>)) void fwd_mfma(
                             p[i] = __builtin_amdgcn_exp2f(fmaf(x[4 * j + i], c, -m));
                             ls[i] += p[i];
                         }
-                        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * mult, p[1] * mult, 0, false);
-                        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * mult, p[3] * mult, w, true);
+                        i16x2 cv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                            i16x2{0, 0}, p[0], p[1], esc, false);
+                        cv = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(cv, p[2], p[3], esc, true);
+                        w = __builtin_bit_cast(int, cv);
                     }
                     pf8[4 * h + j] = w;
                 }

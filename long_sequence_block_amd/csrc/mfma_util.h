@@ -52,6 +52,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const bf16 *base, int
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));  // packed fp8 conversions
 template <int D>
 __device__ __forceinline__ i32x4 row_desc(const bf16 *base, int rows, int64_t rs) {
     const uint32_t bytes = rows > 0 ? (uint32_t)((int64_t)(rows - 1) * rs * 2 + D * 2) : 0u;
