@@ -32,7 +32,10 @@ HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 # Per-file additions.  The bf16 forward's scores are finite or -inf (never
 # NaN), so it is built without NaN semantics and with IEEE mode off, which
 # lets row maxima use v_max3_f32 without canonicalising each input.
-FILE_FLAGS = {"mfma_fwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# The MXFP8 backward keeps its MFMA results in VGPRs (the vector work reads
+# every score and dP value; in AGPRs each would first be copied out).
+FILE_FLAGS = {"mfma_fwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+              "mfma_bwd_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
