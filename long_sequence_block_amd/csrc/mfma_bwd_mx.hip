@@ -114,8 +114,8 @@ __device__ __forceinline__ void dma_rows8(const uint8_t *x, const Shape &s, int6
     dma_tile<D / 2>(row_desc<D / 2>(base, rows, rs), dst, voff, wave);
 }
 
-// First byte of the scales of row tok, head h, in [H, T, D/32], and where the
-// dword-aligned window that holds them starts (mis bytes earlier).
+// How many bytes before the scales of row tok, head h ([H, T, D/32]) the
+// dword-aligned window that dma_scales loads starts.
 template <int D>
 __device__ __forceinline__ int scale_mis(const Shape &s, int h, int64_t tok) {
     return (int)((((int64_t)h * s.T + tok) * (D / 32)) & 3);
