@@ -132,8 +132,9 @@ MXB = [
     ([129, 254], 3, 64, 16, 4, 1),
     # the largest block and window the ABI takes (every earlier key)
     ([300, 77, 0, 5, 130], 2, 64, 2**31 - 1, 2**31 - 1, 1),
-    # 1101 users: the tile decode's four-users-per-thread form
+    # 1101 users: the tile decode's four-users-per-thread form, both head dims
     ([int(x) for x in np.random.default_rng(33).integers(0, 30, 1101)], 1, 64, 16, 2, 1),
+    ([int(x) for x in np.random.default_rng(34).integers(0, 40, 1101)], 1, 128, 32, 3, -1),
 ]
 
 
@@ -217,3 +218,14 @@ def test_mx_bwd_deterministic_and_users_independent():
         torch.cuda.synchronize()
         for a, b in zip(g1, gu):
             assert torch.equal(a[t0:t1], b), f"user {u}"
+
+
+def test_mx_bwd_empty_batch():
+    """Users with no tokens (T = 0): the call succeeds and launches nothing."""
+    c = wl.random_mxbwd_case(710, [0, 0, 0], 2, 64)
+    dev = device_inputs(c)
+    out = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((2, 0), dtype=torch.float32, device="cuda")
+    dq, dk, dv = run_mx_bwd(dev, out, lse, 16, 2, 0.125)
+    torch.cuda.synchronize()
+    assert dq.shape == dk.shape == dv.shape == (0, 2, 64)
