@@ -38,7 +38,8 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "block-attention TFLOP/s and tokens/s (fwd+bwd, jagged bf16) and % of MFMA peak"
 KERNEL_SOURCES = ("common.h", "kernels.h", "mfma_util.h", "lds_tile.h", "api.hip",
-                  "scalar_kernels.hip", "mfma_fwd.hip", "mfma_bwd.hip", "rope.hip")
+                  "scalar_kernels.hip", "mfma_fwd.hip", "mfma_bwd.hip", "mfma_bwd_mx.hip",
+                  "rope.hip")
 
 
 def pairs_per_head(offsets: np.ndarray, B: int, W: int) -> int:
@@ -48,6 +49,23 @@ def pairs_per_head(offsets: np.ndarray, B: int, W: int) -> int:
         i = np.arange(L, dtype=np.int64)
         total += int(np.sum(i - np.maximum(0, i // B - W + 1) * B + 1))
     return total
+
+
+def cpu_sample_users(w, offsets: np.ndarray, budget: float = 1.5e12) -> int:
+    """Users [0, n) whose oracle work (forward, and backward for training
+    workloads) stays within `budget` flops, at least one: about 30 s on 16
+    host threads for the plain oracle.  The MXFP8 oracle quantizes every
+    weight and dS element in scalar code, so it gets a quarter of that."""
+    per = 4.0 * w.head_dim + (8.0 * w.head_dim if w.backward else 0.0)
+    budget = budget / 4 if w.mx else budget
+    spent, n = 0.0, 0
+    for u in range(len(offsets) - 1):
+        spent += per * w.heads * pairs_per_head(offsets[u:u + 2] - offsets[u], w.block_size,
+                                                w.window_blocks)
+        if n > 0 and spent > budget:
+            break
+        n += 1
+    return max(n, 1)
 
 
 def source_code(text: str) -> str:
@@ -543,7 +561,8 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        users = min(args.cpu_users, w.users) if args.cpu_users > 0 else w.users
+        users = (min(args.cpu_users, w.users) if args.cpu_users > 0
+                 else cpu_sample_users(w, off_np))
         res["cpu_baseline"] = cpu_baseline(w, users, 4.0 * D + (8.0 * D if w.backward else 0))
     print(json.dumps(res), flush=True)
 
