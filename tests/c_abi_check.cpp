@@ -221,6 +221,29 @@ void check_rejections(hipStream_t stream) {
         {"empty batch", blockattn_fwd(nullptr, nullptr, nullptr, nullptr, 0, 0, 1, 64, 16, 1,
                                       0.1f, BLOCKATTN_BF16, nullptr, nullptr, stream),
          BLOCKATTN_OK},
+        {"mx_fwd head_dim 32", blockattn_mx_fwd(p, p, p, p, p, off, 1, 16, 1, 32, 16, 1, 0.1f, p,
+                                                (float *)p, stream),
+         BLOCKATTN_ERR_UNSUPPORTED},
+        {"mxpv_fwd head_dim 32", blockattn_mxpv_fwd(p, p, p, p, p, p, off, 1, 16, 1, 32, 16, 1,
+                                                    0.1f, p, (float *)p, stream),
+         BLOCKATTN_ERR_UNSUPPORTED},
+        {"mx_bwd head_dim 32",
+         blockattn_mx_bwd(p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, (const float *)p, off, 1,
+                          16, 1, 32, 16, 1, 0.1f, p, p, p, p, 1 << 20, stream),
+         BLOCKATTN_ERR_UNSUPPORTED},
+        {"mx_bwd misaligned scale",
+         blockattn_mx_bwd(p, p, p, p, p, p, p, p, p, (char *)p + 2, p, p, p, p, p,
+                          (const float *)p, off, 1, 16, 1, 64, 16, 1, 0.1f, p, p, p, p, 1 << 20,
+                          stream),
+         BLOCKATTN_ERR_INVALID_ARGUMENT},
+        {"mx_bwd null dout_t",
+         blockattn_mx_bwd(p, p, p, p, p, p, p, p, p, p, p, p, nullptr, p, p, (const float *)p,
+                          off, 1, 16, 1, 64, 16, 1, 0.1f, p, p, p, p, 1 << 20, stream),
+         BLOCKATTN_ERR_INVALID_ARGUMENT},
+        {"mx_bwd workspace small",
+         blockattn_mx_bwd(p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, (const float *)p, off, 1,
+                          16, 1, 64, 16, 1, 0.1f, p, p, p, p, 8, stream),
+         BLOCKATTN_ERR_WORKSPACE},
     };
     for (const Want &w : cases) {
         const bool ok = w.got == w.want;
