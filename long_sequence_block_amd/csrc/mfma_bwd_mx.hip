@@ -424,69 +424,78 @@ __global__ __launch_bounds__(kThreads, (kWaves<D, ROLE>)) void bwd_mx(Shape s, M
             // (a half that no lane of the wave sees always counts as masked
             // below, and every position of it fails the visibility test, so
             // it comes out as zeros without a path of its own)
-            float p[16], ds[16];
+            const bool masked = ROLE == 0 ? (a + 31 > wr0 || a < full_lo)
+                                          : (a < w_last || a + 31 >= full_hi);
+            const int x0 = a + 16 * g - my_lo;
+            // The weights first (scores, P and, in the key pass, P's codes),
+            // then dP and dS, so that only one operand half and one product
+            // result are live at a time.  Register r is position a + 16g + r;
+            // lse * log2(e) and -delta per register belong to the lane's
+            // query (query pass) or to the half's queries 16g + r (key pass).
+            const lds_t *st = b + MxBuf<D>::kStats + 4 * (a - c0 + 16 * g);
+            float p[16];
             {
-                i32x8 f1[D / 64], f2[D / 64];
-                int s1[D / 64], s2[D / 64];
+                i32x8 f1[D / 64];
+                int s1[D / 64];
                 read_half8<D>(b, b + 64 * D + scale_mis<D>(s, t.h, t.tok0 + c0) + srd, h, rd, f1,
                               s1);
-                read_half8<D>(b + kT, b + kT + 64 * D + scale_mis<D>(s, t.h, t.tok0 + c0) + srd,
-                              h, rd, f2, s2);
-                // scores and dP - delta; register r is position a + 16g + r.
-                // -delta and lse * log2(e) per register: the lane's query
-                // (query pass) or the half's queries 16g + r (key pass).
-                f32x16 nd;
                 float l2[16];
                 if constexpr (ROLE == 0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        nd[r] = ndlt;
-                        l2[r] = lse2;
-                    }
+                    for (int r = 0; r < 16; ++r) l2[r] = lse2;
                 } else {
-                    const lds_t *st = b + MxBuf<D>::kStats + 4 * (a - c0 + 16 * g);
 #pragma unroll
                     for (int r = 0; r < 16; r += 4) {
                         const f32x4v l4 = *(const __attribute__((address_space(3))) f32x4v *)(
                             st + 4 * r);
-                        const f32x4v d4 = *(const __attribute__((address_space(3))) f32x4v *)(
-                            st + 256 + 4 * r);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            l2[r + e] = l4[e];
-                            nd[r + e] = d4[e];
-                        }
+                        for (int e = 0; e < 4; ++e) l2[r + e] = l4[e];
                     }
                 }
                 const f32x16 sc = hd_product<D>(f1, s1, fa, sa, f32x16{});
-                const f32x16 dp = hd_product<D>(f2, s2, fb, sb, nd);
-                const bool masked = ROLE == 0 ? (a + 31 > wr0 || a < full_lo)
-                                              : (a < w_last || a + 31 >= full_hi);
                 // (two loops on the wave-uniform flag: the unmasked halves,
                 // most of them, carry no visibility test)
                 if (masked) {
-                    const int x0 = a + 16 * g - my_lo;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const bool vis = ROLE == 0 ? (uint32_t)(x0 + r) <= span
                                                    : (uint32_t)(x0 + r) < span;
                         p[r] = vis ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2[r])) : 0.f;
-                        ds[r] = p[r] * dp[r];
                     }
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
+                    for (int r = 0; r < 16; ++r)
                         p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -l2[r]));
-                        ds[r] = p[r] * dp[r];
-                    }
                 }
             }
-            if constexpr (ROLE == 0) {
-                e1[h] = quant_block(ds, q1 + 4 * h);
-            } else {
-                e1[h] = quant_block(p, q1 + 4 * h);
-                e2[h] = quant_block(ds, q2 + 4 * h);
+            if constexpr (ROLE == 1) e1[h] = quant_block(p, q1 + 4 * h);
+            float ds[16];
+            {
+                i32x8 f2[D / 64];
+                int s2[D / 64];
+                read_half8<D>(b + kT, b + kT + 64 * D + scale_mis<D>(s, t.h, t.tok0 + c0) + srd,
+                              h, rd, f2, s2);
+                f32x16 nd;
+                if constexpr (ROLE == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) nd[r] = ndlt;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4) {
+                        const f32x4v d4 = *(const __attribute__((address_space(3))) f32x4v *)(
+                            st + 256 + 4 * r);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) nd[r + e] = d4[e];
+                    }
+                }
+                const f32x16 dp = hd_product<D>(f2, s2, fb, sb, nd);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ds[r] = p[r] * dp[r];
             }
+            if constexpr (ROLE == 0)
+                e1[h] = quant_block(ds, q1 + 4 * h);
+            else
+                e2[h] = quant_block(ds, q2 + 4 * h);
         }
         const i32x8 x1 = i32x8{q1[0], q1[1], q1[2], q1[3], q1[4], q1[5], q1[6], q1[7]};
         if constexpr (ROLE == 0) {
