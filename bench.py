@@ -106,11 +106,11 @@ def measured_traffic(kernel: str, workload: str):
 def measured_counters(kernel: str, workload: str):
     """Shader clock and MFMA busy share of the dominant kernel from the
     committed rocprofv3 counter summary (fwd_mfma for the forward; for the
-    backward, each of its bwd_mfma passes), or None if there is none for the
+    backward, each of its passes, bf16 or MXFP8), or None if there is none for the
     current kernel sources."""
     files = ([f"fwd_{workload}_counters.md", f"fwd-bwd_{workload}_counters.md"]
              if kernel == "fwd" else [f"fwd-bwd_{workload}_counters.md"])
-    row_key = "fwd_mfma" if kernel == "fwd" else "bwd_mfma"
+    row_key = ("fwd_mfma",) if kernel == "fwd" else ("bwd_mfma", "bwd_mx")
     for f in files:
         path = os.path.join(ROOT, "profiles", f)
         if not os.path.exists(path):
