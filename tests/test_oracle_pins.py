@@ -1151,3 +1151,48 @@ def test_mx_bwd_p_and_ds_blocks_hold_one_keys_queries():
         np.testing.assert_allclose(got_dv[key], 4.0 * dv[key], rtol=1e-12)
         np.testing.assert_allclose(got_dk[key], 4.0 * dk[key], rtol=1e-9,
                                    atol=1e-12 * np.abs(dk).max())
+
+
+def _mx_quantize(x, off, axis):
+    """x quantized with the block rule along head dims (axis 'd', 32-element
+    blocks) or along each user's tokens (axis 't', 32-token blocks from the
+    user's first token)."""
+    y = x.copy()
+    T, H, D = x.shape
+    if axis == "d":
+        for t in range(T):
+            for h in range(H):
+                for b in range(D // 32):
+                    y[t, h, 32 * b:32 * b + 32] = oracle.mx_quantize_block(x[t, h, 32 * b:32 * b + 32])
+        return y
+    for u in range(len(off) - 1):
+        for t0 in range(int(off[u]), int(off[u + 1]), 32):
+            t1 = min(t0 + 32, int(off[u + 1]))
+            for h in range(H):
+                for d in range(D):
+                    y[t0:t1, h, d] = oracle.mx_quantize_block(x[t0:t1, h, d])
+    return y
+
+
+def test_mx_bwd_error_against_the_exact_gradient():
+    """A property, not a pin: on N(0,1) inputs quantized along each product's
+    contraction, the MXFP8 backward stays within 10% (relative L2 norm) of
+    the exact gradient of the unquantized inputs, and quantizing P and dS in
+    the backward adds at most 4% (three mantissa bits round a value by about
+    2-4%).  A wrong block exponent or axis would land far outside."""
+    rng = np.random.default_rng(12)
+    off = wl.offsets_from_lengths([200, 37, 130])
+    T, H, D, B, W = int(off[-1]), 2, 64, 32, 3
+    sc = 1 / math.sqrt(D)
+    q, k, v, do = (rng.standard_normal((T, H, D)) for _ in range(4))
+    exact = oracle.bwd(q, k, v, do, off, B, W, sc)
+    qd, kd, vd, dd = (_mx_quantize(x, off, "d") for x in (q, k, v, do))
+    qt, kt, dt = (_mx_quantize(x, off, "t") for x in (q, k, do))
+    o, lse = oracle.fwd(qd, kd, vd, off, B, W, sc)
+    args = (qd, kd, vd, dd, o, lse, qt, kt, dt, off, B, W, sc)
+    got = oracle.mx_bwd(*args)
+    unq = oracle.mx_bwd(*args, quantize=False)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    for g, e, u in zip(got, exact, unq):
+        assert 0.01 < rel(g, e) < 0.10
+        assert 0.005 < rel(g, u) < 0.04
