@@ -632,11 +632,16 @@ struct BwdSched {
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t lds_addr(const lds_t *p) { return (uint32_t)(uintptr_t)p; }
 
-// Tile index of the n-th request of a group: runs group, group + ngroups,
-// ... of kRunTiles tiles, in order.
+// Tile index of the n-th request of a group.  The table is cut into rounds
+// of ngroups runs of kRunTiles tiles; a group takes one run of each round,
+// in snake order (run `group` of even rounds, run ngroups-1-group of odd
+// ones), so a group that drew a costly run in one round draws a cheap end of
+// the next where run costs trend along the table.
 // (Saturated at INT32_MAX, which no tile index reaches.)
 __device__ __forceinline__ int queue_tile(int n, int group, int ngroups) {
-    const int64_t j = ((int64_t)(n / kRunTiles) * ngroups + group) * kRunTiles + n % kRunTiles;
+    const int r = n / kRunTiles;
+    const int gq = (r & 1) ? ngroups - 1 - group : group;
+    const int64_t j = ((int64_t)r * ngroups + gq) * kRunTiles + n % kRunTiles;
     return (int)min(j, (int64_t)INT32_MAX);
 }
 
