@@ -28,6 +28,25 @@ int oracle_gdpa_bwd(const double *q, const double *k, const double *v, const dou
                     const int32_t *offsets, int batch, int64_t T, int H, int D, int B, int W,
                     double scale, int act, double *dq, double *dk, double *dv);
 int64_t oracle_pair_count(const int32_t *offsets, int batch, int B, int W);
+int oracle_mxpv_fwd(const double *q, const double *k, const double *v, const int32_t *offsets,
+                    int batch, int64_t T, int H, int D, int B, int W, double scale, double *out,
+                    double *lse);
+int oracle_mxpv_slack(const double *q, const double *k, const double *v,
+                      const int32_t *offsets, int batch, int64_t T, int H, int D, int B, int W,
+                      double scale, const double *eps2, double *slack);
+int oracle_mx_bwd(const double *q, const double *k, const double *v, const double *dout,
+                  const double *out, const double *lse, const double *qt, const double *kt,
+                  const double *dot_t, const int32_t *offsets, int batch, int64_t T, int H,
+                  int D, int B, int W, double scale, int quant, double *dq, double *dk,
+                  double *dv);
+int oracle_mx_bwd_bounds(const double *q, const double *k, const double *v,
+                         const double *dout, const double *out, const double *lse,
+                         const double *qt, const double *kt, const double *dot_t,
+                         const int32_t *offsets, int batch, int64_t T, int H, int D, int B,
+                         int W, double scale, double rho, double *dq, double *dk, double *dv,
+                         double *sl_dq, double *sl_dk, double *sl_dv, double *ab_dq,
+                         double *ab_dk, double *ab_dv);
+void oracle_mx_quantize_block(double *x, int64_t n);
 }
 
 namespace {
@@ -100,6 +119,30 @@ void abi_checks() {
     expect(blockattn_mx_fwd(kFake, kFake, kFake, kFake, kFake, off, 2, 100, 2, 32, 64, 2, 0.125f,
                             kFake, (float *)kFake, nullptr) == BLOCKATTN_ERR_UNSUPPORTED,
            "mx D = 32");
+    expect(blockattn_mxpv_fwd(kFake, kFake, kFake, kFake, kFake, kFake, off, 2, 100, 2, 32, 64,
+                              2, 0.125f, kFake, (float *)kFake, nullptr) ==
+               BLOCKATTN_ERR_UNSUPPORTED, "mxpv D = 32");
+    expect(blockattn_mxpv_fwd(kFake, kFake, kFake, kFake, nullptr, kFake, off, 2, 100, 2, 64, 64,
+                              2, 0.125f, kFake, (float *)kFake, nullptr) ==
+               BLOCKATTN_ERR_INVALID_ARGUMENT, "mxpv null v_t");
+    expect(blockattn_mx_bwd(kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake,
+                            kFake, kFake, kFake, kFake, kFake, (const float *)kFake, off, 2, 100,
+                            2, 32, 64, 2, 0.125f, kFake, kFake, kFake, kFake, 1 << 20,
+                            nullptr) == BLOCKATTN_ERR_UNSUPPORTED, "mx_bwd D = 32");
+    expect(blockattn_mx_bwd(kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake,
+                            (char *)kFake + 2, kFake, kFake, kFake, kFake, kFake,
+                            (const float *)kFake, off, 2, 100, 2, 64, 64, 2, 0.125f, kFake,
+                            kFake, kFake, kFake, 1 << 20, nullptr) ==
+               BLOCKATTN_ERR_INVALID_ARGUMENT, "mx_bwd misaligned scale");
+    expect(blockattn_mx_bwd(kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake, kFake,
+                            kFake, kFake, kFake, kFake, kFake, (const float *)kFake, off, 2, 100,
+                            2, 64, 64, 2, 0.125f, kFake, kFake, kFake, kFake, 16,
+                            nullptr) == BLOCKATTN_ERR_WORKSPACE, "mx_bwd workspace small");
+    expect(blockattn_mx_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, off, 2, 0, 2, 64, INT32_MAX, INT32_MAX, 0.125f, nullptr,
+                            nullptr, nullptr, nullptr, 0, nullptr) == BLOCKATTN_OK,
+           "mx_bwd empty");
     expect(blockattn_rope(kFake, kFake, off, 2, 100, 2, 64, 0.f, BLOCKATTN_BF16, kFake, kFake,
                           nullptr) == BLOCKATTN_ERR_INVALID_ARGUMENT, "rope base 0");
     expect(blockattn_gdpa_fwd(kFake, kFake, kFake, off, 2, 100, 2, 64, 64, 2, 0.125f, 3,
@@ -151,7 +194,36 @@ void oracle_checks() {
         }
         for (double x : o) expect(std::isfinite(x), "finite output");
         expect(oracle_pair_count(off.data(), batch, c.B, c.W) >= 0, "pair count");
+        // the MXFP8 definitions on the same shapes (the values need not be
+        // codes: the oracle's quantization applies to whatever it is given)
+        expect(oracle_mxpv_fwd(q.data(), k.data(), v.data(), off.data(), batch, T, c.H, c.D, c.B,
+                               c.W, 0.5, o.data(), lse.data()) == 0, "oracle_mxpv_fwd");
+        std::vector<double> eps2((size_t)c.H * T, 1e-3), sl(n);
+        expect(oracle_mxpv_slack(q.data(), k.data(), v.data(), off.data(), batch, T, c.H, c.D,
+                                 c.B, c.W, 0.5, eps2.data(), sl.data()) == 0, "oracle_mxpv_slack");
+        expect(oracle_fwd(q.data(), k.data(), v.data(), off.data(), batch, T, c.H, c.D, c.B, c.W,
+                          0.5, o.data(), lse.data()) == 0, "oracle_fwd for the mx backward");
+        for (int quant = 0; quant <= 1; ++quant)
+            expect(oracle_mx_bwd(q.data(), k.data(), v.data(), d.data(), o.data(), lse.data(),
+                                 q.data(), k.data(), d.data(), off.data(), batch, T, c.H, c.D,
+                                 c.B, c.W, 0.5, quant, dq.data(), dk.data(), dv.data()) == 0,
+                   "oracle_mx_bwd");
+        std::vector<double> s1(n), s2(n), s3(n), a1(n), a2(n), a3(n);
+        expect(oracle_mx_bwd_bounds(q.data(), k.data(), v.data(), d.data(), o.data(), lse.data(),
+                                    q.data(), k.data(), d.data(), off.data(), batch, T, c.H, c.D,
+                                    c.B, c.W, 0.5, 1.0 / 2048, dq.data(), dk.data(), dv.data(),
+                                    s1.data(), s2.data(), s3.data(), a1.data(), a2.data(),
+                                    a3.data()) == 0, "oracle_mx_bwd_bounds");
+        for (double x : dq) expect(std::isfinite(x), "finite mx dq");
     }
+    // the block rule on odd lengths, zeros and a lone value
+    for (int64_t len : {0, 1, 31, 33, 95}) {
+        std::vector<double> b = values((size_t)len, 7);
+        if (len > 2) b[1] = 0.0;
+        oracle_mx_quantize_block(b.data(), len);
+        for (double x : b) expect(std::isfinite(x), "finite block codes");
+    }
+    oracle_mx_quantize_block(nullptr, 5);
     // malformed offsets are rejected, not read past
     const int32_t bad[3] = {0, 9, 4};
     std::vector<double> x(64, 0.0), y(64, 0.0), l(16, 0.0);
