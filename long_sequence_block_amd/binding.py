@@ -226,25 +226,53 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
+def _check_tensor(t, shape, dtype, dev, what):
+    """A caller's tensor: the given shape and dtype, contiguous, on device
+    dev (a kernel handed a host pointer or a wrong-sized buffer would fault,
+    so these are checked before any call)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{what} must be on {dev}")
+
+
+def _check_offsets(offsets, dev):
+    if (not isinstance(offsets, torch.Tensor) or offsets.dtype != torch.int32
+            or offsets.dim() != 1 or offsets.numel() < 1 or not offsets.is_contiguous()
+            or not offsets.is_cuda or offsets.device != dev):
+        raise ValueError(f"offsets must be a contiguous 1-D int32 tensor of batch + 1 "
+                         f"entries on {dev}")
+
+
 def _check(q, k, v, offsets):
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must be [T, H, D] tensors of one shape")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
-    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
-        raise ValueError("offsets must be a 1-D int32 device tensor")
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not q.is_cuda:
+        raise ValueError("q must be a [T, H, D] device tensor")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, q.shape, q.dtype, q.device, n)
+    _check_offsets(offsets, q.device)
 
 
 def _check_like(q, *ts, what="out and dout"):
     for t in ts:
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{what} must match q")
+        _check_tensor(t, q.shape, q.dtype, q.device, what)
 
 
-def _check_lse(lse, H, T):
-    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [H, T] tensor")
+def _check_lse(lse, H, T, dev):
+    _check_tensor(lse, (H, T), torch.float32, dev, "lse")
+
+
+def _outputs(q, out, lse, out_dtype=None):
+    """The forward's out [T, H, D] and lse fp32 [H, T]: the caller's, checked,
+    or new ones (called with the call's stream current)."""
+    T, H, D = q.shape
+    dt = q.dtype if out_dtype is None else out_dtype
+    out = torch.empty((T, H, D), dtype=dt, device=q.device) if out is None else out
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor(out, (T, H, D), dt, q.device, "out")
+    _check_tensor(lse, (H, T), torch.float32, q.device, "lse")
+    return out, lse
 
 
 def _torch_stream(stream):
@@ -255,20 +283,33 @@ def _torch_stream(stream):
 def _workspace(q, offsets, code, workspace):
     """The backward's workspace tensor: the caller's, or a new device buffer
     of blockattn_bwd_workspace_size bytes (None if none is needed).  Called
-    with the call's stream current (see above)."""
+    with the call's stream current (see above).  Its size and alignment are
+    the C call's to check."""
     T, H, _ = q.shape
     need = blockattn_bwd_workspace_size(T, offsets.numel() - 1, H, code)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and (not isinstance(workspace, torch.Tensor)
+                                  or not workspace.is_cuda or workspace.device != q.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
     return workspace
 
 
 def _ws_args(ws):
-    return (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+    return (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
 
 
-def _grads(q, grads):
-    return tuple(torch.empty_like(q) for _ in range(3)) if grads is None else grads
+def _grads(q, grads, dtype=None):
+    """dq, dk, dv [T, H, D]: the caller's three tensors, checked, or new ones."""
+    dt = q.dtype if dtype is None else dtype
+    if grads is None:
+        return tuple(torch.empty(q.shape, dtype=dt, device=q.device) for _ in range(3))
+    if len(grads) != 3:
+        raise ValueError("grads must be three tensors (dq, dk, dv)")
+    for t, n in zip(grads, ("dq", "dk", "dv")):
+        _check_tensor(t, q.shape, dt, q.device, n)
+    return tuple(grads)
 
 
 def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
@@ -278,8 +319,7 @@ def fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float,
     T, H, D = q.shape
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
-        out = torch.empty_like(q) if out is None else out
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+        out, lse = _outputs(q, out, lse)
         rc = blockattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
                            offsets.numel() - 1, T, H, D, block_size, window_blocks,
                            float(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr(),
@@ -295,7 +335,7 @@ def bwd(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks: int,
     _check(q, k, v, offsets)
     T, H, D = q.shape
     _check_like(q, out, dout)
-    _check_lse(lse, H, T)
+    _check_lse(lse, H, T, q.device)
     code = _dtype_code(q)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
@@ -321,7 +361,7 @@ def bwd_noalloc(q, k, v, out, dout, lse, offsets, block_size: int, window_blocks
     _check(q, k, v, offsets)
     T, H, D = q.shape
     _check_like(q, out, dout)
-    _check_lse(lse, H, T)
+    _check_lse(lse, H, T, q.device)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
         dq, dk, dv = _grads(q, grads)
@@ -342,8 +382,7 @@ def swa_fwd(q, k, v, offsets, window_tokens: int, scale: float, out=None, lse=No
     T, H, D = q.shape
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
-        out = torch.empty_like(q) if out is None else out
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+        out, lse = _outputs(q, out, lse)
         rc = blockattn_swa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
                                offsets.numel() - 1, T, H, D, window_tokens, float(scale),
                                _dtype_code(q), out.data_ptr(), lse.data_ptr(), st.cuda_stream)
@@ -358,7 +397,7 @@ def swa_bwd(q, k, v, out, dout, lse, offsets, window_tokens: int, scale: float,
     _check(q, k, v, offsets)
     T, H, D = q.shape
     _check_like(q, out, dout)
-    _check_lse(lse, H, T)
+    _check_lse(lse, H, T, q.device)
     code = _dtype_code(q)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
@@ -402,7 +441,7 @@ def rope_bwd(q_rot, k_rot, v, out, dout, lse, offsets, block_size: int, window_b
     _check(q_rot, k_rot, v, offsets)
     T, H, D = q_rot.shape
     _check_like(q_rot, out, dout)
-    _check_lse(lse, H, T)
+    _check_lse(lse, H, T, q_rot.device)
     code = _dtype_code(q_rot)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
@@ -430,6 +469,7 @@ def gdpa_fwd(q, k, v, offsets, block_size: int, window_blocks: int, scale: float
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
         out = torch.empty_like(q) if out is None else out
+        _check_like(q, out, what="out")
         rc = blockattn_gdpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), offsets.data_ptr(),
                                 offsets.numel() - 1, T, H, D, block_size, window_blocks,
                                 float(scale), int(activation), _dtype_code(q), out.data_ptr(),
@@ -463,24 +503,37 @@ def gdpa_bwd(q, k, v, dout, offsets, block_size: int, window_blocks: int, scale:
     return dq, dk, dv
 
 
+def _check_mx_rows(dev, T, H, D, **ts):
+    """E4M3 codes [T, H, D] and their E8M0 scales [H, T, D/32] (uint8)."""
+    for n, t in ts.items():
+        shape = (T, H, D) if not n.endswith("scale") else (H, T, D // 32)
+        _check_tensor(t, shape, torch.uint8, dev, n)
+
+
+def _check_mx_tok(dev, T, H, D, batch, **ts):
+    """Token-blocked E4M3 codes [H, D, 32 nb] and scales [H, nb, D] (uint8),
+    nb = ceil(T/32) + batch."""
+    nb = -(-T // 32) + batch
+    for n, t in ts.items():
+        shape = (H, D, 32 * nb) if not n.endswith("scale") else (H, nb, D)
+        _check_tensor(t, shape, torch.uint8, dev, n)
+
+
 def mx_fwd(q, q_scale, k, k_scale, v, offsets, block_size: int, window_blocks: int,
            scale: float, out=None, lse=None, stream=None):
     """Forward with q and k in MXFP8 (blockattn_mx_fwd): q, k uint8 [T, H, D]
     E4M3 codes; q_scale, k_scale uint8 [H, T, D/32] E8M0 scales; v bf16.
     Returns (out bf16 [T, H, D], lse fp32 [H, T])."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not q.is_cuda:
+        raise ValueError("q must be a [T, H, D] device tensor")
     T, H, D = q.shape
-    for t in (q, k):
-        if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q and k must be contiguous uint8 [T, H, D] device tensors")
-    for t in (q_scale, k_scale):
-        if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
-            raise ValueError("q_scale and k_scale must be contiguous uint8 [H, T, D/32]")
-    if v.dtype != torch.bfloat16 or v.shape != (T, H, D) or not v.is_contiguous():
-        raise ValueError("v must be a contiguous bf16 [T, H, D] tensor")
+    dev = q.device
+    _check_mx_rows(dev, T, H, D, q=q, q_scale=q_scale, k=k, k_scale=k_scale)
+    _check_tensor(v, (T, H, D), torch.bfloat16, dev, "v")
+    _check_offsets(offsets, dev)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
-        out = torch.empty_like(v) if out is None else out
-        lse = torch.empty((H, T), dtype=torch.float32, device=v.device) if lse is None else lse
+        out, lse = _outputs(q, out, lse, torch.bfloat16)
         rc = blockattn_mx_fwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(),
                               k_scale.data_ptr(), v.data_ptr(), offsets.data_ptr(),
                               offsets.numel() - 1, T, H, D, block_size, window_blocks,
@@ -498,22 +551,16 @@ def mxpv_fwd(q, q_scale, k, k_scale, v_t, v_scale, offsets, block_size: int,
     blocked by user, padding with finite codes) and v_scale uint8 [H, nb, D]
     with nb = ceil(T/32) + batch (workloads.mx_v_device_layout builds them).
     Returns (out bf16 [T, H, D], lse fp32 [H, T])."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not q.is_cuda:
+        raise ValueError("q must be a [T, H, D] device tensor")
     T, H, D = q.shape
-    nb = -(-T // 32) + offsets.numel() - 1
-    for t in (q, k):
-        if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q and k must be contiguous uint8 [T, H, D] device tensors")
-    for t in (q_scale, k_scale):
-        if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
-            raise ValueError("q_scale and k_scale must be contiguous uint8 [H, T, D/32]")
-    if v_t.dtype != torch.uint8 or v_t.shape != (H, D, 32 * nb) or not v_t.is_contiguous():
-        raise ValueError("v_t must be a contiguous uint8 [H, D, 32 (ceil(T/32) + batch)] tensor")
-    if v_scale.dtype != torch.uint8 or v_scale.shape != (H, nb, D) or not v_scale.is_contiguous():
-        raise ValueError("v_scale must be a contiguous uint8 [H, ceil(T/32) + batch, D] tensor")
+    dev = q.device
+    _check_offsets(offsets, dev)
+    _check_mx_rows(dev, T, H, D, q=q, q_scale=q_scale, k=k, k_scale=k_scale)
+    _check_mx_tok(dev, T, H, D, offsets.numel() - 1, v_t=v_t, v_scale=v_scale)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
-        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device) if out is None else out
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+        out, lse = _outputs(q, out, lse, torch.bfloat16)
         rc = blockattn_mxpv_fwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(),
                                 k_scale.data_ptr(), v_t.data_ptr(), v_scale.data_ptr(),
                                 offsets.data_ptr(), offsets.numel() - 1, T, H, D, block_size,
@@ -533,28 +580,20 @@ def mx_bwd(q, q_scale, k, k_scale, v, v_scale, dout, dout_scale, q_t, q_t_scale,
     user-blocked: workloads.mx_v_device_layout builds them), nb =
     ceil(T/32) + batch; out bf16 [T, H, D] and lse fp32 [H, T] from the
     forward.  Returns (dq, dk, dv), bf16 [T, H, D]."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not q.is_cuda:
+        raise ValueError("q must be a [T, H, D] device tensor")
     T, H, D = q.shape
-    nb = -(-T // 32) + offsets.numel() - 1
-    for t in (q, k, v, dout):
-        if t.dtype != torch.uint8 or t.shape != (T, H, D) or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v, dout must be contiguous uint8 [T, H, D] device tensors")
-    for t in (q_scale, k_scale, v_scale, dout_scale):
-        if t.dtype != torch.uint8 or t.shape != (H, T, D // 32) or not t.is_contiguous():
-            raise ValueError("head-dim scales must be contiguous uint8 [H, T, D/32]")
-    for t in (q_t, k_t, dout_t):
-        if t.dtype != torch.uint8 or t.shape != (H, D, 32 * nb) or not t.is_contiguous():
-            raise ValueError("q_t, k_t, dout_t must be contiguous uint8 "
-                             "[H, D, 32 (ceil(T/32) + batch)]")
-    for t in (q_t_scale, k_t_scale, dout_t_scale):
-        if t.dtype != torch.uint8 or t.shape != (H, nb, D) or not t.is_contiguous():
-            raise ValueError("token scales must be contiguous uint8 [H, ceil(T/32) + batch, D]")
-    if out.dtype != torch.bfloat16 or out.shape != (T, H, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 [T, H, D] tensor")
-    _check_lse(lse, H, T)
+    dev = q.device
+    _check_offsets(offsets, dev)
+    _check_mx_rows(dev, T, H, D, q=q, q_scale=q_scale, k=k, k_scale=k_scale, v=v,
+                   v_scale=v_scale, dout=dout, dout_scale=dout_scale)
+    _check_mx_tok(dev, T, H, D, offsets.numel() - 1, q_t=q_t, q_t_scale=q_t_scale, k_t=k_t,
+                  k_t_scale=k_t_scale, dout_t=dout_t, dout_t_scale=dout_t_scale)
+    _check_tensor(out, (T, H, D), torch.bfloat16, dev, "out")
+    _check_lse(lse, H, T, dev)
     st = _torch_stream(stream)
     with torch.cuda.stream(st):
-        dq, dk, dv = (tuple(torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device)
-                            for _ in range(3)) if grads is None else grads)
+        dq, dk, dv = _grads(q, grads, torch.bfloat16)
         ws = _workspace(q, offsets, BF16, workspace)
         ws_ptr, ws_len = _ws_args(ws)
         rc = blockattn_mx_bwd(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
