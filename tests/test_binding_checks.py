@@ -80,8 +80,9 @@ def test_each_wrong_argument_is_rejected():
                                                    out=short),
         "mx scale transposed": lambda: lsb.mx_fwd(u8, sc.transpose(0, 1).contiguous(), u8, sc,
                                                   x, off, B, W, s),
-        "mxpv v_t one block short": lambda: lsb.mxpv_fwd(u8, sc, u8, sc, tok[:, :, 32:].contiguous(),
-                                                         tsc, off, B, W, s),
+        "mxpv v_t one block short": lambda: lsb.mxpv_fwd(u8, sc, u8, sc,
+                                                         tok[:, :, 32:].contiguous(), tsc, off,
+                                                         B, W, s),
         "mx_bwd grads in fp32": lambda: lsb.mx_bwd(u8, sc, u8, sc, u8, sc, u8, sc, tok, tsc, tok,
                                                    tsc, tok, tsc, out, l, off, B, W, s,
                                                    grads=(f32, f32, f32)),
@@ -93,3 +94,31 @@ def test_each_wrong_argument_is_rejected():
         with pytest.raises(ValueError):
             call()
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_caller_buffers_give_the_same_results():
+    """out, lse, grads and workspace passed in are used as they are: the
+    results equal those of a call that allocates them."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    x, k, v, do = (torch.randn(T, H, D, device=dev, generator=g).to(torch.bfloat16)
+                   for _ in range(4))
+    off = torch.tensor([0, 40, T], dtype=torch.int32, device=dev)
+    s = 0.125
+    out, lse = lsb.fwd(x, k, v, off, B, W, s)
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    r = lsb.fwd(x, k, v, off, B, W, s, out=out2, lse=lse2)
+    assert r[0] is out2 and r[1] is lse2
+    grads = lsb.bwd(x, k, v, out, do, lse, off, B, W, s)
+    mine = tuple(torch.empty_like(x) for _ in range(3))
+    ws = torch.empty(lsb.blockattn_bwd_workspace_size(T, 2, H, lsb.BF16), dtype=torch.uint8,
+                     device=dev)
+    r2 = lsb.bwd(x, k, v, out, do, lse, off, B, W, s, grads=mine, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    for a, b, c in zip(grads, mine, r2):
+        assert b is c
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
