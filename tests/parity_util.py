@@ -351,3 +351,26 @@ def row_slice(L: int, a: int, b: int, B: int, W: int):
     s0 = max(0, a // B - W + 1) * B
     e = min(L, ((b - 1) // B + W) * B)
     return s0, e
+
+
+def random_shapes(n, seed, head_dims=(32, 64, 128), fp32_share=0.2):
+    """n seeded shape sets (lengths, H, D, B, W, dtype, scale sign): 1-10
+    users mixing empty, one- or two-token, short and multi-tile lengths,
+    H 1-3, D from head_dims, B log-uniform in 1-300, W 1-8, a share in fp32
+    and a quarter with a negative scale."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        users = int(rng.integers(1, 11))
+        kind = rng.random(users)
+        lengths = [int(x) for x in np.where(
+            kind < 0.15, rng.integers(0, 3, users),
+            np.where(kind < 0.6, rng.integers(3, 130, users), rng.integers(130, 700, users)))]
+        H = int(rng.integers(1, 4))
+        D = int(rng.choice(list(head_dims)))
+        B = max(int(np.exp(rng.uniform(0.0, np.log(300.0)))), 1)
+        W = int(rng.integers(1, 9))
+        dtype = "fp32" if rng.random() < fp32_share else "bf16"
+        sign = -1.0 if rng.random() < 0.25 else 1.0
+        out.append((lengths, H, D, B, W, dtype, sign))
+    return out

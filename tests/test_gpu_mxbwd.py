@@ -26,7 +26,7 @@ import torch
 import long_sequence_block_amd as lsb
 import oracle
 from long_sequence_block_amd import workloads as wl
-from parity_util import MxBwdParity, user_ranges
+from parity_util import MxBwdParity, random_shapes, user_ranges
 
 pytestmark = pytest.mark.gpu
 
@@ -143,6 +143,20 @@ def test_mx_bwd_every_element(idx):
     lengths, H, D, B, W, sign = MXB[idx]
     _print(f"mxbwd {idx}: {len(lengths)} users, lengths={lengths[:8]} H={H} D={D} B={B} W={W}")
     c = wl.random_mxbwd_case(500 + idx, lengths, H, D)
+    p = mx_bwd_parity(c, B, W, sign / math.sqrt(D))
+    _print("  " + p.summary())
+
+
+MXB_RANDOM = random_shapes(12, 2027, head_dims=(64, 128), fp32_share=0.0)
+
+
+@pytest.mark.parametrize("idx", range(len(MXB_RANDOM)))
+def test_mx_bwd_random_shape_every_element(idx):
+    """Seeded random shapes (parity_util.random_shapes): user mixes, head
+    counts, blocks and windows the listed cases do not name."""
+    lengths, H, D, B, W, _, sign = MXB_RANDOM[idx]
+    _print(f"mxbwd random {idx}: lengths={lengths} H={H} D={D} B={B} W={W} sign {sign:+.0f}")
+    c = wl.random_mxbwd_case(800 + idx, lengths, H, D)
     p = mx_bwd_parity(c, B, W, sign / math.sqrt(D))
     _print("  " + p.summary())
 

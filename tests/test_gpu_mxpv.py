@@ -34,7 +34,7 @@ import torch
 import long_sequence_block_amd as lsb
 import oracle
 from long_sequence_block_amd import workloads as wl
-from parity_util import compare_by_users
+from parity_util import compare_by_users, random_shapes
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +112,19 @@ def test_mxpv_fwd_every_element(idx):
     lengths, H, D, B, W, sign = MXPV[idx]
     _print(f"mxpv {idx}: {len(lengths)} users, lengths={lengths[:8]} H={H} D={D} B={B} W={W}")
     c = wl.random_mxpv_case(300 + idx, lengths, H, D)
+    p = mxpv_parity(c, B, W, sign / math.sqrt(D), 1 << 30)
+    _print("  " + p.summary())
+
+
+MXPV_RANDOM = random_shapes(12, 2028, head_dims=(64, 128), fp32_share=0.0)
+
+
+@pytest.mark.parametrize("idx", range(len(MXPV_RANDOM)))
+def test_mxpv_fwd_random_shape_every_element(idx):
+    """Seeded random shapes (parity_util.random_shapes)."""
+    lengths, H, D, B, W, _, sign = MXPV_RANDOM[idx]
+    _print(f"mxpv random {idx}: lengths={lengths} H={H} D={D} B={B} W={W} sign {sign:+.0f}")
+    c = wl.random_mxpv_case(450 + idx, lengths, H, D)
     p = mxpv_parity(c, B, W, sign / math.sqrt(D), 1 << 30)
     _print("  " + p.summary())
 
