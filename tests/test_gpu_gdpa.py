@@ -18,7 +18,8 @@ import torch
 import long_sequence_block_amd as lsb
 import oracle
 from long_sequence_block_amd import workloads as wl
-from parity_util import GdpaParity, host_rows, np64, to_device, to_device_lazy, user_ranges
+from parity_util import (GdpaParity, host_rows, np64, random_shapes, to_device, to_device_lazy,
+                         user_ranges)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,11 +56,9 @@ GDPA = [
 ]
 
 
-@pytest.mark.parametrize("idx", range(len(GDPA)))
-def test_gdpa_every_element(idx):
-    lengths, H, D, B, W, dtype, act, sign = GDPA[idx]
-    _print(f"gdpa {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype} act={act}")
-    case = wl.random_case(1000 + idx, lengths, H, D)
+def gdpa_case(seed, lengths, H, D, B, W, dtype, act, sign):
+    """Forward and backward of one case, every element against the oracle."""
+    case = wl.random_case(seed, lengths, H, D)
     dev, host = to_device(case, dtype)
     scale = sign / math.sqrt(D)
     out = lsb.gdpa_fwd(dev["q"], dev["k"], dev["v"], dev["offsets"], B, W, scale, act)
@@ -71,6 +70,25 @@ def test_gdpa_every_element(idx):
     add_gdpa(p, host, (np64(out), [np64(g) for g in grads]), B, W, scale, act)
     p.finish()
     _print("  " + p.summary())
+
+
+@pytest.mark.parametrize("idx", range(len(GDPA)))
+def test_gdpa_every_element(idx):
+    lengths, H, D, B, W, dtype, act, sign = GDPA[idx]
+    _print(f"gdpa {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype} act={act}")
+    gdpa_case(1000 + idx, lengths, H, D, B, W, dtype, act, sign)
+
+
+GDPA_RANDOM = random_shapes(10, 2029)
+
+
+@pytest.mark.parametrize("idx", range(len(GDPA_RANDOM)))
+def test_gdpa_random_shape_every_element(idx):
+    """Seeded random shapes (parity_util.random_shapes), SiLU and GELU in turn."""
+    lengths, H, D, B, W, dtype, sign = GDPA_RANDOM[idx]
+    act = 1 + idx % 2
+    _print(f"gdpa random {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype} act={act}")
+    gdpa_case(1100 + idx, lengths, H, D, B, W, dtype, act, sign)
 
 
 @pytest.mark.timeout(900)

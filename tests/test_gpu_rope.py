@@ -15,7 +15,8 @@ import torch
 import long_sequence_block_amd as lsb
 import oracle
 from long_sequence_block_amd import workloads as wl
-from parity_util import assert_close, compare_by_users, np64, to_device, to_device_lazy
+from parity_util import (assert_close, compare_by_users, np64, random_shapes, to_device,
+                         to_device_lazy)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,18 +84,14 @@ ROPE_ATTN = [
 ]
 
 
-@pytest.mark.parametrize("idx", range(len(ROPE_ATTN)))
-def test_rope_attention_fwd_bwd_every_element(idx):
+def rope_attention_case(seed, lengths, H, D, B, W, dtype, base, scale):
     """rope, then the block-attention forward on the rotated q and k, then
     the backward with the rotation's transpose fused in: out, lse and the
     gradients with respect to the unrotated q, k and v.  The reference
     attends on the oracle's rotation stored in the call's dtype, as the GPU
     path stores its rotated q and k."""
-    lengths, H, D, B, W, dtype, base = ROPE_ATTN[idx]
-    _print(f"rope attention {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype}")
-    case = wl.random_case(950 + idx, lengths, H, D)
+    case = wl.random_case(seed, lengths, H, D)
     dev, host = to_device(case, dtype)
-    scale = 1.0 / math.sqrt(D)
     qr, kr = lsb.rope(dev["q"], dev["k"], dev["offsets"], base)
     out, lse = lsb.fwd(qr, kr, dev["v"], dev["offsets"], B, W, scale)
     hq, hk = rotated_ref(host, base, dtype)
@@ -111,6 +108,24 @@ def test_rope_attention_fwd_bwd_every_element(idx):
     plain = lsb.bwd(qr, kr, dev["v"], out, dev["dout"], lse, dev["offsets"], B, W, scale)
     assert torch.equal(plain[2], grads[2])
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("idx", range(len(ROPE_ATTN)))
+def test_rope_attention_fwd_bwd_every_element(idx):
+    lengths, H, D, B, W, dtype, base = ROPE_ATTN[idx]
+    _print(f"rope attention {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype}")
+    rope_attention_case(950 + idx, lengths, H, D, B, W, dtype, base, 1.0 / math.sqrt(D))
+
+
+ROPE_RANDOM = random_shapes(8, 2030)
+
+
+@pytest.mark.parametrize("idx", range(len(ROPE_RANDOM)))
+def test_rope_attention_random_shape_every_element(idx):
+    """Seeded random shapes (parity_util.random_shapes)."""
+    lengths, H, D, B, W, dtype, sign = ROPE_RANDOM[idx]
+    _print(f"rope random {idx}: lengths={lengths} H={H} D={D} B={B} W={W} {dtype}")
+    rope_attention_case(1200 + idx, lengths, H, D, B, W, dtype, 10000.0, sign / math.sqrt(D))
 
 
 @pytest.mark.timeout(900)
