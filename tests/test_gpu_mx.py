@@ -29,7 +29,7 @@ import torch
 import long_sequence_block_amd as lsb
 import oracle
 from long_sequence_block_amd import workloads as wl
-from parity_util import Parity, compare_by_users, np64
+from parity_util import Parity, compare_by_users, np64, random_shapes
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +100,18 @@ def test_mx_fwd_every_element(idx):
     lengths, H, D, B, W, sign = MX[idx]
     _print(f"mx {idx}: {len(lengths)} users, lengths={lengths[:8]} H={H} D={D} B={B} W={W}")
     c = wl.random_mx_case(idx, lengths, H, D)
+    mx_parity(c, B, W, sign / math.sqrt(D), 1 << 30)
+
+
+MX_RANDOM = random_shapes(10, 2031, head_dims=(64, 128), fp32_share=0.0)
+
+
+@pytest.mark.parametrize("idx", range(len(MX_RANDOM)))
+def test_mx_fwd_random_shape_every_element(idx):
+    """Seeded random shapes (parity_util.random_shapes)."""
+    lengths, H, D, B, W, _, sign = MX_RANDOM[idx]
+    _print(f"mx random {idx}: lengths={lengths} H={H} D={D} B={B} W={W} sign {sign:+.0f}")
+    c = wl.random_mx_case(200 + idx, lengths, H, D)
     mx_parity(c, B, W, sign / math.sqrt(D), 1 << 30)
 
 
