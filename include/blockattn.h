@@ -34,7 +34,12 @@
  * overlap.  Outputs are fully overwritten, never accumulated into.  Results are
  * bitwise deterministic for identical inputs.  Malformed offsets (not
  * satisfying the rules above) give unspecified values but no out-of-bounds
- * memory access: every user range is clamped to [0, T].
+ * memory access: every user range is clamped to [0, T].  Input values are
+ * expected to be finite: a NaN or infinity in q, k, v or dout can make NaN
+ * any output of the 128-row tiles that read it, rows that do not see that
+ * element included (the matrix products multiply masked weights, which are
+ * zero, by every value a tile reads, and 0 x NaN is NaN); it never causes an
+ * out-of-bounds access.
  *
  * Errors.  Return codes only; nothing throws across the ABI.  Argument checks
  * happen before any HIP call, so an invalid call enqueues nothing.
