@@ -238,6 +238,27 @@ def cpu_baseline(w, users: int, flops_per_pair_head: float):
             "cpu_model": cpu_model(), "single_thread": single}
 
 
+WARM_SECONDS = 0.5  # least wall time of untimed steps before a timed region
+
+
+def warm_up(fn, steps: int, seconds: float = WARM_SECONDS) -> int:
+    """Runs fn back to back at least `steps` times and for at least `seconds`
+    of wall time, then waits for the GPU.  The GPU raises its clocks over its
+    first tens of milliseconds under load, so a timed region that starts
+    earlier measures that ramp: in one run of the jagged training step, 20
+    timed steps after 5 warm-up steps took 0.92 ms each, and every later
+    group of 20 about 0.84 ms.  Returns how many times fn ran."""
+    import torch
+    n, t_end = 0, time.perf_counter() + seconds
+    while n < steps or time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 4 == 0:  # keep the host within a few calls of the GPU
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def copy_calibration(mib: int, steps: int, warmup: int):
     """Times torch's device-to-device copy of a known size: its HBM byte
     counters (read mib MiB, write mib MiB per launch) calibrate the counters
@@ -246,9 +267,7 @@ def copy_calibration(mib: int, steps: int, warmup: int):
     n = mib << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
-    for _ in range(warmup):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    warm_up(lambda: dst.copy_(src), warmup)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
@@ -284,8 +303,8 @@ def length_sweep(steps: int, warmup: int):
         out = torch.empty_like(q)
         lse = torch.empty((H, T), dtype=torch.float32, device=dev)
         for W, kind in ((w.window_blocks, "block window"), (L // B, "full causal")):
-            for _ in range(warmup):
-                lsb.fwd(q, k, v, off, B, W, w.scale, out=out, lse=lse)
+            warm_up(lambda: lsb.fwd(q, k, v, off, B, W, w.scale, out=out, lse=lse), warmup,
+                    0.2)
             times = []
             for _ in range(steps):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -338,6 +357,8 @@ def main():
                     help="long-context workload: per-user length (sweep)")
     ap.add_argument("--window-blocks", type=int, default=0,
                     help="override the workload's window W (e.g. L/B: full causal attention)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="override the workload's block size B (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold pass (steps after an L2 / Infinity Cache flush)")
@@ -373,6 +394,9 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.length:
         w = wl.long_context(args.length)
+    if args.block_size:
+        w = dataclasses.replace(w, block_size=args.block_size,
+                                name=f"{w.name}-B{args.block_size}")
     if args.window_blocks:
         w = dataclasses.replace(w, window_blocks=args.window_blocks,
                                 name=f"{w.name}-W{args.window_blocks}")
@@ -449,9 +473,7 @@ def main():
         if w.backward and ev is not None:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm_up(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -535,7 +557,8 @@ def main():
 
     res = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm_steps,
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp8" if w.mx_v else "mxfp8(qk)+bf16" if w.mx else w.dtype,
         "data": "synthetic (seeded; lognormal jagged lengths, N(0,1) values"
@@ -553,7 +576,9 @@ def main():
         "pct_mfma_peak": round(100.0 * tflops / peak, 3),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "timing": ("value and ms_per_step: warm, the timed steps run back to back with "
-                   "inputs resident in HBM; calls.cold: per-call medians after a 512 MiB "
+                   "inputs resident in HBM, after at least `warmup` untimed steps and "
+                   f"{WARM_SECONDS} s of them (warmup_steps_run), so that the GPU's clocks "
+                   "have settled under the load; calls.cold: per-call medians after a 512 MiB "
                    "write that evicts L2 and the Infinity Cache"),
         "calls": calls,
         "roofline": roof,

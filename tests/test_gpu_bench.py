@@ -25,6 +25,7 @@ def test_bench_json_line():
                 "roofline", "cpu_baseline"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["warmup_steps_run"] >= 1   # at least `warmup`, and half a second of steps
     assert d["value"] > 0 and d["ms_per_step"] > 0
     assert d["config"]["workload"] == "tiny-fp32"
     roof = d["roofline"]
